@@ -1,0 +1,30 @@
+"""CPU oracle for single-token grouped-query decode attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute anything in this package: only the test suite, the graft smoke entry
+and the benchmark's ``cpu_baseline`` leg use it. It shares no code with the
+HIP library or its Python binding, and imports neither.
+
+Modules:
+  gqa_oracle  vectorised fp64 numpy definition of the decode step, plus the
+              exact decoders for the stored KV/query formats.
+  brute       pure-Python loops (math.fsum / math.exp) for tiny inputs.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against facts fixed
+by the pages or by mathematics (closed forms, invariants, a library special
+case, brute force). No function here is "parity unpinned".
+"""
+
+from .gqa_oracle import (  # noqa: F401
+    HEAD_DIM,
+    NUM_KV_HEADS,
+    NUM_Q_HEADS,
+    GROUP,
+    decode_bf16_bits,
+    decode_e4m3fn_bits,
+    decode_f16_bits,
+    decode_storage,
+    gqa_decode_head,
+    gqa_decode_reference,
+    gqa_decode_weights,
+)

@@ -1,0 +1,253 @@
+"""Pins for the CPU oracle: facts fixed by the pages or by mathematics.
+
+Each test would fail for a plausible mistake in the oracle (dropped scale,
+misplaced k/v scale, wrong head mapping, transposed K/V, off-by-one length,
+missing max shift, wrong fp8 exponent bias or subnormal rule). None of them
+re-types the oracle's own vectorised formula.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (
+    GROUP,
+    HEAD_DIM,
+    NUM_KV_HEADS,
+    NUM_Q_HEADS,
+    decode_bf16_bits,
+    decode_e4m3fn_bits,
+    decode_f16_bits,
+    gqa_decode_head,
+    gqa_decode_reference,
+    gqa_decode_weights,
+)
+from oracle.brute import brute_decode
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_case(rng, B, C, lens=None):
+    q = rng.standard_normal((B, NUM_Q_HEADS, HEAD_DIM))
+    kv = rng.standard_normal((B, 2, NUM_KV_HEADS, C, HEAD_DIM))
+    if lens is None:
+        lens = rng.integers(1, C + 1, size=B)
+    return q, kv, np.asarray(lens)
+
+
+# ---------------------------------------------------------------- pin 9: formats
+def test_e4m3fn_matches_torch_for_all_codes():
+    """Library special case: torch.float8_e4m3fn is the format the pages name."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = decode_e4m3fn_bits(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~both_nan], ref[~both_nan])
+    # sign of zero is preserved too
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+
+
+def test_e4m3fn_anchor_values_from_spec():
+    path = os.path.join(GOLDEN, "e4m3fn_anchor_values.txt")
+    n = 0
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            code_s, val_s = line.split()
+            got = decode_e4m3fn_bits(np.array([int(code_s, 16)], dtype=np.uint8))[0]
+            want = float(val_s)
+            if math.isnan(want):
+                assert math.isnan(got), code_s
+            else:
+                assert got == want and math.copysign(1, got) == math.copysign(1, want), code_s
+            n += 1
+    assert n >= 10
+
+
+def test_e4m3fn_all_finite_codes_exact_in_bf16_and_f16():
+    # Why converting fp8 to bf16/f16 on the GPU loses nothing: every finite
+    # e4m3fn value has <= 4 significant bits and exponent in [-9, 8].
+    vals = decode_e4m3fn_bits(np.arange(256, dtype=np.uint8))
+    vals = vals[np.isfinite(vals)]
+    assert np.array_equal(torch.tensor(vals).to(torch.bfloat16).double().numpy(), vals)
+    assert np.array_equal(torch.tensor(vals).to(torch.float16).double().numpy(), vals)
+
+
+def test_16bit_decoders_match_torch():
+    rng = np.random.default_rng(7)
+    bits = rng.integers(0, 1 << 16, size=4096).astype(np.uint16)
+    bf = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    hf = torch.from_numpy(bits.view(np.int16)).view(torch.float16).double().numpy()
+    ob, oh = decode_bf16_bits(bits), decode_f16_bits(bits)
+    assert np.array_equal(np.isnan(ob), np.isnan(bf)) and np.array_equal(ob[~np.isnan(ob)], bf[~np.isnan(bf)])
+    assert np.array_equal(np.isnan(oh), np.isnan(hf)) and np.array_equal(oh[~np.isnan(oh)], hf[~np.isnan(hf)])
+
+
+# ---------------------------------------------------------------- pin 1: weights
+def test_softmax_weights_sum_to_one():
+    rng = np.random.default_rng(1)
+    q, kv, lens = _rand_case(rng, 3, 50)
+    for w in gqa_decode_weights(q, kv, lens, q_scale=0.7):
+        assert w.min() >= 0.0
+        assert np.max(np.abs(w.sum(axis=1) - 1.0)) <= 1e-12
+
+
+# ---------------------------------------------------------------- pin 2: L = 1
+@pytest.mark.parametrize("v_scale", [1.0, 1.0 / 64])
+def test_single_token_returns_scaled_v_row0(v_scale):
+    rng = np.random.default_rng(2)
+    q, kv, _ = _rand_case(rng, 2, 9)
+    lens = np.array([1, 1])
+    out = gqa_decode_reference(q, kv, lens, q_scale=3.0, k_scale=0.25, v_scale=v_scale)
+    for b in range(2):
+        for h in range(NUM_Q_HEADS):
+            assert np.array_equal(out[b, h], v_scale * kv[b, 1, h // GROUP, 0])
+
+
+# ---------------------------------------------------------------- pin 3: identical keys
+def test_identical_keys_give_mean_of_values():
+    rng = np.random.default_rng(3)
+    q, kv, _ = _rand_case(rng, 2, 40)
+    lens = np.array([17, 40])
+    kv[:, 0] = kv[:, 0, :, :1, :]          # every key equals key 0
+    out = gqa_decode_reference(q, kv, lens, v_scale=0.5)
+    for b, L in enumerate(lens):
+        for h in range(NUM_Q_HEADS):
+            want = 0.5 * kv[b, 1, h // GROUP, :L].mean(axis=0)
+            np.testing.assert_allclose(out[b, h], want, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- pin 4: padding
+@pytest.mark.parametrize("pad", ["random", "nan"])
+def test_capacity_padding_is_invisible(pad):
+    rng = np.random.default_rng(4)
+    L = np.array([5, 13])
+    q, kv_tight, _ = _rand_case(rng, 2, 13, L)
+    kv_tight[0, :, :, 5:] = rng.standard_normal(kv_tight[0, :, :, 5:].shape)
+    kv_wide = (rng.standard_normal((2, 2, NUM_KV_HEADS, 52, HEAD_DIM)) if pad == "random"
+               else np.full((2, 2, NUM_KV_HEADS, 52, HEAD_DIM), np.nan))
+    kv_wide[:, :, :, :13] = kv_tight
+    kv_wide[0, :, :, 5:13] = np.nan if pad == "nan" else 1e3
+    a = gqa_decode_reference(q, kv_tight, L)
+    b = gqa_decode_reference(q, kv_wide, L)
+    assert np.array_equal(a, b)
+    assert np.all(np.isfinite(b))
+
+
+# ---------------------------------------------------------------- pin 5: brute force
+def test_brute_force_agrees_on_tiny_inputs():
+    rng = np.random.default_rng(5)
+    q, kv, _ = _rand_case(rng, 2, 6)
+    lens = np.array([6, 3])
+    qs, ks, vs = 0.8, 1.7, 0.3
+    ref = gqa_decode_reference(q, kv, lens, qs, ks, vs)
+    brute = np.array(brute_decode(q.tolist(), kv.tolist(), lens.tolist(), qs, ks, vs))
+    np.testing.assert_allclose(ref, brute, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- pin 6: SDPA
+def test_matches_torch_sdpa_fp64_with_gqa():
+    rng = np.random.default_rng(6)
+    q, kv, _ = _rand_case(rng, 3, 70)
+    lens = np.array([70, 1, 33])
+    qs, ks, vs = 0.5, 2.0, 0.125
+    ref = gqa_decode_reference(q, kv, lens, qs, ks, vs)
+    for b, L in enumerate(lens):
+        qt = torch.from_numpy(q[b]).view(1, NUM_Q_HEADS, 1, HEAD_DIM)
+        kt = torch.from_numpy(kv[b, 0, :, :L]).view(1, NUM_KV_HEADS, L, HEAD_DIM)
+        vt = torch.from_numpy(kv[b, 1, :, :L]).view(1, NUM_KV_HEADS, L, HEAD_DIM)
+        sd = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, scale=qs * ks / math.sqrt(HEAD_DIM), enable_gqa=True)
+        np.testing.assert_allclose(ref[b], vs * sd[0, :, 0].numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- pin 7: grouping
+def test_head_h_reads_kv_head_h_div_4():
+    rng = np.random.default_rng(8)
+    q, kv, _ = _rand_case(rng, 2, 11)
+    lens = np.array([11, 4])
+    for g in range(NUM_KV_HEADS):
+        kv[:, 1, g] = float(g)
+    out = gqa_decode_reference(q, kv, lens)
+    for h in range(NUM_Q_HEADS):
+        np.testing.assert_allclose(out[:, h], float(h // 4), rtol=0, atol=1e-13, err_msg=str(h))
+
+
+# ---------------------------------------------------------------- closed form
+@pytest.mark.parametrize("qs,ks,vs", [(1.0, 1.0, 1.0), (0.5, 1.0 / 64, 1.0 / 64), (3.0, 0.25, 2.0)])
+def test_two_token_closed_form(qs, ks, vs):
+    """Two keys, k0 = 0, k1 = c*e0: weight of key 1 is the logistic function
+    of the score gap qs*ks*q0*c/sqrt(128); out = vs*((1-w)v0 + w v1)."""
+    rng = np.random.default_rng(9)
+    B, C = 1, 4
+    q = np.zeros((B, NUM_Q_HEADS, HEAD_DIM))
+    kv = rng.standard_normal((B, 2, NUM_KV_HEADS, C, HEAD_DIM))
+    a = np.linspace(-3.0, 3.0, NUM_Q_HEADS)
+    q[0, :, 0] = a
+    q[0, :, 1:] = rng.standard_normal((NUM_Q_HEADS, HEAD_DIM - 1))
+    cvals = np.linspace(0.5, 4.0, NUM_KV_HEADS)
+    kv[0, 0, :, 0] = 0.0
+    kv[0, 0, :, 1] = 0.0
+    kv[0, 0, :, 1, 0] = cvals
+    out = gqa_decode_reference(q, kv, [2], qs, ks, vs)
+    for h in range(NUM_Q_HEADS):
+        g = h // 4
+        gap = qs * ks * a[h] * cvals[g] / math.sqrt(128.0)
+        w1 = 1.0 / (1.0 + math.exp(-gap))
+        want = vs * ((1.0 - w1) * kv[0, 1, g, 0] + w1 * kv[0, 1, g, 1])
+        np.testing.assert_allclose(out[0, h], want, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- pin 8: limits
+def test_one_hot_limit_and_huge_scores():
+    """One key whose scaled score beats every other by > 60 nats takes all
+    the weight (the rest sum to < 9 * e^-60)."""
+    rng = np.random.default_rng(10)
+    qrows = rng.standard_normal((GROUP, HEAD_DIM)) * 1e-3
+    qrows[:, 0] = 1.0 + np.abs(rng.standard_normal(GROUP))
+    k = rng.standard_normal((9, HEAD_DIM)) * 1e-3
+    v = rng.standard_normal((9, HEAD_DIM))
+    k[4] = 0.0
+    k[4, 0] = 61.0 * math.sqrt(HEAD_DIM)
+    out = gqa_decode_head(qrows, k, v)
+    np.testing.assert_allclose(out, np.tile(v[4], (GROUP, 1)), rtol=0, atol=1e-20)
+    # scores of order 1e4 would overflow exp without the max shift
+    out2 = gqa_decode_head(qrows, k * 20.0, v)
+    assert np.all(np.isfinite(out2))
+    np.testing.assert_allclose(out2, np.tile(v[4], (GROUP, 1)), rtol=0, atol=1e-20)
+
+
+def test_joint_token_permutation_invariance():
+    rng = np.random.default_rng(11)
+    qrows = rng.standard_normal((GROUP, HEAD_DIM))
+    k = rng.standard_normal((37, HEAD_DIM))
+    v = rng.standard_normal((37, HEAD_DIM))
+    perm = rng.permutation(37)
+    a = gqa_decode_head(qrows, k, v, 0.9, 1.1, 0.7)
+    b = gqa_decode_head(qrows, k[perm], v[perm], 0.9, 1.1, 0.7)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- contract errors
+@pytest.mark.parametrize("bad", [0.0, -1.0, float("nan"), float("inf")])
+def test_rejects_bad_scales(bad):
+    rng = np.random.default_rng(12)
+    q, kv, lens = _rand_case(rng, 1, 4)
+    with pytest.raises(ValueError):
+        gqa_decode_reference(q, kv, lens, q_scale=bad)
+    with pytest.raises(ValueError):
+        gqa_decode_reference(q, kv, lens, v_scale=bad)
+
+
+@pytest.mark.parametrize("L", [0, 5])
+def test_rejects_lengths_outside_capacity(L):
+    rng = np.random.default_rng(13)
+    q, kv, _ = _rand_case(rng, 1, 4)
+    with pytest.raises(ValueError):
+        gqa_decode_reference(q, kv, [L])
