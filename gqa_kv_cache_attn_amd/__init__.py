@@ -19,8 +19,9 @@ __all__ = [
 
 def __getattr__(name):
     if name in __all__ or name in ("binding", "GqaPrepared", "library_path"):
-        from . import binding
+        import importlib
 
+        binding = importlib.import_module(__name__ + ".binding")
         if name == "binding":
             return binding
         return getattr(binding, name)

@@ -1,0 +1,259 @@
+"""ctypes binding of libgqa_decode.so (argument marshalling only).
+
+Every function here forwards to the C entry point of the same name in
+``include/gqa_decode.h``: it takes device pointers from the tensors, the
+current (or given) HIP stream, and maps the returned status to an exception.
+No step of the decode runs in Python. If the library is missing this module
+raises at import: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH
+
+library_path = LIB_PATH
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m gqa_kv_cache_attn_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_ALIAS, GQA_ERR_UNSUPPORTED_DEVICE = 0, 1, 2, 3
+GQA_ERR_CAPTURE, GQA_ERR_OUT_OF_MEMORY, GQA_ERR_HIP = 4, 5, 6
+GQA_F16, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
+GQA_FLAG_FUSED_COMBINE = 1
+NUM_Q_HEADS, NUM_KV_HEADS, HEAD_DIM = 32, 8, 128
+
+STATUS_NAMES = {
+    0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_ALIAS",
+    3: "GQA_ERR_UNSUPPORTED_DEVICE", 4: "GQA_ERR_CAPTURE",
+    5: "GQA_ERR_OUT_OF_MEMORY", 6: "GQA_ERR_HIP",
+}
+
+
+class GqaDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("capacity", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float), ("flags", ctypes.c_int32),
+    ]
+
+
+class GqaPlan(ctypes.Structure):
+    _fields_ = [
+        ("route", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("chunk_tokens", ctypes.c_int32), ("num_workgroups", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_uint64),
+    ]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+_DescP, _PlanP = ctypes.POINTER(GqaDesc), ctypes.POINTER(GqaPlan)
+
+
+def _sig(name, restype, argtypes):
+    fn = getattr(_lib, name)
+    fn.restype, fn.argtypes = restype, argtypes
+    return fn
+
+
+_gqa_decode = _sig("gqa_decode", ctypes.c_int, [_DescP, _vp, _vp, _vp, _f32, _vp, _vp])
+_prepare = _sig("prepare_gqa_decode", ctypes.c_int,
+                [_DescP, _vp, _vp, _vp, _f32, _vp, _i32, ctypes.POINTER(_vp)])
+_launch = _sig("launch_gqa_decode_prepared", ctypes.c_int, [_vp, _vp])
+_launch_timed = _sig("launch_gqa_decode_prepared_timed", ctypes.c_int, [_vp, _vp, _vp, _vp, _vp])
+_destroy = _sig("gqa_prepared_destroy", None, [_vp])
+_ws_bytes = _sig("gqa_prepared_workspace_bytes", ctypes.c_size_t, [_vp])
+_prep_plan = _sig("gqa_prepared_plan", ctypes.c_int, [_vp, _PlanP])
+_validate = _sig("gqa_validate_args", ctypes.c_int, [_DescP, _vp, _vp, _vp, _f32, _vp, _i32])
+_plan = _sig("gqa_plan_decode", ctypes.c_int, [_DescP, _i32, _PlanP])
+_last_error = _sig("gqa_last_error", ctypes.c_char_p, [])
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != GQA_OK:
+        msg = (_last_error() or b"").decode(errors="replace")
+        if status in (GQA_ERR_INVALID_ARG, GQA_ERR_ALIAS):
+            err = GqaError(status, msg)
+            raise ValueError(str(err)) from err
+        raise GqaError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor, role: str) -> int:
+    if t.dtype == torch.float16:
+        return GQA_F16
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if role == "kv" and t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return GQA_FP8_E4M3
+    raise ValueError(f"unsupported {role} dtype {t.dtype}")
+
+
+def make_desc(q: torch.Tensor, kv: torch.Tensor, k_scale: float = 1.0,
+              v_scale: float = 1.0, fused_combine: bool = False) -> GqaDesc:
+    if q.dim() != 3 or kv.dim() != 5:
+        raise ValueError("q must be [batch, 32, 128] and kv [batch, 2, 8, capacity, 128]")
+    if tuple(q.shape[1:]) != (NUM_Q_HEADS, HEAD_DIM):
+        raise ValueError(f"q must be [batch, 32, 128], got {tuple(q.shape)}")
+    if kv.shape[1] != 2 or kv.shape[0] != q.shape[0]:
+        raise ValueError(f"kv must be [batch, 2, 8, capacity, 128], got {tuple(kv.shape)}")
+    return GqaDesc(batch=q.shape[0], capacity=kv.shape[3], num_q_heads=q.shape[1],
+                   num_kv_heads=kv.shape[2], head_dim=kv.shape[4],
+                   q_dtype=_dtype_code(q, "q"), kv_dtype=_dtype_code(kv, "kv"),
+                   k_scale=k_scale, v_scale=v_scale,
+                   flags=GQA_FLAG_FUSED_COMBINE if fused_combine else 0)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check_devices(*ts):
+    devs = {t.device for t in ts}
+    if len(devs) != 1 or next(iter(devs)).type != "cuda":
+        raise ValueError("q, kv, seq_lens and out must be on the same GPU")
+
+
+def gqa_decode(q: torch.Tensor, kv: torch.Tensor, seq_lens: torch.Tensor,
+               q_scale: float = 1.0, out: Optional[torch.Tensor] = None,
+               k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> torch.Tensor:
+    """Enqueue one decode step on the current stream; returns ``out``."""
+    if out is None:
+        out = torch.empty_like(q)
+    _check_devices(q, kv, seq_lens, out)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q's shape and dtype")
+    desc = make_desc(q, kv, k_scale, v_scale)
+    with torch.cuda.device(q.device):
+        st = _gqa_decode(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(seq_lens), q_scale,
+                         _ptr(out), _stream_handle(stream, q.device))
+    _check(st)
+    return out
+
+
+class GqaPrepared:
+    """Owner of a prepared handle and of references to its tensors."""
+
+    def __init__(self, handle: int, tensors: dict, desc: GqaDesc):
+        self._handle = handle
+        self.tensors = tensors   # keeps q/kv/seq_lens/out alive as long as the handle
+        self.desc = desc
+
+    @property
+    def handle(self) -> int:
+        if not self._handle:
+            raise ValueError("prepared handle already destroyed")
+        return self._handle
+
+    @property
+    def out(self) -> torch.Tensor:
+        return self.tensors["O"]
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(_ws_bytes(self.handle))
+
+    @property
+    def plan(self) -> dict:
+        p = GqaPlan()
+        _check(_prep_plan(self.handle, ctypes.byref(p)))
+        return p.as_dict()
+
+    def destroy(self):
+        if self._handle:
+            _destroy(self._handle)
+            self._handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def prepare_gqa_decode(q: torch.Tensor, kv: torch.Tensor, seq_lens: torch.Tensor,
+                       out: torch.Tensor, q_scale: float = 1.0,
+                       num_splits: Optional[int] = None, k_scale: float = 1.0,
+                       v_scale: float = 1.0, fused_combine: bool = False) -> GqaPrepared:
+    """Validate, plan and allocate the split workspace once (outside capture)."""
+    _check_devices(q, kv, seq_lens, out)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q's shape and dtype")
+    desc = make_desc(q, kv, k_scale, v_scale, fused_combine)
+    h = _vp()
+    with torch.cuda.device(q.device):
+        st = _prepare(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(seq_lens), q_scale, _ptr(out),
+                      0 if num_splits is None else int(num_splits), ctypes.byref(h))
+    _check(st)
+    return GqaPrepared(h.value, {"Q": q, "KV": kv, "sequence_lengths": seq_lens, "O": out}, desc)
+
+
+def launch_gqa_decode_prepared(prepared: GqaPrepared, stream=None) -> torch.Tensor:
+    """Enqueue the prepared step (no allocation, no host sync); returns O."""
+    dev = prepared.out.device
+    _check(_launch(prepared.handle, _stream_handle(stream, dev)))
+    return prepared.out
+
+
+def launch_gqa_decode_prepared_timed(prepared: GqaPrepared, ev_start, ev_mid, ev_end,
+                                     stream=None) -> torch.Tensor:
+    """As launch_gqa_decode_prepared, recording three torch.cuda.Events (already
+    created, i.e. recorded once) around the attention kernel and the combine."""
+    dev = prepared.out.device
+    hs = [None if e is None else e.cuda_event for e in (ev_start, ev_mid, ev_end)]
+    _check(_launch_timed(prepared.handle, _stream_handle(stream, dev), *hs))
+    return prepared.out
+
+
+def gqa_validate_args(desc: GqaDesc, q_ptr: Optional[int], kv_ptr: Optional[int],
+                      lens_ptr: Optional[int], q_scale: float, out_ptr: Optional[int],
+                      num_splits: int = 0) -> int:
+    """Host-only validation (no device access); returns the raw status code."""
+    return int(_validate(ctypes.byref(desc), q_ptr, kv_ptr, lens_ptr, q_scale, out_ptr,
+                         num_splits))
+
+
+def gqa_plan(desc: GqaDesc, num_splits: int = 0) -> dict:
+    """Host-only launch plan for a descriptor."""
+    p = GqaPlan()
+    _check(_plan(ctypes.byref(desc), num_splits, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def last_error() -> str:
+    return (_last_error() or b"").decode(errors="replace")

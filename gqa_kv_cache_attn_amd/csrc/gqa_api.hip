@@ -1,0 +1,416 @@
+// C-ABI layer of libgqa_decode.so: argument validation, launch planning, the
+// prepared handle with its split workspace, and the convenience call.
+//
+// The entry points mirror the FlashInfer sm110_gqa_decode article's API
+// (convenience call; prepare + launch-prepared pair; "three differences":
+// caller-owned non-aliasing output, finite positive q_scale, a launch that
+// allocates nothing and reads nothing on the host; num_splits never replaced
+// silently) in plain C: pointers, sizes, a status code.
+//
+// Host code here never reads device memory; lengths stay on the device.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <utility>
+
+#include "../../include/gqa_decode.h"
+#include "gqa_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gqa_status_t fail(gqa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+gqa_status_t ok() {
+  g_last_error.clear();
+  return GQA_OK;
+}
+
+constexpr int kTargetWorkgroups = 2048;  // ~8 per CU on a 256-CU part
+
+int elem_bytes(int dt) { return dt == GQA_FP8_E4M3 ? 1 : 2; }
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return na != 0 && nb != 0 && a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+
+gqa_status_t check_desc(const gqa_desc_t* d) {
+  if (d == nullptr) return fail(GQA_ERR_INVALID_ARG, "desc is NULL");
+  if (d->num_q_heads != GQA_NUM_Q_HEADS || d->num_kv_heads != GQA_NUM_KV_HEADS ||
+      d->head_dim != GQA_HEAD_DIM)
+    return fail(GQA_ERR_INVALID_ARG,
+                "geometry is fixed at 32 query heads / 8 KV heads / head_dim 128 (got %d/%d/%d)",
+                d->num_q_heads, d->num_kv_heads, d->head_dim);
+  if (d->batch < 0) return fail(GQA_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", d->batch);
+  if (d->capacity < 1 || d->capacity > GQA_MAX_CAPACITY)
+    return fail(GQA_ERR_INVALID_ARG, "capacity must be in [1, %d] (got %d)", GQA_MAX_CAPACITY,
+                d->capacity);
+  if (d->q_dtype != GQA_F16 && d->q_dtype != GQA_BF16)
+    return fail(GQA_ERR_INVALID_ARG, "q dtype must be F16 or BF16 (got %d)", d->q_dtype);
+  const bool kv_ok = d->kv_dtype == GQA_FP8_E4M3 || d->kv_dtype == d->q_dtype;
+  if (!kv_ok)
+    return fail(GQA_ERR_INVALID_ARG,
+                "unsupported (q, kv) dtype pair (%d, %d): kv must match q or be FP8_E4M3",
+                d->q_dtype, d->kv_dtype);
+  if (!scale_ok(d->k_scale) || !scale_ok(d->v_scale))
+    return fail(GQA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
+  if (d->kv_dtype != GQA_FP8_E4M3 && (d->k_scale != 1.0f || d->v_scale != 1.0f))
+    return fail(GQA_ERR_INVALID_ARG,
+                "k_scale/v_scale apply to an fp8 cache only; a 16-bit cache needs 1.0");
+  if ((d->flags & ~GQA_FLAG_FUSED_COMBINE) != 0)
+    return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)d->flags);
+  return GQA_OK;
+}
+
+// Workspace: part_o [B,32,S,128] f32 | part_ml [B,32,S,2] f32 | counters [B,8] u32.
+struct WorkspaceLayout {
+  uint64_t ml_offset, counter_offset, total;
+};
+
+WorkspaceLayout workspace_layout(int64_t batch, int64_t splits) {
+  WorkspaceLayout w;
+  const uint64_t heads = (uint64_t)batch * GQA_NUM_Q_HEADS;
+  w.ml_offset = heads * (uint64_t)splits * GQA_HEAD_DIM * sizeof(float);
+  w.counter_offset = w.ml_offset + heads * (uint64_t)splits * 2 * sizeof(float);
+  w.total = w.counter_offset + (((uint64_t)batch * GQA_NUM_KV_HEADS * sizeof(uint32_t) + 255) & ~255ull);
+  return w;
+}
+
+gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p) {
+  const int64_t C = d->capacity;
+  const int64_t granules = (C + GQA_CHUNK_GRANULE - 1) / GQA_CHUNK_GRANULE;
+  int64_t chunk_granules;
+  if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", num_splits);
+  if (num_splits == 0) {
+    if (C <= GQA_SHORT_CAPACITY_MAX) {
+      chunk_granules = granules;
+    } else {
+      // Automatic: whole workgroup steps (64 tokens), about kTargetWorkgroups chunks.
+      constexpr int64_t kStepGranules = 64 / GQA_CHUNK_GRANULE;
+      const int64_t steps = (C + 63) / 64;
+      const int64_t total = std::max<int64_t>(1, (int64_t)d->batch * GQA_NUM_KV_HEADS * steps);
+      int64_t chunk_steps = std::max<int64_t>(1, (total + kTargetWorkgroups - 1) / kTargetWorkgroups);
+      chunk_steps = std::min(chunk_steps, steps);
+      chunk_granules = chunk_steps * kStepGranules;
+    }
+  } else if (num_splits == 1) {
+    chunk_granules = granules;
+  } else {
+    const int64_t per = (C + num_splits - 1) / num_splits;
+    chunk_granules = (per + GQA_CHUNK_GRANULE - 1) / GQA_CHUNK_GRANULE;
+    const int64_t chunk = chunk_granules * GQA_CHUNK_GRANULE;
+    if ((C + chunk - 1) / chunk != num_splits)
+      return fail(GQA_ERR_INVALID_ARG,
+                  "num_splits=%d cannot be honoured for capacity %lld with %d-token chunks "
+                  "(would give %lld); pass 0 for automatic",
+                  num_splits, (long long)C, GQA_CHUNK_GRANULE, (long long)((C + chunk - 1) / chunk));
+  }
+  const int64_t chunk = chunk_granules * GQA_CHUNK_GRANULE;
+  const int64_t S = (C + chunk - 1) / chunk;
+  const int64_t wgs = (int64_t)d->batch * GQA_NUM_KV_HEADS * S;
+  if (wgs > INT32_MAX) return fail(GQA_ERR_INVALID_ARG, "problem too large for one launch");
+  p->route = C <= GQA_SHORT_CAPACITY_MAX ? 0 : 1;
+  p->num_splits = (int32_t)S;
+  p->chunk_tokens = (int32_t)chunk;
+  p->num_workgroups = (int32_t)wgs;
+  p->workspace_bytes = S > 1 ? workspace_layout(d->batch, S).total : 0;
+  return GQA_OK;
+}
+
+gqa_status_t check_args(const gqa_desc_t* d, const void* q, const void* kv, const int32_t* lens,
+                        float q_scale, const void* out) {
+  gqa_status_t st = check_desc(d);
+  if (st != GQA_OK) return st;
+  if (!scale_ok(q_scale))
+    return fail(GQA_ERR_INVALID_ARG, "q_scale must be finite and > 0 (got %g)", (double)q_scale);
+  if (d->batch == 0) return GQA_OK;
+  if (!q || !kv || !lens || !out) return fail(GQA_ERR_INVALID_ARG, "q, kv, seq_lens and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(lens, 4))
+    return fail(GQA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned and seq_lens 4-byte aligned");
+  const size_t B = (size_t)d->batch;
+  const size_t q_bytes = B * GQA_NUM_Q_HEADS * GQA_HEAD_DIM * elem_bytes(d->q_dtype);
+  const size_t kv_bytes =
+      B * 2 * GQA_NUM_KV_HEADS * (size_t)d->capacity * GQA_HEAD_DIM * elem_bytes(d->kv_dtype);
+  const size_t len_bytes = B * sizeof(int32_t);
+  if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, kv, kv_bytes) ||
+      ranges_overlap(out, q_bytes, lens, len_bytes))
+    return fail(GQA_ERR_ALIAS, "out must not overlap q, kv or seq_lens");
+  return GQA_OK;
+}
+
+// --- device gate (gfx950 only) ------------------------------------------------
+std::mutex g_dev_mu;
+std::map<int, bool> g_dev_ok;
+
+gqa_status_t check_device(int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  *dev_out = dev;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  auto it = g_dev_ok.find(dev);
+  if (it == g_dev_ok.end()) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(GQA_ERR_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    const bool good = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    it = g_dev_ok.emplace(dev, good).first;
+    if (!good)
+      return fail(GQA_ERR_UNSUPPORTED_DEVICE, "device %d is %s; this library is built for gfx950",
+                  dev, prop.gcnArchName);
+  }
+  if (!it->second) return fail(GQA_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  return GQA_OK;
+}
+
+gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, const int32_t* lens,
+                        float q_scale, void* out, const gqa_plan_t& p, void* ws) {
+  gqa::StepArgs a;
+  a.q = q;
+  a.kv = kv;
+  a.seq_lens = lens;
+  a.out = out;
+  const WorkspaceLayout wl = workspace_layout(d->batch, p.num_splits);
+  char* base = static_cast<char*>(ws);
+  a.part_o = ws ? reinterpret_cast<float*>(base) : nullptr;
+  a.part_ml = ws ? reinterpret_cast<float*>(base + wl.ml_offset) : nullptr;
+  a.counters = ws ? reinterpret_cast<uint32_t*>(base + wl.counter_offset) : nullptr;
+  a.fused_combine = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
+  a.batch = d->batch;
+  a.capacity = d->capacity;
+  a.num_splits = p.num_splits;
+  a.chunk_tokens = p.chunk_tokens;
+  // log2-domain score scale, computed once on the host in double precision.
+  const double scale = (double)q_scale * (double)d->k_scale / std::sqrt((double)GQA_HEAD_DIM) /
+                       std::log(2.0);
+  a.scale_log2 = (float)scale;
+  a.v_scale = d->v_scale;
+  return a;
+}
+
+gqa_status_t enqueue(const gqa::StepArgs& a, const gqa_desc_t* d, hipStream_t stream,
+                     hipEvent_t ev_mid = nullptr) {
+  hipError_t e = gqa::enqueue_decode_step(a, d->q_dtype, d->kv_dtype, stream, ev_mid);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// --- convenience-call workspace cache, per (device, stream) ----------------------
+struct CacheEntry {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_cache_mu;
+std::map<std::pair<int, uintptr_t>, CacheEntry> g_cache;
+
+}  // namespace
+
+struct gqa_prepared {
+  gqa_desc_t desc;
+  gqa_plan_t plan;
+  const void* q;
+  const void* kv;
+  const int32_t* seq_lens;
+  void* out;
+  float q_scale;
+  void* workspace;
+  int device;
+};
+
+extern "C" {
+
+GQA_API const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+GQA_API gqa_status_t gqa_validate_args(const gqa_desc_t* desc, const void* q, const void* kv,
+                                       const int32_t* seq_lens, float q_scale, const void* out,
+                                       int32_t num_splits) {
+  gqa_status_t st = check_args(desc, q, kv, seq_lens, q_scale, out);
+  if (st != GQA_OK) return st;
+  gqa_plan_t p;
+  st = make_plan(desc, num_splits, &p);
+  if (st != GQA_OK) return st;
+  return ok();
+}
+
+GQA_API gqa_status_t gqa_plan_decode(const gqa_desc_t* desc, int32_t num_splits, gqa_plan_t* plan) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  gqa_status_t st = check_desc(desc);
+  if (st != GQA_OK) return st;
+  st = make_plan(desc, num_splits, plan);
+  if (st != GQA_OK) return st;
+  return ok();
+}
+
+GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
+                                        const int32_t* seq_lens, float q_scale, void* out,
+                                        int32_t num_splits, gqa_prepared_t** handle) {
+  if (handle == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  *handle = nullptr;
+  gqa_status_t st = check_args(desc, q, kv, seq_lens, q_scale, out);
+  if (st != GQA_OK) return st;
+  gqa_plan_t p;
+  st = make_plan(desc, num_splits, &p);
+  if (st != GQA_OK) return st;
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != GQA_OK) return st;
+  void* ws = nullptr;
+  if (p.workspace_bytes > 0 && desc->batch > 0) {
+    hipError_t e = hipMalloc(&ws, p.workspace_bytes);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(GQA_ERR_OUT_OF_MEMORY, "hipMalloc(%llu) for the split workspace failed: %s",
+                  (unsigned long long)p.workspace_bytes, hipGetErrorString(e));
+    }
+    // The per-head counters must start at zero; launches keep them at zero.
+    e = hipMemset(ws, 0, p.workspace_bytes);
+    if (e != hipSuccess) {
+      (void)hipFree(ws);
+      return fail(GQA_ERR_HIP, "hipMemset of the workspace failed: %s", hipGetErrorString(e));
+    }
+  }
+  gqa_prepared* h = new (std::nothrow) gqa_prepared;
+  if (h == nullptr) {
+    if (ws) (void)hipFree(ws);
+    return fail(GQA_ERR_OUT_OF_MEMORY, "out of host memory");
+  }
+  h->desc = *desc;
+  h->plan = p;
+  h->q = q;
+  h->kv = kv;
+  h->seq_lens = seq_lens;
+  h->out = out;
+  h->q_scale = q_scale;
+  h->workspace = ws;
+  h->device = dev;
+  *handle = h;
+  return ok();
+}
+
+GQA_API gqa_status_t launch_gqa_decode_prepared_timed(gqa_prepared_t* h, hipStream_t stream,
+                                                      hipEvent_t ev_start, hipEvent_t ev_mid,
+                                                      hipEvent_t ev_end) {
+  if (h == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  if (h->desc.batch == 0) return ok();
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (cur != h->device && (e = hipSetDevice(h->device)) != hipSuccess)
+    return fail(GQA_ERR_HIP, "hipSetDevice(%d) failed: %s", h->device, hipGetErrorString(e));
+  gqa_status_t st = GQA_OK;
+  if (ev_start != nullptr && (e = hipEventRecord(ev_start, stream)) != hipSuccess)
+    st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  if (st == GQA_OK) {
+    const gqa::StepArgs a =
+        step_args(&h->desc, h->q, h->kv, h->seq_lens, h->q_scale, h->out, h->plan, h->workspace);
+    st = enqueue(a, &h->desc, stream, ev_mid);
+  }
+  if (st == GQA_OK && ev_end != nullptr && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
+    st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  if (cur != h->device) (void)hipSetDevice(cur);
+  return st;
+}
+
+GQA_API gqa_status_t launch_gqa_decode_prepared(gqa_prepared_t* h, hipStream_t stream) {
+  return launch_gqa_decode_prepared_timed(h, stream, nullptr, nullptr, nullptr);
+}
+
+GQA_API void gqa_prepared_destroy(gqa_prepared_t* h) {
+  if (h == nullptr) return;
+  if (h->workspace) (void)hipFree(h->workspace);
+  delete h;
+}
+
+GQA_API size_t gqa_prepared_workspace_bytes(const gqa_prepared_t* h) {
+  return (h && h->workspace) ? (size_t)h->plan.workspace_bytes : 0;
+}
+
+GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* h, gqa_plan_t* plan) {
+  if (h == nullptr || plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
+  *plan = h->plan;
+  return ok();
+}
+
+GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
+                                const int32_t* seq_lens, float q_scale, void* out,
+                                hipStream_t stream) {
+  gqa_status_t st = check_args(desc, q, kv, seq_lens, q_scale, out);
+  if (st != GQA_OK) return st;
+  gqa_plan_t p;
+  st = make_plan(desc, 0, &p);
+  if (st != GQA_OK) return st;
+  if (desc->batch == 0) return ok();
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != GQA_OK) return st;
+
+  void* ws = nullptr;
+  if (p.workspace_bytes > 0) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    CacheEntry& ce = g_cache[{dev, reinterpret_cast<uintptr_t>(stream)}];
+    if (ce.bytes < p.workspace_bytes) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      hipError_t e = hipStreamIsCapturing(stream, &cs);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GQA_ERR_HIP, "hipStreamIsCapturing failed: %s", hipGetErrorString(e));
+      }
+      if (cs != hipStreamCaptureStatusNone)
+        return fail(GQA_ERR_CAPTURE,
+                    "gqa_decode would allocate %llu workspace bytes while the stream is "
+                    "capturing; use prepare_gqa_decode/launch_gqa_decode_prepared",
+                    (unsigned long long)p.workspace_bytes);
+      if (ce.ptr) {
+        // Work already enqueued on this stream may still use the old buffer.
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipStreamSynchronize failed: %s", hipGetErrorString(e));
+        (void)hipFree(ce.ptr);
+        ce.ptr = nullptr;
+        ce.bytes = 0;
+      }
+      e = hipMalloc(&ce.ptr, p.workspace_bytes);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        ce.ptr = nullptr;
+        return fail(GQA_ERR_OUT_OF_MEMORY, "hipMalloc(%llu) for the split workspace failed: %s",
+                    (unsigned long long)p.workspace_bytes, hipGetErrorString(e));
+      }
+      // Zero it (counters) on the stream, ahead of the launch that uses it.
+      e = hipMemsetAsync(ce.ptr, 0, p.workspace_bytes, stream);
+      if (e != hipSuccess) {
+        (void)hipFree(ce.ptr);
+        ce.ptr = nullptr;
+        return fail(GQA_ERR_HIP, "hipMemsetAsync of the workspace failed: %s", hipGetErrorString(e));
+      }
+      ce.bytes = p.workspace_bytes;
+    }
+    ws = ce.ptr;
+  }
+  return enqueue(step_args(desc, q, kv, seq_lens, q_scale, out, p, ws), desc, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,37 @@
+// Internal interface between the C-ABI layer (gqa_api.hip) and the gfx950
+// kernels (gqa_kernels.hip). Not installed; callers use include/gqa_decode.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace gqa {
+
+enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
+
+// Arguments of one decode step, passed to the kernels by value.
+struct StepArgs {
+  const void* q;             // [batch, 32, 128] q dtype
+  const void* kv;            // [batch, 2, 8, capacity, 128] kv dtype
+  const int32_t* seq_lens;   // [batch]
+  void* out;                 // [batch, 32, 128] q dtype
+  float* part_o;             // [batch, 32, num_splits, 128] unnormalised chunk outputs
+  float* part_ml;            // [batch, 32, num_splits, 2] chunk (max, sum), log2 domain
+  uint32_t* counters;        // [batch, 8] finished chunks per (request, KV head); 0 between launches
+  int32_t batch;
+  int32_t capacity;
+  int32_t num_splits;        // chunks per (request, KV head); 1 = normalise in place
+  int32_t chunk_tokens;      // multiple of 16
+  float scale_log2;          // q_scale * k_scale * log2(e) / sqrt(128)
+  float v_scale;
+  int32_t fused_combine;     // 1: last workgroup of a head combines; 0: separate combine kernel
+};
+
+// Enqueue the attention kernel (and, for num_splits > 1, the combine kernel).
+// Returns the first launch error. Arguments are assumed validated. When given,
+// `ev_mid` is recorded between the two kernels (or after the only one).
+hipError_t enqueue_decode_step(const StepArgs& args, int q_dtype, int kv_dtype,
+                               hipStream_t stream, hipEvent_t ev_mid = nullptr);
+
+}  // namespace gqa

@@ -1,0 +1,552 @@
+// gfx950 kernels for single-token grouped-query decode attention.
+//
+// The step (FlashInfer sm110_gqa_decode article, "input contract" and
+// "convenience API"): 4 query rows of one request share one KV head; scores
+// are taken in the log2 domain, exp2(scale_log2 * s) with
+// scale_log2 = q_scale / sqrt(128) / ln 2 (times k_scale for an fp8 cache,
+// Thor FP8 KV notes, patch 2), and the output is the softmax-weighted sum of
+// the V rows of the valid prefix, times v_scale.
+//
+// Work split. A workgroup (4 waves of 64 lanes) owns one chunk of one
+// (request, KV head): `chunk_tokens` consecutive cache slots. Within the
+// chunk the waves take 16-token tiles round-robin. Every chunk keeps an fp32
+// online softmax (running max m, running sum l, unnormalised output O) in the
+// log2 domain; the 4 waves merge through LDS at the end. With one chunk per
+// head the workgroup normalises and writes the output; otherwise it writes
+// (m, l, O) as FP32 partials — the split-KV scheme of the article's
+// "default routes and num_splits" section — and a log-sum-exp combine kernel
+// merges the chunks of each query head.
+//
+// Tile math on the matrix cores. The 4 grouped query rows form a 16-row MFMA
+// operand (rows 4..15 zero; the cores have ~10x the throughput this stream
+// needs, so the padding costs nothing measurable):
+//   scores^T[16 tok, 16 rows] = K_tile[16 tok, 128] x Q^T[128, 16]
+//       4 x v_mfma_f32_16x16x32_{bf16,f16}; K arrives straight from HBM in
+//       the A-operand layout (lane = token, 8 consecutive dims per lane).
+//   O[16 rows, 128]           += P[16 rows, 16 tok] x V_tile[16 tok, 128]
+//       8 x v_mfma_f32_16x16x16_{bf16,f16}; the score accumulator already is
+//       the P A-operand layout, and each lane loads 16 contiguous bytes of a
+//       V row (a wave covers 4 whole rows per load), which a byte permute
+//       turns into the B-operand layout (4 tokens of one dim per lane).
+// fp8 e4m3 K/V bytes are widened to bf16/f16 in registers with the gfx950
+// packed converts (exact: every e4m3 value is representable), so the cache
+// is read once, at 1 byte per element.
+//
+// Loads are raw buffer loads whose range ends at the chunk's last valid
+// slot: slots past the request's length are never fetched (they read as 0
+// without touching memory), which also makes the one-tile-ahead prefetch
+// free at the end of a chunk.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gqa_kernels.h"
+
+namespace gqa {
+namespace {
+
+constexpr int kHeadDim = 128;
+constexpr int kQHeads = 32;
+constexpr int kKvHeads = 8;
+constexpr int kGroup = 4;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16;               // tokens per wave step
+constexpr int kStep = kTile * kWaves;   // tokens per workgroup step
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
+
+// Build-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef GQA_MIN_WAVES_PER_SIMD
+#define GQA_MIN_WAVES_PER_SIMD 2
+#endif
+#ifndef GQA_KV_LOAD_POLICY
+#define GQA_KV_LOAD_POLICY 0   // cache-policy bits of the K/V buffer loads
+#endif
+constexpr int kLoadAux = GQA_KV_LOAD_POLICY;
+
+typedef uint32_t u32;
+typedef u32 u32x4 __attribute__((ext_vector_type(4)));
+typedef u32 u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Element-type traits for the MFMA operand type (= query dtype).
+// ---------------------------------------------------------------------------
+template <int QT>
+struct Elem;
+
+template <>
+struct Elem<kBF16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 p, u32x2 v, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, p),
+                                                     __builtin_bit_cast(i16x4, v), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ u32 pack(float a, float b) {
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(u32, v);
+  }
+  static __device__ __forceinline__ float lo(u32 x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float hi(u32 x) { return __uint_as_float(x & 0xffff0000u); }
+  // Two e4m3 codes (bytes 2*sel, 2*sel+1 of x) -> two bf16 (exact).
+  template <bool kHiWord>
+  static __device__ __forceinline__ u32 from_fp8(u32 x) {
+    return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, kHiWord));
+  }
+  static __device__ __forceinline__ void store2(void* p, float a, float b) {
+    *reinterpret_cast<u32*>(p) = pack(a, b);
+  }
+};
+
+template <>
+struct Elem<kF16> {
+  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 pv(u32x2 p, u32x2 v, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, p),
+                                                 __builtin_bit_cast(f16x4, v), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ u32 pack(float a, float b) {
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(u32, v);
+  }
+  static __device__ __forceinline__ float lo(u32 x) {
+    return (float)__builtin_bit_cast(f16x2, x)[0];
+  }
+  static __device__ __forceinline__ float hi(u32 x) {
+    return (float)__builtin_bit_cast(f16x2, x)[1];
+  }
+  template <bool kHiWord>
+  static __device__ __forceinline__ u32 from_fp8(u32 x) {
+    return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, kHiWord));
+  }
+  static __device__ __forceinline__ void store2(void* p, float a, float b) {
+    *reinterpret_cast<u32*>(p) = pack(a, b);
+  }
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Dim-block (8 dims) that lane group `grp` feeds to QK instruction `i`.
+// 16-bit cache: load i covers bytes [64i, 64i+64) of 16 rows, block 4i+grp.
+// fp8 cache:    load p covers bytes [64p, 64p+64); its two halves feed
+//               instructions 2p and 2p+1, blocks 8p + 2grp + {0,1}.
+template <int KVT>
+__device__ __forceinline__ int qk_dim_block(int i, int grp) {
+  if constexpr (KVT == kFP8) {
+    return 8 * (i >> 1) + 2 * grp + (i & 1);
+  } else {
+    return 4 * i + grp;
+  }
+}
+
+// Registers of one 16-token tile.
+template <int KVT>
+struct Tile;
+
+template <>
+struct Tile<kF16> {
+  u32x4 k[4];  // K: token n16, dim block 4i+grp
+  u32x4 v[4];  // V: token 4grp+e, dims [8 n16, 8 n16 + 8)
+};
+template <>
+struct Tile<kBF16> : Tile<kF16> {};
+template <>
+struct Tile<kFP8> {
+  u32x4 k[2];  // K: token n16, bytes [64p + 16grp, +16)
+  u32x2 v[4];  // V: token 4grp+e, dims [8 n16, 8 n16 + 8)
+};
+
+template <int KVT>
+__device__ __forceinline__ void load_tile(Tile<KVT>& t, __amdgpu_buffer_rsrc_t rk,
+                                          __amdgpu_buffer_rsrc_t rv, int j0, int n16, int grp) {
+  if constexpr (KVT == kFP8) {
+    const int ko = (j0 + n16) * kHeadDim + 16 * grp;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) t.k[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * p, 0, kLoadAux);
+    const int vo = (j0 + 4 * grp) * kHeadDim + 8 * n16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      t.v[e] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + e * kHeadDim, 0, kLoadAux);
+  } else {
+    const int ko = (j0 + n16) * (2 * kHeadDim) + 16 * grp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * i, 0, kLoadAux);
+    const int vo = (j0 + 4 * grp) * (2 * kHeadDim) + 16 * n16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      t.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + e * (2 * kHeadDim), 0, kLoadAux);
+  }
+}
+
+// Running state of one wave.
+struct Softmax {
+  float m;      // running max of log2-domain scores of row n16 (uniform per row)
+  float l;      // this lane's share of the running sum
+  f32x4 o[8];   // O[row 4grp+r][dim 8 n16 + c] in o[c][r] (rows 0..3 live in grp 0)
+};
+
+template <int QT, int KVT>
+__device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, const u32x4 (&qf)[4],
+                                             int j0, int c1, int grp, float scale_log2) {
+  using E = Elem<QT>;
+  // ---- scores^T[token 4grp + r][row n16] ------------------------------------
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KVT == kFP8) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32 w0 = t.k[p][2 * h], w1 = t.k[p][2 * h + 1];
+        u32x4 kk = {E::template from_fp8<false>(w0), E::template from_fp8<true>(w0),
+                    E::template from_fp8<false>(w1), E::template from_fp8<true>(w1)};
+        s = E::qk(kk, qf[2 * p + h], s);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = E::qk(t.k[i], qf[i], s);
+  }
+
+  // ---- online softmax, log2 domain -----------------------------------------
+  float x[4];
+  const int tok0 = j0 + 4 * grp;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (tok0 + r < c1) ? s[r] * scale_log2 : -INFINITY;
+  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);   // finite: the tile holds >= 1 valid token
+  const float alpha = fast_exp2(st.m - m_new);
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[r] - m_new);
+  const u32 p01 = E::pack(p[0], p[1]);
+  const u32 p23 = E::pack(p[2], p[3]);
+  // bf16 keeps 8 significant bits of a weight; the PV product then takes the
+  // weights as hi + lo bf16 pairs (16 bits), so only fp32 rounding is left and
+  // l sums the fp32 weights. f16 weights (11 bits) go in one piece and l sums
+  // the rounded weights the product sees.
+  u32 q01 = 0u, q23 = 0u;
+  if constexpr (QT == kBF16) {
+    q01 = E::pack(p[0] - E::lo(p01), p[1] - E::hi(p01));
+    q23 = E::pack(p[2] - E::lo(p23), p[3] - E::hi(p23));
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  } else {
+    st.l = st.l * alpha + ((E::lo(p01) + E::hi(p01)) + (E::lo(p23) + E::hi(p23)));
+  }
+  st.m = m_new;
+
+  // Rows 0..3 of O live in lanes 0..15; they need alpha of rows 0..3.
+  const float al0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
+  const float al1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
+  const float al2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
+  const float al3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
+  if (al0 != 1.f || al1 != 1.f || al2 != 1.f || al3 != 1.f) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      st.o[c][0] *= al0;
+      st.o[c][1] *= al1;
+      st.o[c][2] *= al2;
+      st.o[c][3] *= al3;
+    }
+  }
+
+  // ---- O += P x V ------------------------------------------------------------
+  const u32x2 pa = {p01, p23};
+  const u32x2 pl = {q01, q23};
+  auto pv = [&](f32x4 acc, u32x2 bv) {
+    acc = E::pv(pa, bv, acc);
+    if constexpr (QT == kBF16) acc = E::pv(pl, bv, acc);
+    return acc;
+  };
+  if constexpr (KVT == kFP8) {
+    // For dim 8 n16 + c the B operand is {V[tok0+0..3][c]}: interleave the
+    // bytes of two tokens, then widen byte pairs.
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      u32 lo_a[2], lo_b[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const u32 x0 = t.v[2 * q][w], x1 = t.v[2 * q + 1][w];
+        lo_a[q] = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
+        lo_b[q] = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
+      }
+      const u32x2 b0 = {E::template from_fp8<false>(lo_a[0]), E::template from_fp8<false>(lo_a[1])};
+      const u32x2 b1 = {E::template from_fp8<true>(lo_a[0]), E::template from_fp8<true>(lo_a[1])};
+      const u32x2 b2 = {E::template from_fp8<false>(lo_b[0]), E::template from_fp8<false>(lo_b[1])};
+      const u32x2 b3 = {E::template from_fp8<true>(lo_b[0]), E::template from_fp8<true>(lo_b[1])};
+      st.o[4 * w + 0] = pv(st.o[4 * w + 0], b0);
+      st.o[4 * w + 1] = pv(st.o[4 * w + 1], b1);
+      st.o[4 * w + 2] = pv(st.o[4 * w + 2], b2);
+      st.o[4 * w + 3] = pv(st.o[4 * w + 3], b3);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u32 v0 = t.v[0][w], v1 = t.v[1][w], v2 = t.v[2][w], v3 = t.v[3][w];
+      const u32x2 be = {(v0 & 0xffffu) | (v1 << 16), (v2 & 0xffffu) | (v3 << 16)};
+      const u32x2 bo = {(v0 >> 16) | (v1 & 0xffff0000u), (v2 >> 16) | (v3 & 0xffff0000u)};
+      st.o[2 * w + 0] = pv(st.o[2 * w + 0], be);
+      st.o[2 * w + 1] = pv(st.o[2 * w + 1], bo);
+    }
+  }
+}
+
+// How a workgroup finishes its chunk.
+enum Mode : int {
+  kModeDirect = 0,      // single chunk per head: normalise and write the output
+  kModeSplit = 1,       // write the chunk partial; a separate kernel combines
+  kModeSplitFused = 2,  // write the partial; the head's last workgroup combines
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Log-sum-exp merge of the chunk partials of the 4 query heads of (request b,
+// KV head g): wave r takes head 4g + r, lane l dims 2l and 2l + 1.
+//   M = max_s m_s,  out = v_scale * sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// Only the chunks that start below the current length are read, so partials
+// left by an earlier launch with longer lengths never enter the result.
+template <int QT>
+__device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int g, int L) {
+  using E = Elem<QT>;
+  const int lane = threadIdx.x & 63;
+  const int r = threadIdx.x >> 6;
+  const int S = a.num_splits;
+  const size_t head = (size_t)b * kQHeads + kGroup * g + r;
+  char* outp = static_cast<char*>(a.out) + (head * kHeadDim + 2 * lane) * 2;
+  const int n = (L + a.chunk_tokens - 1) / a.chunk_tokens;
+  if (n == 0) {
+    E::store2(outp, 0.f, 0.f);
+    return;
+  }
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + head * S;
+  const float2* po = reinterpret_cast<const float2*>(a.part_o + head * (size_t)S * kHeadDim) + lane;
+  float mloc = -INFINITY;
+  for (int s = lane; s < n; s += 64) mloc = fmaxf(mloc, ml[s].x);
+  const float M = wave_max(mloc);   // every valid chunk has a finite max
+  float lloc = 0.f;
+  for (int s = lane; s < n; s += 64) {
+    const float2 v = ml[s];
+    lloc += fast_exp2(v.x - M) * v.y;
+  }
+  const float l = wave_sum(lloc);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < n; ++s) {
+    const float f = fast_exp2(ml[s].x - M);
+    const float2 v = po[(size_t)s * (kHeadDim / 2)];
+    o0 += f * v.x;
+    o1 += f * v.y;
+  }
+  const float inv = a.v_scale / l;
+  E::store2(outp, o0 * inv, o1 * inv);
+}
+
+template <int QT, int KVT, int kMode>
+__global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attention_kernel(StepArgs a) {
+  using E = Elem<QT>;
+  constexpr int kKvBytes = (KVT == kFP8) ? 1 : 2;
+  constexpr int kRowBytes = kHeadDim * kKvBytes;
+
+  __shared__ float s_o[kWaves][kGroup][kHeadDim];
+  __shared__ float s_m[kWaves][kGroup];
+  __shared__ float s_l[kWaves][kGroup];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n16 = lane & 15;
+  const int grp = lane >> 4;
+
+  const int S = a.num_splits;
+  const int split = (int)blockIdx.x % S;
+  const int bg = (int)blockIdx.x / S;
+  const int g = bg % kKvHeads;
+  const int b = bg / kKvHeads;
+  const int C = a.capacity;
+  const int L = min(max(a.seq_lens[b], 0), C);
+  const int c0 = split * a.chunk_tokens;
+
+  // Epilogue coordinates: 256 threads cover 4 rows x 64 dim pairs.
+  const int er = tid >> 6;
+  const int ed = (tid & 63) * 2;
+  const size_t head = (size_t)b * kQHeads + kGroup * g + er;
+
+  if (c0 >= L) {
+    // Chunks past the length take no part. An empty request (L = 0) has no
+    // chunk at all: unless a combine kernel follows, chunk 0 writes its zeros.
+    if (kMode != kModeSplit && split == 0)
+      E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, 0.f, 0.f);
+    return;
+  }
+  const int c1 = min(c0 + a.chunk_tokens, L);
+
+  const char* kvb = static_cast<const char*>(a.kv);
+  const size_t plane = (size_t)C * kRowBytes;
+  const char* kplane = kvb + ((size_t)(b * 2 + 0) * kKvHeads + g) * plane;
+  const char* vplane = kvb + ((size_t)(b * 2 + 1) * kKvHeads + g) * plane;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kplane, (u32)c1 * kRowBytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vplane, (u32)c1 * kRowBytes);
+
+  // Query fragment: B operand of the QK product, row n16 (< 4), dim block per
+  // instruction as the K loads deliver it. Rows 4..15 are zero.
+  u32x4 qf[4];
+  {
+    const char* qrow = static_cast<const char*>(a.q) +
+                       ((size_t)b * kQHeads + kGroup * g + (n16 & 3)) * (kHeadDim * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * qk_dim_block<KVT>(i, grp));
+      qf[i] = (n16 < kGroup) ? v : (u32x4){0u, 0u, 0u, 0u};
+    }
+  }
+
+  Softmax st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  int j0 = c0 + kTile * wave;
+  if (j0 < c1) {
+    Tile<KVT> ta, tb;
+    load_tile<KVT>(ta, rk, rv, j0, n16, grp);
+    for (;;) {
+      load_tile<KVT>(tb, rk, rv, j0 + kStep, n16, grp);   // past c1: reads 0, no traffic
+      process_tile<QT, KVT>(st, ta, qf, j0, c1, grp, a.scale_log2);
+      j0 += kStep;
+      if (j0 >= c1) break;
+      load_tile<KVT>(ta, rk, rv, j0 + kStep, n16, grp);
+      process_tile<QT, KVT>(st, tb, qf, j0, c1, grp, a.scale_log2);
+      j0 += kStep;
+      if (j0 >= c1) break;
+    }
+  }
+
+  // ---- merge the 4 waves ----------------------------------------------------
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (lane < kGroup) {
+    s_m[wave][lane] = st.m;
+    s_l[wave][lane] = l;
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4* dst = reinterpret_cast<float4*>(&s_o[wave][r][8 * n16]);
+      dst[0] = make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
+      dst[1] = make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
+    }
+  }
+  __syncthreads();
+
+  float M = s_m[0][er];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][er]);
+  float o0 = 0.f, o1 = 0.f, lsum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float f = fast_exp2(s_m[w][er] - M);  // idle waves: m = -inf -> 0
+    o0 += f * s_o[w][er][ed];
+    o1 += f * s_o[w][er][ed + 1];
+    lsum += f * s_l[w][er];
+  }
+
+  if constexpr (kMode == kModeDirect) {
+    const float inv = a.v_scale / lsum;
+    E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
+  } else {
+    const size_t slot = head * (size_t)S + split;
+    *reinterpret_cast<float2*>(a.part_o + slot * kHeadDim + ed) = make_float2(o0, o1);
+    if ((tid & 63) == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(M, lsum);
+    if constexpr (kMode == kModeSplitFused) {
+      // Publish this chunk, count it, and let the head's last chunk combine.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned n_valid = (unsigned)((L + a.chunk_tokens - 1) / a.chunk_tokens);
+        const unsigned prev = atomicAdd(a.counters + bg, 1u);
+        const int last = (prev + 1u == n_valid);
+        if (last) atomicExch(a.counters + bg, 0u);   // ready for the next launch
+        s_last = last;
+      }
+      __syncthreads();
+      if (!s_last) return;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      combine_head_group<QT>(a, b, g, L);
+    }
+  }
+}
+
+// Separate log-sum-exp combine: one workgroup per (request, KV head).
+template <int QT>
+__global__ __launch_bounds__(kThreads) void gqa_combine_kernel(StepArgs a) {
+  const int bg = blockIdx.x;
+  const int b = bg / kKvHeads;
+  const int L = min(max(a.seq_lens[b], 0), a.capacity);
+  combine_head_group<QT>(a, b, bg % kKvHeads, L);
+}
+
+template <int QT, int KVT>
+hipError_t enqueue_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
+  const unsigned wgs = (unsigned)a.batch * kKvHeads * (unsigned)a.num_splits;
+  hipError_t e;
+  const bool separate = a.num_splits > 1 && !a.fused_combine;
+  if (a.num_splits == 1) {
+    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, kModeDirect>), dim3(wgs), dim3(kThreads), 0,
+                       stream, a);
+  } else if (separate) {
+    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, kModeSplit>), dim3(wgs), dim3(kThreads), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, kModeSplitFused>), dim3(wgs), dim3(kThreads),
+                       0, stream, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev_mid != nullptr && (e = hipEventRecord(ev_mid, stream)) != hipSuccess) return e;
+  if (!separate) return hipSuccess;
+  hipLaunchKernelGGL((gqa_combine_kernel<QT>), dim3((unsigned)a.batch * kKvHeads), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t enqueue_decode_step(const StepArgs& a, int q_dtype, int kv_dtype, hipStream_t stream,
+                               hipEvent_t ev_mid) {
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return enqueue_typed<kBF16, kBF16>(a, stream, ev_mid);
+  if (q_dtype == kF16 && kv_dtype == kF16) return enqueue_typed<kF16, kF16>(a, stream, ev_mid);
+  if (q_dtype == kBF16 && kv_dtype == kFP8) return enqueue_typed<kBF16, kFP8>(a, stream, ev_mid);
+  if (q_dtype == kF16 && kv_dtype == kFP8) return enqueue_typed<kF16, kFP8>(a, stream, ev_mid);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gqa

@@ -1,0 +1,197 @@
+/*
+ * gqa_decode.h — C ABI of the MI355X (gfx950) single-token grouped-query
+ * decode-attention library (libgqa_decode.so).
+ *
+ * Operation. For every request b and query head h (32 per request, sharing
+ * 8 KV heads, head dimension 128, so head h reads KV head h / 4):
+ *
+ *     s_j     = q_scale * k_scale / sqrt(128) * dot(q[b,h,:], K[b,h/4,j,:])
+ *     out[b,h,:] = v_scale * sum_{j < L_b} softmax_j(s) * V[b,h/4,j,:]
+ *
+ * with L_b = seq_lens[b]. Sources: the FlashInfer sm110_gqa_decode article
+ * (cf-1.com news 5454068): "why a separate SM110 GQA decode path" (fixed
+ * 32/8/128 geometry, one query token per request), "input contract" (layout
+ * and the device-only lengths), "convenience API" (signature, the grouped
+ * q view, the log2-domain scale), "prepared continuous decode" (prepare
+ * phase, the three differences, lifecycle and concurrency, num_splits and
+ * the FP32 split workspace); and the Thor FP8 KV-cache porting notes
+ * (kipfel.ltd), section 1, patches 1-2 (uint8 bytes reinterpreted as
+ * float8_e4m3fn; scores *= k_scale, normalised output *= v_scale).
+ *
+ * Layouts (all dense, contiguous, row-major, device memory, 16-byte aligned):
+ *   q        [batch, 32, 128]                  q_dtype (F16 or BF16)
+ *   kv       [batch, 2, 8, capacity, 128]      kv_dtype; plane 0 = K, 1 = V
+ *                                              (FP8: OCP E4M3FN bytes)
+ *   seq_lens [batch] int32, read on the device only (4-byte aligned)
+ *   out      [batch, 32, 128]                  q_dtype (written by the call)
+ *
+ * Ownership. The caller owns q, kv, seq_lens and out and must keep them
+ * alive until the enqueued work (and any captured graph containing it)
+ * has retired. A prepared handle stores their addresses, never copies, and
+ * owns only its split workspace.
+ *
+ * Lengths. Keeping 1 <= seq_lens[b] <= capacity is the caller's job; the
+ * host never reads them. Kernels clamp each length to [0, capacity] so they
+ * never read outside the cache: a length <= 0 yields an all-zero output row
+ * block and a length > capacity behaves as capacity. Slots at or beyond the
+ * length are never loaded (their contents, NaN included, cannot matter).
+ *
+ * Errors. Every entry point returns a gqa_status_t and never throws. On any
+ * error nothing is enqueued and out is untouched; gqa_last_error() returns a
+ * thread-local message describing the most recent failure on this thread.
+ * Every kernel launch is checked.
+ */
+#ifndef GQA_DECODE_H_
+#define GQA_DECODE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_API __attribute__((visibility("default")))
+
+#define GQA_NUM_Q_HEADS 32
+#define GQA_NUM_KV_HEADS 8
+#define GQA_HEAD_DIM 128
+/* Capacities up to this value take the short route (one workgroup per
+ * (request, KV head), no workspace), as the article's routing paragraph
+ * does for capacity <= 64. */
+#define GQA_SHORT_CAPACITY_MAX 64
+/* Split chunks are multiples of this many tokens (one wave tile). */
+#define GQA_CHUNK_GRANULE 16
+/* Largest accepted capacity (keeps every per-head K/V plane below 2 GiB). */
+#define GQA_MAX_CAPACITY (1 << 22)
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARG = 1,        /* bad pointer, geometry, dtype, scale, split */
+  GQA_ERR_ALIAS = 2,              /* out overlaps q, kv or seq_lens */
+  GQA_ERR_UNSUPPORTED_DEVICE = 3, /* current device is not gfx950 */
+  GQA_ERR_CAPTURE = 4,            /* convenience call would allocate during capture */
+  GQA_ERR_OUT_OF_MEMORY = 5,      /* workspace allocation failed */
+  GQA_ERR_HIP = 6                 /* a HIP runtime call or launch failed */
+} gqa_status_t;
+
+typedef enum gqa_dtype {
+  GQA_F16 = 0,
+  GQA_BF16 = 1,
+  GQA_FP8_E4M3 = 2 /* KV only: OCP E4M3FN bytes (torch.float8_e4m3fn) */
+} gqa_dtype_t;
+
+/* Problem descriptor. Fields are int32/float so the struct has one layout
+ * for every caller. Accepted dtype pairs (q, kv): (F16, F16), (BF16, BF16),
+ * (F16, FP8_E4M3), (BF16, FP8_E4M3). out has q's dtype. k_scale and v_scale
+ * must be finite and > 0, and must equal 1.0 unless kv is FP8_E4M3 (a scale
+ * on a 16-bit cache is rejected rather than silently ignored). */
+typedef struct gqa_desc {
+  int32_t batch;        /* >= 0; 0 makes every call a no-op */
+  int32_t capacity;     /* 1 .. GQA_MAX_CAPACITY (kv.shape[-2]) */
+  int32_t num_q_heads;  /* must be 32 */
+  int32_t num_kv_heads; /* must be 8 */
+  int32_t head_dim;     /* must be 128 */
+  int32_t q_dtype;      /* gqa_dtype_t */
+  int32_t kv_dtype;     /* gqa_dtype_t */
+  float k_scale;        /* multiplies every score (fp8 cache) */
+  float v_scale;        /* multiplies the normalised output (fp8 cache) */
+  int32_t flags;        /* GQA_FLAG_* bits; 0 for the defaults */
+} gqa_desc_t;
+
+/* Split plans merge their chunks with a log-sum-exp combine kernel launched
+ * right after the attention kernel on the same stream. With this flag the
+ * last workgroup to finish a (request, KV head) merges inside the attention
+ * kernel instead (one launch; a per-head counter in the workspace, reset by
+ * that workgroup, tells it that it is last). The fused form needs an
+ * agent-scope release/acquire fence pair around every workgroup's partial,
+ * which on a multi-XCD part costs more than the second launch saves, so it
+ * is opt-in. */
+#define GQA_FLAG_FUSED_COMBINE 1
+
+/* Launch plan chosen for a descriptor (host arithmetic only). */
+typedef struct gqa_plan {
+  int32_t route;           /* 0 = short (capacity <= 64), 1 = split */
+  int32_t num_splits;      /* chunks per (request, KV head); 1 = no combine */
+  int32_t chunk_tokens;    /* tokens per chunk, a multiple of GQA_CHUNK_GRANULE */
+  int32_t num_workgroups;  /* workgroups of the attention kernel */
+  uint64_t workspace_bytes;/* FP32 partials (+ per-head counters); 0 when num_splits == 1 */
+} gqa_plan_t;
+
+typedef struct gqa_prepared gqa_prepared_t;
+
+/* Convenience call: validate, plan (num_splits chosen automatically) and
+ * enqueue the whole decode step on `stream`, asynchronously. Split partials
+ * live in a library-owned workspace cached per (device, stream) that only
+ * grows; growing it allocates, so a call made while `stream` is capturing
+ * that would need to grow it returns GQA_ERR_CAPTURE instead. Calls on the
+ * same stream are ordered and may share the cache; the prepared pair below
+ * is the capture-safe interface. */
+GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
+                                const int32_t* seq_lens, float q_scale, void* out,
+                                hipStream_t stream);
+
+/* Prepare phase (run outside any capture): validates the descriptor and the
+ * buffers (non-null, 16-byte aligned, out not overlapping q/kv/seq_lens by
+ * address range), requires q_scale finite and > 0, picks the route, and
+ * allocates the FP32 split workspace once with hipMalloc on the current
+ * device. num_splits: 0 = automatic; 1 = one chunk per (request, KV head)
+ * with the output normalised in place; n >= 2 = exactly n chunks — a value
+ * the chunking cannot honour exactly (ceil(capacity / chunk) != n with chunk
+ * a multiple of 16) is rejected with GQA_ERR_INVALID_ARG, never replaced.
+ * On success *handle owns the workspace; release it with
+ * gqa_prepared_destroy. */
+GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q,
+                                        const void* kv, const int32_t* seq_lens,
+                                        float q_scale, void* out, int32_t num_splits,
+                                        gqa_prepared_t** handle);
+
+/* Enqueue a prepared decode step on `stream`: no allocation, no host read of
+ * device memory, no synchronisation — hipGraph-capturable. Buffer contents
+ * (q, kv, seq_lens within [1, capacity]) may change between launches. The
+ * workspace is mutable: a handle must not run on two unordered streams (or
+ * graphs) at once; streams ordered by events may share it. Partials of an
+ * earlier launch are never read: the combine derives the number of valid
+ * chunks from the current lengths. */
+GQA_API gqa_status_t launch_gqa_decode_prepared(gqa_prepared_t* handle, hipStream_t stream);
+
+/* launch_gqa_decode_prepared with instrumentation: records `ev_start` on
+ * `stream` before the attention kernel, `ev_mid` right after it and `ev_end`
+ * after the combine kernel (immediately after `ev_mid` when there is no
+ * combine). The events must have been created by the caller on the handle's
+ * device; any of them may be NULL to skip it. For timing tools. */
+GQA_API gqa_status_t launch_gqa_decode_prepared_timed(gqa_prepared_t* handle, hipStream_t stream,
+                                                      hipEvent_t ev_start, hipEvent_t ev_mid,
+                                                      hipEvent_t ev_end);
+
+/* Free the workspace and the handle (after its work has retired). NULL is a no-op. */
+GQA_API void gqa_prepared_destroy(gqa_prepared_t* handle);
+
+/* Workspace bytes owned by the handle (0 for NULL or single-chunk plans). */
+GQA_API size_t gqa_prepared_workspace_bytes(const gqa_prepared_t* handle);
+
+/* Copy of the handle's launch plan; GQA_ERR_INVALID_ARG for NULL arguments. */
+GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* handle, gqa_plan_t* plan);
+
+/* Host-only validation of a call's arguments (never touches a device, so it
+ * runs without a GPU). Same checks and status codes as prepare_gqa_decode,
+ * except the device check. */
+GQA_API gqa_status_t gqa_validate_args(const gqa_desc_t* desc, const void* q, const void* kv,
+                                       const int32_t* seq_lens, float q_scale,
+                                       const void* out, int32_t num_splits);
+
+/* Host-only planning: the route, chunking and workspace a call would use
+ * (num_splits as for prepare_gqa_decode). Runs without a GPU. */
+GQA_API gqa_status_t gqa_plan_decode(const gqa_desc_t* desc, int32_t num_splits,
+                                     gqa_plan_t* plan);
+
+/* Thread-local description of the last error on this thread ("" if none). */
+GQA_API const char* gqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H_ */

@@ -1,0 +1,173 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared
+symbol, and its host-only validation and planning behave as documented.
+No device is touched (validation never dereferences a pointer)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_decode.h")
+
+b = pytest.importorskip("gqa_kv_cache_attn_amd.binding")
+
+OK, INVALID, ALIAS = b.GQA_OK, b.GQA_ERR_INVALID_ARG, b.GQA_ERR_ALIAS
+MiB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"GQA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_three_page_entry_points():
+    names = declared_functions()
+    for n in ("gqa_decode", "prepare_gqa_decode", "launch_gqa_decode_prepared"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(b.library_path)
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def desc(batch=2, capacity=1024, q=b.GQA_BF16, kv=b.GQA_BF16, ks=1.0, vs=1.0, hq=32, hkv=8, d=128):
+    return b.GqaDesc(batch=batch, capacity=capacity, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                     q_dtype=q, kv_dtype=kv, k_scale=ks, v_scale=vs)
+
+
+# Fake, well-separated, aligned device addresses: validation only compares them.
+Q, KV, LENS, OUT = 1 * 1024 * MiB, 2 * 1024 * MiB, 3 * 1024 * MiB, 4 * 1024 * MiB
+
+
+def v(d, q=Q, kv=KV, lens=LENS, qs=1.0, out=OUT, ns=0):
+    return b.gqa_validate_args(d, q, kv, lens, qs, out, ns)
+
+
+def test_valid_arguments_pass():
+    assert v(desc()) == OK
+    assert v(desc(q=b.GQA_F16, kv=b.GQA_F16)) == OK
+    assert v(desc(q=b.GQA_BF16, kv=b.GQA_FP8_E4M3, ks=1 / 64, vs=1 / 64)) == OK
+    assert v(desc(q=b.GQA_F16, kv=b.GQA_FP8_E4M3)) == OK
+
+
+@pytest.mark.parametrize("field,value", [("num_q_heads", 16), ("num_kv_heads", 4), ("head_dim", 64),
+                                         ("capacity", 0), ("capacity", -3), ("batch", -1),
+                                         ("capacity", (1 << 22) + 1)])
+def test_fixed_geometry_and_sizes(field, value):
+    d = desc()
+    setattr(d, field, value)
+    assert v(d) == INVALID
+    assert b.last_error()
+
+
+@pytest.mark.parametrize("q,kv", [(b.GQA_F16, b.GQA_BF16), (b.GQA_BF16, b.GQA_F16),
+                                  (b.GQA_FP8_E4M3, b.GQA_FP8_E4M3), (7, b.GQA_BF16),
+                                  (b.GQA_BF16, 9)])
+def test_unsupported_dtype_pairs(q, kv):
+    assert v(desc(q=q, kv=kv)) == INVALID
+
+
+@pytest.mark.parametrize("qs", [0.0, -1.0, math.nan, math.inf, -math.inf])
+def test_q_scale_must_be_finite_positive(qs):
+    assert v(desc(), qs=qs) == INVALID
+
+
+@pytest.mark.parametrize("ks,vs", [(0.0, 1.0), (1.0, -2.0), (math.nan, 1.0), (1.0, math.inf)])
+def test_fp8_scales_must_be_finite_positive(ks, vs):
+    assert v(desc(kv=b.GQA_FP8_E4M3, ks=ks, vs=vs)) == INVALID
+
+
+def test_scale_on_16bit_cache_is_rejected_not_ignored():
+    assert v(desc(ks=0.5)) == INVALID
+    assert v(desc(vs=2.0)) == INVALID
+
+
+@pytest.mark.parametrize("which", ["q", "kv", "lens", "out"])
+def test_null_pointers(which):
+    args = dict(q=Q, kv=KV, lens=LENS, out=OUT)
+    args[which] = None
+    assert v(desc(), **args) == INVALID
+
+
+@pytest.mark.parametrize("which,off", [("q", 8), ("kv", 4), ("out", 2), ("lens", 2)])
+def test_misalignment(which, off):
+    args = dict(q=Q, kv=KV, lens=LENS, out=OUT)
+    args[which] += off
+    assert v(desc(), **args) == INVALID
+
+
+def test_out_aliasing_is_detected_by_address_range():
+    d = desc(batch=2, capacity=1024)
+    q_bytes = 2 * 32 * 128 * 2
+    kv_bytes = 2 * 2 * 8 * 1024 * 128 * 2
+    assert v(d, out=Q) == ALIAS
+    assert v(d, out=Q + q_bytes - 16) == ALIAS          # tail overlap
+    assert v(d, out=Q + q_bytes) == OK                  # adjacent is fine
+    assert v(d, out=KV + kv_bytes // 2) == ALIAS        # inside the cache
+    assert v(d, out=KV - q_bytes + 16) == ALIAS         # straddles the cache start
+    assert v(d, out=LENS - 16) == ALIAS                 # covers the lengths
+    assert v(d, q=KV, out=OUT) == OK                    # inputs may overlap each other
+
+
+def test_batch_zero_is_a_valid_no_op():
+    assert v(desc(batch=0), q=None, kv=None, lens=None, out=None) == OK
+
+
+def test_plan_routes_on_capacity():
+    for C in (1, 16, 63, 64):
+        p = b.gqa_plan(desc(capacity=C))
+        assert p["route"] == 0 and p["num_splits"] == 1 and p["workspace_bytes"] == 0
+        assert p["chunk_tokens"] >= C
+    for C in (65, 1024, 131072):
+        assert b.gqa_plan(desc(capacity=C))["route"] == 1
+
+
+@pytest.mark.parametrize("C", [65, 100, 1000, 1024, 8192, 65536, 131072])
+@pytest.mark.parametrize("B", [1, 8, 32])
+def test_auto_plan_is_consistent(B, C):
+    p = b.gqa_plan(desc(batch=B, capacity=C))
+    S, T = p["num_splits"], p["chunk_tokens"]
+    assert T % 16 == 0 and T % 64 == 0
+    assert S == -(-C // T)
+    assert p["num_workgroups"] == B * 8 * S
+    # FP32 partials (O, then max/sum) and one uint32 counter per (request, KV head)
+    want_ws = B * 32 * S * 130 * 4 + ((B * 8 * 4 + 255) // 256) * 256 if S > 1 else 0
+    assert p["workspace_bytes"] == want_ws
+
+
+@pytest.mark.parametrize("C", [100, 1000, 1024, 65536])
+def test_explicit_num_splits_is_honoured_exactly_or_rejected(C):
+    for n in range(1, 80):
+        d = desc(capacity=C)
+        st = v(d, ns=n)
+        if st == OK:
+            p = b.gqa_plan(d, n)
+            assert p["num_splits"] == n and p["chunk_tokens"] % 16 == 0
+            assert -(-C // p["chunk_tokens"]) == n
+        else:
+            assert st == INVALID and "num_splits" in b.last_error()
+    assert v(desc(capacity=1024), ns=10) == OK        # the article's batch-1 / capacity-1024 split
+    assert v(desc(capacity=1024), ns=-1) == INVALID
+    assert v(desc(capacity=1024), ns=1025) == INVALID
+
+
+def test_unknown_flags_are_rejected():
+    d = desc()
+    d.flags = 2
+    assert v(d) == INVALID
+    d.flags = b.GQA_FLAG_FUSED_COMBINE
+    assert v(d) == OK
+
+
+def test_error_message_is_thread_local_and_cleared_on_success():
+    assert v(desc(), qs=-1.0) == INVALID
+    assert "q_scale" in b.last_error()
+    assert v(desc()) == OK
+    assert b.last_error() == ""

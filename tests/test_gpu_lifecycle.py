@@ -1,0 +1,141 @@
+"""GPU lifecycle of the prepared API: hipGraph capture and replay with lengths
+rewritten in place, the convenience call's refusal to allocate inside a
+capture, two handles on concurrent streams, guard bands, and error paths
+that must leave the output untouched."""
+
+import pytest
+import torch
+
+from gpu_util import Workload, all_pairs, binding, compare, make_inputs, oracle_pairs, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(B=4, C=4096, qd="bf16", kd="bf16", seed=31):
+    fp8 = kd == "fp8_e4m3"
+    w = Workload(f"life_{qd}_{kd}", B, C, 1, C, qd, kd, q_scale=0.9,
+                 k_scale=1 / 64 if fp8 else 1.0, v_scale=1 / 64 if fp8 else 1.0, seed=seed)
+    return make_inputs(w, device="cuda")
+
+
+def _prepare(inp, out, num_splits=None, fused_combine=False):
+    b = binding()
+    return b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
+                                num_splits=num_splits, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                                fused_combine=fused_combine)
+
+
+@pytest.mark.parametrize("kd", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_graph_replay_with_rewritten_lengths_matches_direct_launch(kd, fused):
+    b = binding()
+    inp = _inputs(kd=kd)
+    out = torch.empty_like(inp["q"])
+    prep = _prepare(inp, out, fused_combine=fused)
+    assert prep.plan["num_splits"] > 1 and prep.workspace_bytes > 0
+    lens = inp["seq_lens"]
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b.launch_gqa_decode_prepared(prep)          # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        b.launch_gqa_decode_prepared(prep)
+
+    # Long, then shrinking, then growing lengths: stale partials must never leak.
+    schedule = [[4096, 4096, 4096, 4096], [4000, 1, 2049, 63], [17, 16, 15, 1],
+                [1, 2, 3, 4], [4096, 777, 64, 65], [2048, 2048, 2048, 2048]]
+    for new in schedule:
+        lens.copy_(torch.tensor(new, dtype=torch.int32))
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        # eager work between replays, then a direct launch with the same lengths
+        out.fill_(float("nan"))
+        b.launch_gqa_decode_prepared(prep)
+        torch.cuda.synchronize()
+        assert torch.equal(replayed.view(torch.int16), out.view(torch.int16)), new
+    compare(replayed, oracle_pairs(inp, all_pairs(4)), inp, f"graph replay {kd}")
+    del graph
+    prep.destroy()
+
+
+def test_convenience_call_refuses_to_allocate_inside_capture():
+    b = binding()
+    inp = _inputs(B=2, C=4096)
+    out = torch.empty_like(inp["q"])
+    plan = b.gqa_plan(b.make_desc(inp["q"], inp["kv"]))
+    assert plan["workspace_bytes"] > 0
+    x = torch.zeros(4, device="cuda")
+    stream = torch.cuda.Stream()        # fresh stream: its workspace cache is empty
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        with pytest.raises(b.GqaError) as ei:
+            b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], inp["q_scale"], out)
+        x.add_(1.0)
+    assert ei.value.status == b.GQA_ERR_CAPTURE
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.all(x == 1.0)
+
+
+def test_two_handles_on_two_concurrent_streams():
+    b = binding()
+    inp1 = _inputs(seed=41)
+    inp2 = _inputs(seed=42, kd="fp8_e4m3")
+    o1, o2 = torch.empty_like(inp1["q"]), torch.empty_like(inp2["q"])
+    p1, p2 = _prepare(inp1, o1), _prepare(inp2, o2)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(5):
+        with torch.cuda.stream(s1):
+            b.launch_gqa_decode_prepared(p1)
+        with torch.cuda.stream(s2):
+            b.launch_gqa_decode_prepared(p2)
+    torch.cuda.synchronize()
+    compare(o1, oracle_pairs(inp1, all_pairs(4)), inp1, "stream 1")
+    compare(o2, oracle_pairs(inp2, all_pairs(4)), inp2, "stream 2")
+
+
+@pytest.mark.parametrize("num_splits", [None, 1])
+def test_output_guard_bands_are_untouched(num_splits):
+    inp = _inputs(B=3, C=1000, qd="f16", kd="f16")
+    n = inp["q"].numel()
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 12345.0, dtype=torch.float16, device="cuda")
+    out = buf[pad:pad + n].view_as(inp["q"])
+    prep = _prepare(inp, out, num_splits)
+    binding().launch_gqa_decode_prepared(prep)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[pad + n:] == 12345.0)
+    compare(out, oracle_pairs(inp, all_pairs(3)), inp, "guard bands")
+
+
+def test_invalid_calls_enqueue_nothing_and_leave_out_untouched():
+    b = binding()
+    inp = _inputs(B=2, C=512)
+    out = torch.full_like(inp["q"], 7.0)
+    with pytest.raises(ValueError):
+        b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], 0.0, out)
+    with pytest.raises(ValueError):
+        b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], float("nan"), out)
+    with pytest.raises(ValueError):
+        b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, num_splits=31)
+    with pytest.raises(ValueError):   # out aliases q
+        b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], inp["q"])
+    with pytest.raises(ValueError):   # a scale on a 16-bit cache is rejected, not ignored
+        b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], 1.0, out, k_scale=0.5)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)

@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element, to the contract tolerance (max-abs
+2e-3 for a 16-bit cache, 2e-2 for fp8_e4m3), plus the exact special cases."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import (
+    Workload,
+    all_pairs,
+    compare,
+    decoded_out,
+    make_inputs,
+    oracle_pairs,
+    require_gpu,
+    run_decode,
+)
+from gqa_kv_cache_attn_amd.inputs import WORKLOADS
+from oracle import decode_e4m3fn_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sample_pairs(w):
+    if w.batch * 8 <= 256:
+        return all_pairs(w.batch)
+    # Full-size long-context workloads: every other request, one KV head each.
+    return [(b, (5 * b + 1) % 8) for b in range(0, w.batch, 2)]
+
+
+# ------------------------------------------------------------- the five workloads
+@pytest.mark.parametrize("w", WORKLOADS, ids=[w.name for w in WORKLOADS])
+def test_workload_parity(w):
+    print(f"[case] {w.name}", flush=True)
+    inp = make_inputs(w, device="cuda")
+    out_c, _ = run_decode(inp, "convenience")
+    out_p, prep = run_decode(inp, "prepared")
+    print(f"[plan] {prep.plan}", flush=True)
+    refs = oracle_pairs(inp, _sample_pairs(w))
+    compare(out_c, refs, inp, w.name, contract_only=True)
+    # Same plan, same kernels: the two entry points agree bit for bit.
+    assert torch.equal(out_c.view(torch.int16), out_p.view(torch.int16))
+
+
+# ------------------------------------------------------------- split / tail coverage
+DTYPE_PAIRS = [("f16", "f16"), ("bf16", "bf16"), ("bf16", "fp8_e4m3"), ("f16", "fp8_e4m3")]
+
+
+def _small(qd, kd, C=1000, B=5, seed=77, q_scale=0.75):
+    fp8 = kd == "fp8_e4m3"
+    return Workload(f"ragged_{qd}_{kd}_C{C}", B, C, 1, C, qd, kd, q_scale=q_scale,
+                    k_scale=1 / 64 if fp8 else 1.0, v_scale=1 / 32 if fp8 else 1.0, seed=seed)
+
+
+@pytest.mark.parametrize("qd,kd", DTYPE_PAIRS)
+@pytest.mark.parametrize("num_splits", [None, 1, 2, 3, 7, 9, 63])
+def test_split_counts_and_ragged_tails(qd, kd, num_splits):
+    w = _small(qd, kd)
+    lens = torch.tensor([1, 17, 64, 999, 1000], dtype=torch.int32)
+    inp = make_inputs(w, device="cuda", seq_lens=lens)
+    out, prep = run_decode(inp, "prepared", num_splits=num_splits)
+    if num_splits is not None:
+        assert prep.plan["num_splits"] == num_splits
+    compare(out, oracle_pairs(inp, all_pairs(w.batch)), inp, f"{w.name}/S={num_splits}")
+
+
+@pytest.mark.parametrize("qd,kd", DTYPE_PAIRS)
+@pytest.mark.parametrize("num_splits", [None, 7, 63])
+def test_fused_combine_variant(qd, kd, num_splits):
+    """The one-launch variant (last workgroup of a head merges) agrees too."""
+    w = _small(qd, kd, seed=78)
+    lens = torch.tensor([1000, 999, 1, 64, 65], dtype=torch.int32)
+    inp = make_inputs(w, device="cuda", seq_lens=lens)
+    out, prep = run_decode(inp, "prepared", num_splits=num_splits, fused_combine=True)
+    compare(out, oracle_pairs(inp, all_pairs(w.batch)), inp, f"{w.name}/fused/S={num_splits}")
+    sep, _ = run_decode(inp, "prepared", num_splits=num_splits)
+    # Same chunk partials, same merge order: identical bits.
+    assert torch.equal(out.view(torch.int16), sep.view(torch.int16))
+
+
+@pytest.mark.parametrize("qd,kd", DTYPE_PAIRS)
+@pytest.mark.parametrize("C", [1, 7, 16, 33, 63, 64])
+def test_short_route(qd, kd, C):
+    w = _small(qd, kd, C=C, B=6, seed=100 + C)
+    inp = make_inputs(w, device="cuda")
+    out, prep = run_decode(inp, "prepared")
+    assert prep.plan["route"] == 0 and prep.workspace_bytes == 0
+    compare(out, oracle_pairs(inp, all_pairs(w.batch)), inp, w.name)
+
+
+# ------------------------------------------------------------- exact special cases
+@pytest.mark.parametrize("qd,kd", DTYPE_PAIRS)
+@pytest.mark.parametrize("num_splits", [None, 1, 4])
+def test_single_token_returns_v_row0_bit_exact(qd, kd, num_splits):
+    w = _small(qd, kd, C=256, B=3, seed=5)
+    inp = make_inputs(w, device="cuda", seq_lens=torch.ones(3, dtype=torch.int32))
+    out, _ = run_decode(inp, "prepared", num_splits=num_splits)
+    got = decoded_out(out, qd)
+    refs = oracle_pairs(inp, all_pairs(3))
+    for (b, g), ref in refs.items():
+        assert np.array_equal(got[b, 4 * g:4 * g + 4], ref), (b, g)
+
+
+@pytest.mark.parametrize("num_splits,fused", [(None, False), (1, False), (None, True)])
+def test_zero_and_overlong_lengths(num_splits, fused):
+    """Length <= 0 gives zeros; length > capacity behaves as capacity."""
+    w = _small("bf16", "bf16", C=512, B=4, seed=9)
+    inp = make_inputs(w, device="cuda", seq_lens=torch.tensor([0, -5, 600, 512], dtype=torch.int32))
+    out = torch.full_like(inp["q"], float("nan"))
+    out, _ = run_decode(inp, "prepared", num_splits=num_splits, out=out, fused_combine=fused)
+    got = decoded_out(out, "bf16")
+    assert np.all(got[0] == 0) and np.all(got[1] == 0)
+    inp_cap = dict(inp, seq_lens=torch.tensor([1, 1, 512, 512], dtype=torch.int32, device="cuda"))
+    refs = oracle_pairs(inp_cap, [(b, g) for b in (2, 3) for g in range(8)])
+    compare(out, refs, inp, "overlong")
+
+
+@pytest.mark.parametrize("qd,kd", DTYPE_PAIRS)
+@pytest.mark.parametrize("num_splits", [None, 1, 5])
+def test_nan_garbage_past_length_is_never_read(qd, kd, num_splits):
+    w = _small(qd, kd, C=700, B=4, seed=11)
+    lens = torch.tensor([1, 250, 333, 699], dtype=torch.int32)
+    inp = make_inputs(w, device="cuda", seq_lens=lens)
+    kv = inp["kv"]
+    for b, L in enumerate(lens.tolist()):
+        if kd == "fp8_e4m3":
+            kv[b, :, :, L:] = 0x7F        # e4m3fn NaN
+        else:
+            kv[b, :, :, L:] = float("nan")
+    out, _ = run_decode(inp, "prepared", num_splits=num_splits)
+    compare(out, oracle_pairs(inp, all_pairs(4)), inp, f"nan-garbage {qd}/{kd}")
+
+
+@pytest.mark.parametrize("kd", ["bf16", "fp8_e4m3"])
+def test_capacity_padding_is_invisible(kd):
+    qd = "bf16"
+    L = 300
+    w = _small(qd, kd, C=L, B=2, seed=13)
+    tight = make_inputs(w, device="cuda", seq_lens=torch.full((2,), L, dtype=torch.int32))
+    wide_kv = torch.empty(2, 2, 8, 4 * L, 128, dtype=tight["kv"].dtype, device="cuda")
+    if kd == "fp8_e4m3":
+        wide_kv.fill_(0x7F)
+    else:
+        wide_kv.fill_(float("nan"))
+    wide_kv[:, :, :, :L] = tight["kv"]
+    wide = dict(tight, kv=wide_kv)
+    out_t, _ = run_decode(tight, "prepared")
+    out_w, _ = run_decode(wide, "prepared")
+    refs = oracle_pairs(tight, all_pairs(2))
+    compare(out_t, refs, tight, "tight")
+    compare(out_w, refs, wide, "padded x4 with NaN")
+
+
+@pytest.mark.parametrize("kd", ["f16", "fp8_e4m3"])
+def test_head_h_reads_kv_head_h_div_4(kd):
+    qd = "f16"
+    w = _small(qd, kd, C=200, B=3, seed=15)
+    inp = make_inputs(w, device="cuda", seq_lens=torch.tensor([200, 1, 77], dtype=torch.int32))
+    for g in range(8):
+        if kd == "fp8_e4m3":   # e4m3fn code for g * 32 (value g / v_scale-scaled below)
+            code = int(torch.tensor(float(g)).to(torch.float8_e4m3fn).view(torch.uint8))
+            inp["kv"][:, 1, g] = code
+        else:
+            inp["kv"][:, 1, g] = float(g)
+    out, _ = run_decode(inp, "prepared", num_splits=3)
+    got = decoded_out(out, qd)
+    for h in range(32):
+        assert np.all(got[:, h] == (h // 4) * inp["v_scale"]), h
+
+
+def test_identical_keys_average_the_values():
+    w = _small("bf16", "bf16", C=4096, B=2, seed=17)
+    inp = make_inputs(w, device="cuda", seq_lens=torch.tensor([4096, 1234], dtype=torch.int32))
+    inp["kv"][:, 0] = inp["kv"][:, 0, :, :1]
+    out, _ = run_decode(inp, "prepared")
+    refs = oracle_pairs(inp, all_pairs(2))
+    for (b, g), ref in refs.items():
+        L = int(inp["seq_lens"][b])
+        mean = inp["kv"][b, 1, g, :L].double().mean(0).cpu().numpy()
+        np.testing.assert_allclose(ref, np.tile(mean, (4, 1)), rtol=0, atol=1e-12)
+    compare(out, refs, inp, "identical keys")
+
+
+# ------------------------------------------------------------- fp8 decode on the device
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+def test_fp8_every_code_decodes_exactly(qd):
+    """V row 0 holds all 256 e4m3fn codes; with L = 1 the output is
+    v_scale * decode(code) exactly (NaN codes give NaN)."""
+    B = 2
+    w = Workload("fp8codes", B, 16, 1, 1, qd, "fp8_e4m3", k_scale=1.0, v_scale=1 / 64, seed=19)
+    inp = make_inputs(w, device="cuda", seq_lens=torch.ones(B, dtype=torch.int32))
+    codes = (torch.arange(B * 8 * 128, device="cuda") % 256).to(torch.uint8).view(B, 8, 128)
+    inp["kv"][:, 1, :, 0] = codes
+    out, _ = run_decode(inp, "prepared")
+    got = decoded_out(out, qd)
+    want = decode_e4m3fn_bits(codes.cpu().numpy()) / 64.0
+    for h in range(32):
+        g_ = got[:, h]
+        w_ = want[:, h // 4]
+        assert np.array_equal(np.isnan(g_), np.isnan(w_)), h
+        assert np.array_equal(g_[~np.isnan(g_)], w_[~np.isnan(w_)]), h
+
+
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+def test_fp8_full_code_range_parity(qd):
+    """K and V bytes uniform over every finite e4m3fn code (subnormals to 448)."""
+    B, C = 3, 640
+    w = Workload("fp8range", B, C, 1, C, qd, "fp8_e4m3", q_scale=1.0, k_scale=1 / 4096,
+                 v_scale=1 / 64, seed=21)
+    inp = make_inputs(w, device="cuda", seq_lens=torch.tensor([640, 321, 16], dtype=torch.int32))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(23)
+    raw = torch.randint(0, 256, inp["kv"].shape, generator=gen, device="cuda", dtype=torch.int32)
+    raw = torch.where((raw & 0x7F) == 0x7F, raw - 1, raw)   # drop the two NaN codes
+    inp["kv"].copy_(raw.to(torch.uint8))
+    out, _ = run_decode(inp, "prepared", num_splits=4)
+    compare(out, oracle_pairs(inp, all_pairs(B)), inp, f"fp8 full range q={qd}")
+
+
+def test_batch_zero_is_a_no_op():
+    b = pytest.importorskip("gqa_kv_cache_attn_amd.binding")
+    q = torch.empty(0, 32, 128, dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty(0, 2, 8, 64, 128, dtype=torch.bfloat16, device="cuda")
+    lens = torch.empty(0, dtype=torch.int32, device="cuda")
+    out = b.gqa_decode(q, kv, lens)
+    assert out.shape == (0, 32, 128)
+
