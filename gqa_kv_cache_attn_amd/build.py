@@ -21,6 +21,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["gqa_kernels.hip", "gqa_api.hip"]
+# HBM read-ceiling / copy-calibration kernels (measurement only, separate library).
+PROBE_SOURCES = ["hbm_probe.hip"]
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libgqa_hbm_probe.so")
 ARCH = "gfx950"
 
 
@@ -31,21 +34,20 @@ def hipcc_path() -> str:
     raise RuntimeError("hipcc not found (looked at $HIPCC, /opt/rocm/bin/hipcc, PATH)")
 
 
-def compile_command(out_path: str) -> list:
+def compile_command(out_path: str, sources=SOURCES) -> list:
     return [
         hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-fvisibility=hidden", "-Wall", "-Wno-unused-command-line-argument",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE,
-        *[os.path.join(CSRC, s) for s in SOURCES],
+        *[os.path.join(CSRC, s) for s in sources],
         "-o", out_path,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library (always; no staleness shortcut) and return its path."""
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = compile_command(tmp)
+def _compile(sources, out_path, verbose):
+    tmp = out_path + f".tmp{os.getpid()}"
+    cmd = compile_command(tmp, sources)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,7 +58,13 @@ def build(verbose: bool = False) -> str:
     noise = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
     if verbose and noise:
         print("\n".join(noise), file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out_path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the libraries (always; no staleness shortcut); return the decode library path."""
+    _compile(SOURCES, LIB_PATH, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

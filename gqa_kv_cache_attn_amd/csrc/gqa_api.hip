@@ -44,7 +44,10 @@ gqa_status_t ok() {
   return GQA_OK;
 }
 
-constexpr int kTargetWorkgroups = 2048;  // ~8 per CU on a 256-CU part
+// Automatic split planning (measured on MI355X: ~1 MiB of K+V per chunk was
+// best for 16-bit and fp8 caches alike; 768 = 256 CUs x 3 resident workgroups).
+constexpr int64_t kChunkBytes = 1 << 20;
+constexpr int64_t kFillWorkgroups = 768;
 
 int elem_bytes(int dt) { return dt == GQA_FP8_E4M3 ? 1 : 2; }
 
@@ -108,12 +111,17 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p) {
     if (C <= GQA_SHORT_CAPACITY_MAX) {
       chunk_granules = granules;
     } else {
-      // Automatic: whole workgroup steps (64 tokens), about kTargetWorkgroups chunks.
+      // Automatic, in whole workgroup steps (64 tokens): chunks of about
+      // kChunkBytes of K+V each (long enough to amortise a workgroup's
+      // prologue and merge, short enough to balance), but small enough that
+      // the grid still fills every CU once at full capacity.
       constexpr int64_t kStepGranules = 64 / GQA_CHUNK_GRANULE;
       const int64_t steps = (C + 63) / 64;
+      const int64_t step_bytes = 64 * 2 * GQA_HEAD_DIM * (int64_t)elem_bytes(d->kv_dtype);
+      const int64_t by_bytes = std::max<int64_t>(1, kChunkBytes / step_bytes);
       const int64_t total = std::max<int64_t>(1, (int64_t)d->batch * GQA_NUM_KV_HEADS * steps);
-      int64_t chunk_steps = std::max<int64_t>(1, (total + kTargetWorkgroups - 1) / kTargetWorkgroups);
-      chunk_steps = std::min(chunk_steps, steps);
+      const int64_t by_fill = std::max<int64_t>(1, total / kFillWorkgroups);
+      const int64_t chunk_steps = std::min(std::min(by_bytes, by_fill), steps);
       chunk_granules = chunk_steps * kStepGranules;
     }
   } else if (num_splits == 1) {

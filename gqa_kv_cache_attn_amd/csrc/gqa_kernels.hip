@@ -60,7 +60,7 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 #define GQA_MIN_WAVES_PER_SIMD 2
 #endif
 #ifndef GQA_KV_LOAD_POLICY
-#define GQA_KV_LOAD_POLICY 0   // cache-policy bits of the K/V buffer loads
+#define GQA_KV_LOAD_POLICY 2   // cache-policy bits of the K/V loads: 2 = non-temporal
 #endif
 constexpr int kLoadAux = GQA_KV_LOAD_POLICY;
 
@@ -143,9 +143,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u3
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Dim-block (8 dims) that lane group `grp` feeds to QK instruction `i`.
-// 16-bit cache: load i covers bytes [64i, 64i+64) of 16 rows, block 4i+grp.
-// fp8 cache:    load p covers bytes [64p, 64p+64); its two halves feed
-//               instructions 2p and 2p+1, blocks 8p + 2grp + {0,1}.
+// 16-bit cache: block 4i+grp.
+// fp8 cache:    the lane's 16-byte chunk 4p+grp of a K row holds blocks
+//               8p + 2grp + {0,1}, fed to instructions 2p and 2p+1.
 template <int KVT>
 __device__ __forceinline__ int qk_dim_block(int i, int grp) {
   if constexpr (KVT == kFP8) {
@@ -155,45 +155,58 @@ __device__ __forceinline__ int qk_dim_block(int i, int grp) {
   }
 }
 
-// Registers of one 16-token tile.
+// Registers of one 16-token tile, as loaded. Every load instruction reads
+// whole cache rows (K and V alike): a 16-bit row is 256 bytes = 16 lanes x 16
+// bytes, an fp8 row 128 bytes = 8 lanes x 16 bytes (K) or 16 lanes x 8 bytes (V).
 template <int KVT>
 struct Tile;
 
 template <>
 struct Tile<kF16> {
-  u32x4 k[4];  // K: token n16, dim block 4i+grp
+  u32x4 k[4];  // K: token 4grp+e, 16-byte chunk n16 (dims [8 n16, 8 n16 + 8))
   u32x4 v[4];  // V: token 4grp+e, dims [8 n16, 8 n16 + 8)
 };
 template <>
 struct Tile<kBF16> : Tile<kF16> {};
 template <>
 struct Tile<kFP8> {
-  u32x4 k[2];  // K: token n16, bytes [64p + 16grp, +16)
+  u32x4 k[2];  // K: token 8u + lane/8, 16-byte chunk lane%8
   u32x2 v[4];  // V: token 4grp+e, dims [8 n16, 8 n16 + 8)
 };
 
 template <int KVT>
 __device__ __forceinline__ void load_tile(Tile<KVT>& t, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, int j0, int n16, int grp) {
+                                          __amdgpu_buffer_rsrc_t rv, int j0, int lane) {
+  const int n16 = lane & 15, grp = lane >> 4;
   if constexpr (KVT == kFP8) {
-    const int ko = (j0 + n16) * kHeadDim + 16 * grp;
+    const int ko = (j0 + (lane >> 3)) * kHeadDim + 16 * (lane & 7);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) t.k[p] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * p, 0, kLoadAux);
+    for (int u = 0; u < 2; ++u)
+      t.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + u * 8 * kHeadDim, 0, kLoadAux);
     const int vo = (j0 + 4 * grp) * kHeadDim + 8 * n16;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       t.v[e] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + e * kHeadDim, 0, kLoadAux);
   } else {
-    const int ko = (j0 + n16) * (2 * kHeadDim) + 16 * grp;
+    const int ko = (j0 + 4 * grp) * (2 * kHeadDim) + 16 * n16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) t.k[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + 64 * i, 0, kLoadAux);
-    const int vo = (j0 + 4 * grp) * (2 * kHeadDim) + 16 * n16;
+    for (int e = 0; e < 4; ++e)
+      t.k[e] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + e * (2 * kHeadDim), 0, kLoadAux);
+    const int vo = ko;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       t.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + e * (2 * kHeadDim), 0, kLoadAux);
   }
 }
 
+// The QK product wants K with one token per lane (lane n16 = token, 8 dims
+// per lane), the opposite of the row-per-16-lanes layout the coalesced loads
+// deliver. The wave passes its K tile through its own LDS slice: token t's
+// 16-byte chunk c is stored at slot c ^ f(t) of row t, with f(t) = t for
+// 16-bit rows (16 chunks) and f(t) = (t >> 1) & 7 for fp8 rows (8 chunks), so
+// both the stores (16 lanes = one row) and the loads (16 lanes = 16 rows, one
+// chunk each) hit 16 distinct 16-byte bank groups.
+constexpr int kKStageSlots = 16 * 16;  // 16-byte slots per wave (one 16-bit tile)
 // Running state of one wave.
 struct Softmax {
   float m;      // running max of log2-domain scores of row n16 (uniform per row)
@@ -203,16 +216,23 @@ struct Softmax {
 
 template <int QT, int KVT>
 __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, const u32x4 (&qf)[4],
-                                             int j0, int c1, int grp, float scale_log2) {
+                                             u32x4* sk, int j0, int c1, int lane, float scale_log2) {
   using E = Elem<QT>;
+  const int n16 = lane & 15, grp = lane >> 4;
   // ---- scores^T[token 4grp + r][row n16] ------------------------------------
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   if constexpr (KVT == kFP8) {
 #pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int tok = 8 * u + (lane >> 3);
+      sk[tok * 8 + ((lane & 7) ^ ((tok >> 1) & 7))] = t.k[u];
+    }
+#pragma unroll
     for (int p = 0; p < 2; ++p) {
+      const u32x4 k16 = sk[n16 * 8 + ((4 * p + grp) ^ ((n16 >> 1) & 7))];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32 w0 = t.k[p][2 * h], w1 = t.k[p][2 * h + 1];
+        const u32 w0 = k16[2 * h], w1 = k16[2 * h + 1];
         u32x4 kk = {E::template from_fp8<false>(w0), E::template from_fp8<true>(w0),
                     E::template from_fp8<false>(w1), E::template from_fp8<true>(w1)};
         s = E::qk(kk, qf[2 * p + h], s);
@@ -220,7 +240,12 @@ __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, co
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s = E::qk(t.k[i], qf[i], s);
+    for (int e = 0; e < 4; ++e) {
+      const int tok = 4 * grp + e;
+      sk[tok * 16 + (n16 ^ tok)] = t.k[e];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s = E::qk(sk[n16 * 16 + ((4 * i + grp) ^ n16)], qf[i], s);
   }
 
   // ---- online softmax, log2 domain -----------------------------------------
@@ -374,6 +399,7 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
   constexpr int kKvBytes = (KVT == kFP8) ? 1 : 2;
   constexpr int kRowBytes = kHeadDim * kKvBytes;
 
+  __shared__ u32x4 s_k[kWaves][kKStageSlots];
   __shared__ float s_o[kWaves][kGroup][kHeadDim];
   __shared__ float s_m[kWaves][kGroup];
   __shared__ float s_l[kWaves][kGroup];
@@ -436,15 +462,16 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
 
   int j0 = c0 + kTile * wave;
   if (j0 < c1) {
+    u32x4* sk = s_k[wave];
     Tile<KVT> ta, tb;
-    load_tile<KVT>(ta, rk, rv, j0, n16, grp);
+    load_tile<KVT>(ta, rk, rv, j0, lane);
     for (;;) {
-      load_tile<KVT>(tb, rk, rv, j0 + kStep, n16, grp);   // past c1: reads 0, no traffic
-      process_tile<QT, KVT>(st, ta, qf, j0, c1, grp, a.scale_log2);
+      load_tile<KVT>(tb, rk, rv, j0 + kStep, lane);   // past c1: reads 0, no traffic
+      process_tile<QT, KVT>(st, ta, qf, sk, j0, c1, lane, a.scale_log2);
       j0 += kStep;
       if (j0 >= c1) break;
-      load_tile<KVT>(ta, rk, rv, j0 + kStep, n16, grp);
-      process_tile<QT, KVT>(st, tb, qf, j0, c1, grp, a.scale_log2);
+      load_tile<KVT>(ta, rk, rv, j0 + kStep, lane);
+      process_tile<QT, KVT>(st, tb, qf, sk, j0, c1, lane, a.scale_log2);
       j0 += kStep;
       if (j0 >= c1) break;
     }

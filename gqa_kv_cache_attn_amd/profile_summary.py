@@ -1,0 +1,113 @@
+"""Summarise rocprofv3 CSV output into the short text files kept under profiles/.
+
+    python -m gqa_kv_cache_attn_amd.profile_summary stats  --csv K_kernel_stats.csv \\
+        --title T --command "C" --out profiles/X.txt
+    python -m gqa_kv_cache_attn_amd.profile_summary traffic --workload W \\
+        --fetch F_counter_collection.csv --write W_counter_collection.csv \\
+        --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N \\
+        --algorithmic-bytes A --command "C" --out profiles/gqa_attention_kernel_W_traffic.txt
+
+`traffic` scales each counter by what it reads for the probe's plain copy of
+known size (copy_stream_kernel: N bytes read, N bytes written per launch), so
+counter units become bytes; it records the kernel-source digest the counters
+were taken with, and bench.py only reports the figure while that digest still
+matches the source.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+
+from .build import CSRC
+
+KERNEL_MATCH = "gqa_attention_kernel"
+COPY_MATCH = "copy_stream_kernel"
+
+
+def kernel_source_digest() -> str:
+    with open(os.path.join(CSRC, "gqa_kernels.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _counter_avg(path, match):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path)) if match in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"no dispatch of {match} in {path}")
+    return statistics.fmean(vals), len(vals)
+
+
+def cmd_stats(a):
+    rows = list(csv.DictReader(open(a.csv)))
+    lines = [f"# {a.title}", "", f"command: {a.command}", "",
+             "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        if a.only_gqa and "gqa" not in name:
+            continue
+        lines.append(f"| `{name[:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    lines.append("")
+    lines.append(f"kernel_source_sha256_16 = {kernel_source_digest()}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_traffic(a):
+    fetch, nf = _counter_avg(a.fetch, KERNEL_MATCH)
+    write, nw = _counter_avg(a.write, KERNEL_MATCH)
+    cfetch, _ = _counter_avg(a.copy_fetch, COPY_MATCH)
+    cwrite, _ = _counter_avg(a.copy_write, COPY_MATCH)
+    fscale = a.copy_bytes / cfetch          # bytes per FETCH_SIZE unit
+    wscale = a.copy_bytes / cwrite          # bytes per WRITE_SIZE unit
+    fb, wb = fetch * fscale, write * wscale
+    lines = [
+        f"# HBM traffic per launch of {KERNEL_MATCH}, workload {a.workload}",
+        "#",
+        f"# command (FETCH_SIZE pass; WRITE_SIZE pass identical but for the counter): {a.command}",
+        f"# calibration: {COPY_MATCH} copies {a.copy_bytes} bytes per launch; it reads "
+        f"FETCH_SIZE={cfetch:.1f} and WRITE_SIZE={cwrite:.1f}",
+        f"# -> {fscale:.4f} bytes per FETCH_SIZE unit, {wscale:.4f} bytes per WRITE_SIZE unit",
+        f"# dispatches averaged: fetch {nf}, write {nw}",
+        f"workload = {a.workload}",
+        f"num_splits_requested = {a.num_splits}",
+        f"fetch_size_raw = {fetch:.3f}",
+        f"write_size_raw = {write:.3f}",
+        f"fetch_bytes_per_launch = {fb:.0f}",
+        f"write_bytes_per_launch = {wb:.0f}",
+        f"hbm_bytes_per_launch = {fb + wb:.0f}",
+        f"algorithmic_bytes_per_launch = {a.algorithmic_bytes}",
+        f"fetch_over_algorithmic = {fb / a.algorithmic_bytes:.4f}",
+        f"kernel_source_sha256_16 = {kernel_source_digest()}",
+    ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--title", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    s.add_argument("--only-gqa", action="store_true")
+    t = sub.add_parser("traffic")
+    for k in ("workload", "fetch", "write", "copy_fetch", "copy_write", "command", "out"):
+        t.add_argument("--" + k.replace("_", "-"), required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--algorithmic-bytes", type=int, required=True)
+    t.add_argument("--num-splits", type=int, default=0)
+    a = ap.parse_args()
+    cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    main()
