@@ -66,12 +66,12 @@ def kernel_source_digest():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(workload, num_splits):
+def read_traffic(kernel, workload, num_splits):
     """HBM bytes per attention launch from committed rocprofv3 --pmc summaries.
 
     The summary file is only used while its recorded kernel-source digest
     matches the current source; otherwise traffic is reported as null."""
-    path = os.path.join(PROFILES, f"gqa_attention_kernel_{workload}_traffic.txt")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -221,7 +221,8 @@ def main():
     def pct(xs, p):
         return xs[min(len(xs) - 1, int(round(p / 100 * (len(xs) - 1))))] if xs else None
 
-    traffic = read_traffic(w.name, args.num_splits) if not args.fused_combine else None
+    kernel = "gqa_balanced_attention_kernel" if plan["route"] == 2 else "gqa_attention_kernel"
+    traffic = read_traffic(kernel, w.name, args.num_splits) if not args.fused_combine else None
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -246,7 +247,7 @@ def main():
                        "combine_avg": round(statistics.fmean(comb_ms) * 1e3, 2)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_attention_kernel",
+            "kernel": kernel,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

@@ -48,6 +48,24 @@ gqa_status_t ok() {
 // best for 16-bit and fp8 caches alike; 768 = 256 CUs x 3 resident workgroups).
 constexpr int64_t kChunkBytes = 1 << 20;
 constexpr int64_t kFillWorkgroups = 768;
+// Balanced split: host-only plans assume 256 CUs x 3 resident workgroups;
+// prepare and the convenience call use the device's own figure (capped).
+constexpr int kNominalBalancedGrid = 768;
+constexpr int kMaxBalancedGrid = 4096;
+
+// Resident balanced-kernel workgroups per (device, dtype pair), queried once.
+std::mutex g_grid_mu;
+std::map<std::pair<int, int>, int> g_grid;
+
+int device_balanced_grid(int dev, int q_dtype, int kv_dtype) {
+  std::lock_guard<std::mutex> lk(g_grid_mu);
+  const std::pair<int, int> key{dev, q_dtype * 8 + kv_dtype};
+  auto it = g_grid.find(key);
+  if (it != g_grid.end()) return it->second;
+  const int G = gqa::balanced_grid_size(q_dtype, kv_dtype);
+  g_grid.emplace(key, G);
+  return G;
+}
 
 int elem_bytes(int dt) { return dt == GQA_FP8_E4M3 ? 1 : 2; }
 
@@ -88,25 +106,51 @@ gqa_status_t check_desc(const gqa_desc_t* d) {
   return GQA_OK;
 }
 
-// Workspace: part_o [B,32,S,128] f32 | part_ml [B,32,S,2] f32 | counters [B,8] u32.
+// Workspace: part_o [R,128] f32 | part_ml [R,2] f32 | aux int32 array, where R
+// is the number of partial rows: chunked split R = B*32*S (head-major), aux =
+// per-(request, KV head) counters [B*8] (fused merge only); balanced split
+// R = 2G*4 (two slots per workgroup, 4 query rows each), aux = slab prefix [B+1].
 struct WorkspaceLayout {
-  uint64_t ml_offset, counter_offset, total;
+  uint64_t ml_offset, aux_offset, total;
 };
 
-WorkspaceLayout workspace_layout(int64_t batch, int64_t splits) {
+WorkspaceLayout workspace_layout(uint64_t rows, uint64_t aux_ints) {
   WorkspaceLayout w;
-  const uint64_t heads = (uint64_t)batch * GQA_NUM_Q_HEADS;
-  w.ml_offset = heads * (uint64_t)splits * GQA_HEAD_DIM * sizeof(float);
-  w.counter_offset = w.ml_offset + heads * (uint64_t)splits * 2 * sizeof(float);
-  w.total = w.counter_offset + (((uint64_t)batch * GQA_NUM_KV_HEADS * sizeof(uint32_t) + 255) & ~255ull);
+  w.ml_offset = rows * GQA_HEAD_DIM * sizeof(float);
+  w.aux_offset = w.ml_offset + rows * 2 * sizeof(float);
+  w.total = w.aux_offset + ((aux_ints * sizeof(int32_t) + 255) & ~255ull);
   return w;
 }
 
-gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p) {
+WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p) {
+  if (p.route == 2)
+    return workspace_layout(2ull * (uint64_t)p.num_workgroups * 4, (uint64_t)d->batch + 1);
+  return workspace_layout((uint64_t)d->batch * GQA_NUM_Q_HEADS * (uint64_t)p.num_splits,
+                          (uint64_t)d->batch * GQA_NUM_KV_HEADS);
+}
+
+// grid_wgs: resident workgroups of the balanced kernel on the target device
+// (0: the nominal kNominalBalancedGrid, for host-only planning).
+gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, int grid_wgs = 0) {
   const int64_t C = d->capacity;
+  if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", num_splits);
+  const int64_t slabs_per_head = (C + 63) / 64;
+  const int64_t slabs_at_capacity = (int64_t)d->batch * GQA_NUM_KV_HEADS * slabs_per_head;
+  if (num_splits == 0 && C > GQA_SHORT_CAPACITY_MAX && !(d->flags & GQA_FLAG_FUSED_COMBINE) &&
+      d->batch <= gqa::kMaxBalancedBatch && slabs_at_capacity <= INT32_MAX &&
+      slabs_at_capacity >= kNominalBalancedGrid) {
+    // Balanced split: a persistent grid shares the step's slabs evenly.
+    const int G = std::max(1, std::min(grid_wgs > 0 ? grid_wgs : kNominalBalancedGrid,
+                                       kMaxBalancedGrid));
+    p->route = 2;
+    p->num_splits = 0;
+    p->chunk_tokens = 64;
+    p->num_workgroups = G;
+    p->workspace_bytes = d->batch > 0 ? plan_layout(d, *p).total : 0;
+    return GQA_OK;
+  }
   const int64_t granules = (C + GQA_CHUNK_GRANULE - 1) / GQA_CHUNK_GRANULE;
   int64_t chunk_granules;
-  if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", num_splits);
   if (num_splits == 0) {
     if (C <= GQA_SHORT_CAPACITY_MAX) {
       chunk_granules = granules;
@@ -144,7 +188,7 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p) {
   p->num_splits = (int32_t)S;
   p->chunk_tokens = (int32_t)chunk;
   p->num_workgroups = (int32_t)wgs;
-  p->workspace_bytes = S > 1 ? workspace_layout(d->batch, S).total : 0;
+  p->workspace_bytes = S > 1 ? plan_layout(d, *p).total : 0;
   return GQA_OK;
 }
 
@@ -202,12 +246,14 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.kv = kv;
   a.seq_lens = lens;
   a.out = out;
-  const WorkspaceLayout wl = workspace_layout(d->batch, p.num_splits);
+  const WorkspaceLayout wl = plan_layout(d, p);
   char* base = static_cast<char*>(ws);
   a.part_o = ws ? reinterpret_cast<float*>(base) : nullptr;
   a.part_ml = ws ? reinterpret_cast<float*>(base + wl.ml_offset) : nullptr;
-  a.counters = ws ? reinterpret_cast<uint32_t*>(base + wl.counter_offset) : nullptr;
+  a.counters = (ws && p.route != 2) ? reinterpret_cast<uint32_t*>(base + wl.aux_offset) : nullptr;
+  a.slab_prefix = (ws && p.route == 2) ? reinterpret_cast<int32_t*>(base + wl.aux_offset) : nullptr;
   a.fused_combine = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
+  a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
   a.batch = d->batch;
   a.capacity = d->capacity;
   a.num_splits = p.num_splits;
@@ -286,6 +332,10 @@ GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q, c
   int dev = -1;
   st = check_device(&dev);
   if (st != GQA_OK) return st;
+  if (p.route == 2) {   // size the balanced grid for this device
+    st = make_plan(desc, num_splits, &p, device_balanced_grid(dev, desc->q_dtype, desc->kv_dtype));
+    if (st != GQA_OK) return st;
+  }
   void* ws = nullptr;
   if (p.workspace_bytes > 0 && desc->batch > 0) {
     hipError_t e = hipMalloc(&ws, p.workspace_bytes);
@@ -375,6 +425,10 @@ GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const voi
   int dev = -1;
   st = check_device(&dev);
   if (st != GQA_OK) return st;
+  if (p.route == 2) {
+    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc->q_dtype, desc->kv_dtype));
+    if (st != GQA_OK) return st;
+  }
 
   void* ws = nullptr;
   if (p.workspace_bytes > 0) {

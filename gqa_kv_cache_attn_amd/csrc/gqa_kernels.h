@@ -10,6 +10,9 @@ namespace gqa {
 
 enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
 
+// The balanced split keeps the per-request slab prefix in LDS.
+constexpr int kMaxBalancedBatch = 4096;
+
 // Arguments of one decode step, passed to the kernels by value.
 struct StepArgs {
   const void* q;             // [batch, 32, 128] q dtype
@@ -19,6 +22,7 @@ struct StepArgs {
   float* part_o;             // [batch, 32, num_splits, 128] unnormalised chunk outputs
   float* part_ml;            // [batch, 32, num_splits, 2] chunk (max, sum), log2 domain
   uint32_t* counters;        // [batch, 8] finished chunks per (request, KV head); 0 between launches
+  int32_t* slab_prefix;      // [batch + 1] balanced split: 8 * slabs before each request
   int32_t batch;
   int32_t capacity;
   int32_t num_splits;        // chunks per (request, KV head); 1 = normalise in place
@@ -26,7 +30,12 @@ struct StepArgs {
   float scale_log2;          // q_scale * k_scale * log2(e) / sqrt(128)
   float v_scale;
   int32_t fused_combine;     // 1: last workgroup of a head combines; 0: separate combine kernel
+  int32_t grid_wgs;          // > 0: balanced split with this many persistent workgroups
 };
+
+// Workgroups of the balanced split that the current device keeps resident at
+// once (CUs x resident workgroups per CU); 0 if the query fails.
+int balanced_grid_size(int q_dtype, int kv_dtype);
 
 // Enqueue the attention kernel (and, for num_splits > 1, the combine kernel).
 // Returns the first launch error. Arguments are assumed validated. When given,

@@ -53,11 +53,15 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;               // tokens per wave step
 constexpr int kStep = kTile * kWaves;   // tokens per workgroup step
+constexpr int kSlab = kStep;            // unit of work of the balanced split
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 
 // Build-time tuning knobs (defaults are the measured best on MI355X).
 #ifndef GQA_MIN_WAVES_PER_SIMD
 #define GQA_MIN_WAVES_PER_SIMD 2
+#endif
+#ifndef GQA_BALANCED_MIN_WAVES_PER_SIMD
+#define GQA_BALANCED_MIN_WAVES_PER_SIMD 2
 #endif
 #ifndef GQA_KV_LOAD_POLICY
 #define GQA_KV_LOAD_POLICY 2   // cache-policy bits of the K/V loads: 2 = non-temporal
@@ -352,11 +356,61 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Log-sum-exp merge of the chunk partials of the 4 query heads of (request b,
-// KV head g): wave r takes head 4g + r, lane l dims 2l and 2l + 1.
-//   M = max_s m_s,  out = v_scale * sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// Only the chunks that start below the current length are read, so partials
-// left by an earlier launch with longer lengths never enter the result.
+// Log-sum-exp merge of n partial rows of one query head, run by one wave
+// (lane l owns dims 2l and 2l + 1):
+//   M = max_k m_k,  out = v_scale * sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k
+// row(k) gives the k-th partial row. A row whose max is -inf is empty (a
+// workgroup that had no slabs marked it): it gets weight 0 and its O row,
+// possibly stale, is never read. The (m, l) pairs of 64 rows at a time are
+// loaded one per lane, so the whole merge costs two dependent loads.
+template <int QT, typename RowFn>
+__device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, char* outp) {
+  using E = Elem<QT>;
+  const int lane = threadIdx.x & 63;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+  const float2* po = reinterpret_cast<const float2*>(a.part_o);
+  float mloc = -INFINITY;
+  for (int k = lane; k < n; k += 64) mloc = fmaxf(mloc, ml[row(k)].x);
+  const float M = wave_max(mloc);   // finite: at least one row holds data
+  const size_t fallback = row(0);   // a row that holds data, read with weight 0
+  float lloc = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int base = 0; base < n; base += 64) {
+    const int k = base + lane;
+    float wk = 0.f;
+    if (k < n) {
+      const float2 v = ml[row(k)];
+      if (v.x != -INFINITY) {
+        wk = fast_exp2(v.x - M);
+        lloc += wk * v.y;
+      }
+    }
+    const int cnt = min(64, n - base);
+    for (int j0 = 0; j0 < cnt; j0 += 8) {   // 8 independent row loads in flight
+      float f[8];
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        f[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), min(j, 63)));
+        if (j >= cnt) f[u] = 0.f;
+        const size_t r = f[u] != 0.f ? row(base + j) : fallback;
+        v[u] = po[r * (kHeadDim / 2) + lane];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        o0 += f[u] * v[u].x;
+        o1 += f[u] * v[u].y;
+      }
+    }
+  }
+  const float inv = a.v_scale / wave_sum(lloc);
+  E::store2(outp, o0 * inv, o1 * inv);
+}
+
+// Merge of the chunked split for the 4 query heads of (request b, KV head g):
+// wave r takes head 4g + r. Only the chunks that start below the current
+// length are read, so partials left by an earlier launch with longer lengths
+// never enter the result.
 template <int QT>
 __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int g, int L) {
   using E = Elem<QT>;
@@ -370,72 +424,35 @@ __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int
     E::store2(outp, 0.f, 0.f);
     return;
   }
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + head * S;
-  const float2* po = reinterpret_cast<const float2*>(a.part_o + head * (size_t)S * kHeadDim) + lane;
-  float mloc = -INFINITY;
-  for (int s = lane; s < n; s += 64) mloc = fmaxf(mloc, ml[s].x);
-  const float M = wave_max(mloc);   // every valid chunk has a finite max
-  float lloc = 0.f;
-  for (int s = lane; s < n; s += 64) {
-    const float2 v = ml[s];
-    lloc += fast_exp2(v.x - M) * v.y;
-  }
-  const float l = wave_sum(lloc);
-  float o0 = 0.f, o1 = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < n; ++s) {
-    const float f = fast_exp2(ml[s].x - M);
-    const float2 v = po[(size_t)s * (kHeadDim / 2)];
-    o0 += f * v.x;
-    o1 += f * v.y;
-  }
-  const float inv = a.v_scale / l;
-  E::store2(outp, o0 * inv, o1 * inv);
+  merge_rows<QT>(a, n, [&](int k) -> size_t { return head * (size_t)S + k; }, outp);
 }
 
-template <int QT, int KVT, int kMode>
-__global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attention_kernel(StepArgs a) {
-  using E = Elem<QT>;
-  constexpr int kKvBytes = (KVT == kFP8) ? 1 : 2;
-  constexpr int kRowBytes = kHeadDim * kKvBytes;
+// LDS of one workgroup: the 4 waves' K staging slices and the merge buffers.
+struct WorkgroupLds {
+  u32x4 k[kWaves][kKStageSlots];
+  float o[kWaves][kGroup][kHeadDim];
+  float m[kWaves][kGroup];
+  float l[kWaves][kGroup];
+};
 
-  __shared__ u32x4 s_k[kWaves][kKStageSlots];
-  __shared__ float s_o[kWaves][kGroup][kHeadDim];
-  __shared__ float s_m[kWaves][kGroup];
-  __shared__ float s_l[kWaves][kGroup];
-  __shared__ int s_last;
-
+// One workgroup attends the 4 query rows of (request b, KV head g) over the
+// cache slots [c0, c1) (c0 < c1 <= length). On return thread t holds, for
+// row t / 64 and dims 2 (t % 64) + {0, 1}: the chunk's log2-domain max M, its
+// sum of weights l and its unnormalised output (o0, o1). Ends with a barrier,
+// so the caller may call it again for another range.
+template <int QT, int KVT>
+__device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, int c0, int c1,
+                                             WorkgroupLds& lds, float& M, float& lsum, float& o0,
+                                             float& o1) {
+  constexpr int kRowBytes = kHeadDim * ((KVT == kFP8) ? 1 : 2);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n16 = lane & 15;
   const int grp = lane >> 4;
 
-  const int S = a.num_splits;
-  const int split = (int)blockIdx.x % S;
-  const int bg = (int)blockIdx.x / S;
-  const int g = bg % kKvHeads;
-  const int b = bg / kKvHeads;
-  const int C = a.capacity;
-  const int L = min(max(a.seq_lens[b], 0), C);
-  const int c0 = split * a.chunk_tokens;
-
-  // Epilogue coordinates: 256 threads cover 4 rows x 64 dim pairs.
-  const int er = tid >> 6;
-  const int ed = (tid & 63) * 2;
-  const size_t head = (size_t)b * kQHeads + kGroup * g + er;
-
-  if (c0 >= L) {
-    // Chunks past the length take no part. An empty request (L = 0) has no
-    // chunk at all: unless a combine kernel follows, chunk 0 writes its zeros.
-    if (kMode != kModeSplit && split == 0)
-      E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, 0.f, 0.f);
-    return;
-  }
-  const int c1 = min(c0 + a.chunk_tokens, L);
-
   const char* kvb = static_cast<const char*>(a.kv);
-  const size_t plane = (size_t)C * kRowBytes;
+  const size_t plane = (size_t)a.capacity * kRowBytes;
   const char* kplane = kvb + ((size_t)(b * 2 + 0) * kKvHeads + g) * plane;
   const char* vplane = kvb + ((size_t)(b * 2 + 1) * kKvHeads + g) * plane;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kplane, (u32)c1 * kRowBytes);
@@ -462,7 +479,7 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
 
   int j0 = c0 + kTile * wave;
   if (j0 < c1) {
-    u32x4* sk = s_k[wave];
+    u32x4* sk = lds.k[wave];
     Tile<KVT> ta, tb;
     load_tile<KVT>(ta, rk, rv, j0, lane);
     for (;;) {
@@ -482,30 +499,68 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   if (lane < kGroup) {
-    s_m[wave][lane] = st.m;
-    s_l[wave][lane] = l;
+    lds.m[wave][lane] = st.m;
+    lds.l[wave][lane] = l;
   }
   if (grp == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float4* dst = reinterpret_cast<float4*>(&s_o[wave][r][8 * n16]);
+      float4* dst = reinterpret_cast<float4*>(&lds.o[wave][r][8 * n16]);
       dst[0] = make_float4(st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]);
       dst[1] = make_float4(st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]);
     }
   }
   __syncthreads();
-
-  float M = s_m[0][er];
+  const int er = tid >> 6;
+  const int ed = (tid & 63) * 2;
+  M = lds.m[0][er];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][er]);
-  float o0 = 0.f, o1 = 0.f, lsum = 0.f;
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, lds.m[w][er]);
+  o0 = 0.f;
+  o1 = 0.f;
+  lsum = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
-    const float f = fast_exp2(s_m[w][er] - M);  // idle waves: m = -inf -> 0
-    o0 += f * s_o[w][er][ed];
-    o1 += f * s_o[w][er][ed + 1];
-    lsum += f * s_l[w][er];
+    const float f = fast_exp2(lds.m[w][er] - M);  // idle waves: m = -inf -> 0
+    o0 += f * lds.o[w][er][ed];
+    o1 += f * lds.o[w][er][ed + 1];
+    lsum += f * lds.l[w][er];
   }
+  __syncthreads();
+}
+
+// Chunked split: workgroup = one chunk of `chunk_tokens` slots of one
+// (request, KV head); grid B * 8 * num_splits.
+template <int QT, int KVT, int kMode>
+__global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attention_kernel(StepArgs a) {
+  using E = Elem<QT>;
+  __shared__ WorkgroupLds lds;
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int S = a.num_splits;
+  const int split = (int)blockIdx.x % S;
+  const int bg = (int)blockIdx.x / S;
+  const int g = bg % kKvHeads;
+  const int b = bg / kKvHeads;
+  const int L = min(max(a.seq_lens[b], 0), a.capacity);
+  const int c0 = split * a.chunk_tokens;
+
+  // Epilogue coordinates: 256 threads cover 4 rows x 64 dim pairs.
+  const int er = tid >> 6;
+  const int ed = (tid & 63) * 2;
+  const size_t head = (size_t)b * kQHeads + kGroup * g + er;
+
+  if (c0 >= L) {
+    // Chunks past the length take no part. An empty request (L = 0) has no
+    // chunk at all: unless a combine kernel follows, chunk 0 writes its zeros.
+    if (kMode != kModeSplit && split == 0)
+      E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, 0.f, 0.f);
+    return;
+  }
+  const int c1 = min(c0 + a.chunk_tokens, L);
+  float M, lsum, o0, o1;
+  attend_range<QT, KVT>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
 
   if constexpr (kMode == kModeDirect) {
     const float inv = a.v_scale / lsum;
@@ -533,7 +588,8 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
   }
 }
 
-// Separate log-sum-exp combine: one workgroup per (request, KV head).
+// Separate log-sum-exp combine for the chunked split: one workgroup per
+// (request, KV head).
 template <int QT>
 __global__ __launch_bounds__(kThreads) void gqa_combine_kernel(StepArgs a) {
   const int bg = blockIdx.x;
@@ -542,10 +598,160 @@ __global__ __launch_bounds__(kThreads) void gqa_combine_kernel(StepArgs a) {
   combine_head_group<QT>(a, b, bg % kKvHeads, L);
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split. The work of a step is 8 * sum_b ceil(L_b / 64) slabs of 64
+// slots, ordered request-major then KV head. A persistent grid of G
+// workgroups (as many as the device keeps resident) gives workgroup w the
+// slab range [w N / G, (w+1) N / G), so every workgroup streams the same
+// number of bytes whatever the length mix. A range crosses (request, KV head)
+// boundaries: heads it covers whole are normalised and written directly; its
+// first and last piece, when they are only part of a head, become partials
+// in slots 2w and 2w + 1, which the balanced combine merges per head.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int slabs_of(int len, int capacity) {
+  return (min(max(len, 0), capacity) + kSlab - 1) / kSlab;
+}
+
+// pref[b] = 8 * sum_{b' < b} slabs(b'), b = 0..B (B <= kMaxBalancedBatch).
+__device__ __forceinline__ void build_slab_prefix(const StepArgs& a, int* pref, int* wave_tot) {
+  const int B = a.batch;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int per = (B + kThreads - 1) / kThreads;
+  const int lo = min(tid * per, B);
+  const int hi = min(lo + per, B);
+  int own = 0;
+  for (int i = lo; i < hi; ++i) own += slabs_of(a.seq_lens[i], a.capacity);
+  int x = own;   // inclusive scan across the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wave_tot[wave] = x;
+  __syncthreads();
+  int run = x - own;
+  for (int w = 0; w < wave; ++w) run += wave_tot[w];
+  for (int i = lo; i < hi; ++i) {
+    pref[i] = kKvHeads * run;
+    run += slabs_of(a.seq_lens[i], a.capacity);
+  }
+  if (tid == kThreads - 1) pref[B] = kKvHeads * run;
+  __syncthreads();
+}
+
+template <int QT, int KVT>
+__global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa_balanced_attention_kernel(
+    StepArgs a) {
+  using E = Elem<QT>;
+  __shared__ WorkgroupLds lds;
+  __shared__ int s_pref[kMaxBalancedBatch + 1];
+  __shared__ int s_wave_tot[kWaves];
+
+  const int tid = threadIdx.x;
+  const int B = a.batch;
+  build_slab_prefix(a, s_pref, s_wave_tot);
+  const int64_t N = s_pref[B];
+  const int G = (int)gridDim.x;
+  const int w = (int)blockIdx.x;
+  if (w == 0)   // the combine kernel reads the same prefix
+    for (int i = tid; i <= B; i += kThreads) a.slab_prefix[i] = s_pref[i];
+
+  const int er = tid >> 6;
+  const int ed = (tid & 63) * 2;
+  // Slab counts fit in int32 (checked when the plan is made).
+  const int s0 = (int)((int64_t)w * N / G);
+  const int s1 = (int)((int64_t)(w + 1) * N / G);
+  if (s0 == s1) {
+    // Fewer slabs than workgroups: mark slot 2w empty for the combine, which
+    // may look at it when this workgroup falls inside a head's range of workgroups.
+    if ((tid & 63) == 0)
+      *reinterpret_cast<float2*>(a.part_ml + ((size_t)2 * w * kGroup + er) * 2) =
+          make_float2(-INFINITY, 0.f);
+    return;
+  }
+#pragma nounroll
+  for (int s = s0; s < s1;) {
+    // request b with pref[b] <= s < pref[b + 1]
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= s) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int nsb = (s_pref[b + 1] - s_pref[b]) / kKvHeads;   // >= 1 here
+    const int g = (s - s_pref[b]) / nsb;
+    const int seg_start = s_pref[b] + g * nsb;
+    const int seg_end = seg_start + nsb;
+    const int pe = min(s1, seg_end);
+    const int L = min(max(a.seq_lens[b], 0), a.capacity);
+    const int c0 = (s - seg_start) * kSlab;
+    const int c1 = min((pe - seg_start) * kSlab, L);
+    float M, lsum, o0, o1;
+    attend_range<QT, KVT>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
+    const size_t head = (size_t)b * kQHeads + kGroup * g + er;
+    if (s == seg_start && pe == seg_end) {
+      const float inv = a.v_scale / lsum;
+      E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
+    } else {
+      const size_t slot = 2 * (size_t)w + (s == s0 ? 0 : 1);
+      const size_t row = slot * kGroup + er;
+      *reinterpret_cast<float2*>(a.part_o + row * kHeadDim + ed) = make_float2(o0, o1);
+      if ((tid & 63) == 0) *reinterpret_cast<float2*>(a.part_ml + row * 2) = make_float2(M, lsum);
+    }
+    s = pe;
+  }
+}
+
+// Merge of the balanced split, one workgroup per (request, KV head); wave r
+// takes query head 4g + r. Heads that one workgroup covered whole were
+// written by it; empty heads get zeros.
+template <int QT>
+__global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs a) {
+  using E = Elem<QT>;
+  const int bg = blockIdx.x;
+  const int b = bg / kKvHeads;
+  const int g = bg % kKvHeads;
+  const int lane = threadIdx.x & 63;
+  const int r = threadIdx.x >> 6;
+  const size_t head = (size_t)b * kQHeads + kGroup * g + r;
+  char* outp = static_cast<char*>(a.out) + (head * kHeadDim + 2 * lane) * 2;
+  const int64_t N = a.slab_prefix[a.batch];
+  const int nsb = (a.slab_prefix[b + 1] - a.slab_prefix[b]) / kKvHeads;
+  if (nsb == 0) {
+    E::store2(outp, 0.f, 0.f);
+    return;
+  }
+  const int64_t G = a.grid_wgs;
+  const int64_t seg_start = a.slab_prefix[b] + (int64_t)g * nsb;
+  const int64_t seg_end = seg_start + nsb;
+  // workgroup whose range holds slab t: the largest w with w N / G <= t
+  const int wf = (int)(((seg_start + 1) * G - 1) / N);
+  const int wl = (int)((seg_end * G - 1) / N);
+  if (wf == wl) return;
+  // wf's range may begin in an earlier head: then this head is its last piece
+  const int first_slot_bump = ((int64_t)wf * N / G < seg_start) ? 1 : 0;
+  merge_rows<QT>(a, wl - wf + 1,
+                 [&](int k) -> size_t {
+                   return (2 * (size_t)(wf + k) + (k == 0 ? first_slot_bump : 0)) * kGroup + r;
+                 },
+                 outp);
+}
+
 template <int QT, int KVT>
 hipError_t enqueue_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
-  const unsigned wgs = (unsigned)a.batch * kKvHeads * (unsigned)a.num_splits;
   hipError_t e;
+  if (a.grid_wgs > 0) {   // balanced split
+    hipLaunchKernelGGL((gqa_balanced_attention_kernel<QT, KVT>), dim3(a.grid_wgs), dim3(kThreads), 0,
+                       stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev_mid != nullptr && (e = hipEventRecord(ev_mid, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL((gqa_balanced_combine_kernel<QT>), dim3((unsigned)a.batch * kKvHeads),
+                       dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  const unsigned wgs = (unsigned)a.batch * kKvHeads * (unsigned)a.num_splits;
   const bool separate = a.num_splits > 1 && !a.fused_combine;
   if (a.num_splits == 1) {
     hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, kModeDirect>), dim3(wgs), dim3(kThreads), 0,
@@ -565,7 +771,27 @@ hipError_t enqueue_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mi
   return hipGetLastError();
 }
 
+template <int QT, int KVT>
+int balanced_grid_typed() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&gqa_balanced_attention_kernel<QT, KVT>), kThreads,
+          0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
+}
+
 }  // namespace
+
+int balanced_grid_size(int q_dtype, int kv_dtype) {
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return balanced_grid_typed<kBF16, kBF16>();
+  if (q_dtype == kF16 && kv_dtype == kF16) return balanced_grid_typed<kF16, kF16>();
+  if (q_dtype == kBF16 && kv_dtype == kFP8) return balanced_grid_typed<kBF16, kFP8>();
+  if (q_dtype == kF16 && kv_dtype == kFP8) return balanced_grid_typed<kF16, kFP8>();
+  return 0;
+}
 
 hipError_t enqueue_decode_step(const StepArgs& a, int q_dtype, int kv_dtype, hipStream_t stream,
                                hipEvent_t ev_mid) {

@@ -24,7 +24,7 @@ import statistics
 
 from .build import CSRC
 
-KERNEL_MATCH = "gqa_attention_kernel"
+KERNEL_MATCH = "attention_kernel"   # gqa_attention_kernel or gqa_balanced_attention_kernel
 COPY_MATCH = "copy_stream_kernel"
 
 
@@ -67,7 +67,7 @@ def cmd_traffic(a):
     wscale = a.copy_bytes / cwrite          # bytes per WRITE_SIZE unit
     fb, wb = fetch * fscale, write * wscale
     lines = [
-        f"# HBM traffic per launch of {KERNEL_MATCH}, workload {a.workload}",
+        f"# HBM traffic per launch of the attention kernel ({a.kernel}), workload {a.workload}",
         "#",
         f"# command (FETCH_SIZE pass; WRITE_SIZE pass identical but for the counter): {a.command}",
         f"# calibration: {COPY_MATCH} copies {a.copy_bytes} bytes per launch; it reads "
@@ -105,6 +105,7 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--algorithmic-bytes", type=int, required=True)
     t.add_argument("--num-splits", type=int, default=0)
+    t.add_argument("--kernel", default="gqa_balanced_attention_kernel")
     a = ap.parse_args()
     cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
 

@@ -111,13 +111,25 @@ typedef struct gqa_desc {
  * is opt-in. */
 #define GQA_FLAG_FUSED_COMBINE 1
 
-/* Launch plan chosen for a descriptor (host arithmetic only). */
+/* Launch plan chosen for a descriptor (host arithmetic only).
+ * route 0 (short, capacity <= 64) and single-chunk plans: one workgroup per
+ * (request, KV head), output normalised in place, no workspace.
+ * route 1 (chunked split, explicit num_splits >= 2, or the fused merge):
+ * num_splits chunks of chunk_tokens slots per (request, KV head) -> FP32
+ * partials -> log-sum-exp combine, as the article's split routes.
+ * route 2 (balanced split, the automatic choice above capacity 64 for up to
+ * 4096 requests when the cache holds at least 768 slabs of 64 slots across
+ * all (request, KV head) pairs; smaller problems use the chunked split): a
+ * persistent grid of num_workgroups workgroups shares the
+ * step's 64-slot slabs evenly (computed on the device from the lengths);
+ * heads a workgroup covers whole are written directly, the rest are merged
+ * by the combine kernel. num_splits is 0 (varies per head), chunk_tokens 64. */
 typedef struct gqa_plan {
-  int32_t route;           /* 0 = short (capacity <= 64), 1 = split */
-  int32_t num_splits;      /* chunks per (request, KV head); 1 = no combine */
-  int32_t chunk_tokens;    /* tokens per chunk, a multiple of GQA_CHUNK_GRANULE */
+  int32_t route;
+  int32_t num_splits;      /* chunks per (request, KV head); 1 = no combine; 0 = balanced */
+  int32_t chunk_tokens;    /* tokens per chunk (multiple of GQA_CHUNK_GRANULE) or slab (64) */
   int32_t num_workgroups;  /* workgroups of the attention kernel */
-  uint64_t workspace_bytes;/* FP32 partials (+ per-head counters); 0 when num_splits == 1 */
+  uint64_t workspace_bytes;/* FP32 partials (+ counters / slab prefix); 0 when no merge */
 } gqa_plan_t;
 
 typedef struct gqa_prepared gqa_prepared_t;
@@ -137,7 +149,8 @@ GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const voi
  * buffers (non-null, 16-byte aligned, out not overlapping q/kv/seq_lens by
  * address range), requires q_scale finite and > 0, picks the route, and
  * allocates the FP32 split workspace once with hipMalloc on the current
- * device. num_splits: 0 = automatic; 1 = one chunk per (request, KV head)
+ * device. num_splits: 0 = automatic (the balanced split, sized for the current
+ * device); 1 = one chunk per (request, KV head)
  * with the output normalised in place; n >= 2 = exactly n chunks — a value
  * the chunking cannot honour exactly (ceil(capacity / chunk) != n with chunk
  * a multiple of 16) is rejected with GQA_ERR_INVALID_ARG, never replaced.
@@ -183,7 +196,9 @@ GQA_API gqa_status_t gqa_validate_args(const gqa_desc_t* desc, const void* q, co
                                        const void* out, int32_t num_splits);
 
 /* Host-only planning: the route, chunking and workspace a call would use
- * (num_splits as for prepare_gqa_decode). Runs without a GPU. */
+ * (num_splits as for prepare_gqa_decode). Runs without a GPU, so a balanced
+ * plan assumes 768 resident workgroups (256 CUs x 3); prepare uses the
+ * device's own figure. */
 GQA_API gqa_status_t gqa_plan_decode(const gqa_desc_t* desc, int32_t num_splits,
                                      gqa_plan_t* plan);
 

@@ -126,14 +126,37 @@ def test_plan_routes_on_capacity():
         assert p["route"] == 0 and p["num_splits"] == 1 and p["workspace_bytes"] == 0
         assert p["chunk_tokens"] >= C
     for C in (65, 1024, 131072):
-        assert b.gqa_plan(desc(capacity=C))["route"] == 1
+        big = C * 2 * 8 // 64 >= 768
+        assert b.gqa_plan(desc(capacity=C))["route"] == (2 if big else 1)  # balanced when it fills
+        assert b.gqa_plan(desc(capacity=C), 2)["route"] == 1   # explicit split count: chunked
+
+
+def balanced_ws(B, G=768):
+    # partials: 2 slots per workgroup x 4 rows x (128 + 2) floats; slab prefix [B + 1] ints
+    return 2 * G * 4 * 130 * 4 + ((4 * (B + 1) + 255) // 256) * 256
 
 
 @pytest.mark.parametrize("C", [65, 100, 1000, 1024, 8192, 65536, 131072])
-@pytest.mark.parametrize("B", [1, 8, 32])
-def test_auto_plan_is_consistent(B, C):
+@pytest.mark.parametrize("B", [1, 8, 32, 4096])
+def test_auto_plan_is_the_balanced_split(B, C):
     p = b.gqa_plan(desc(batch=B, capacity=C))
+    if B * 8 * -(-C // 64) < 768:      # too small to fill the grid: chunked split
+        assert p["route"] == 1
+        return
+    assert p == {"route": 2, "num_splits": 0, "chunk_tokens": 64, "num_workgroups": 768,
+                 "workspace_bytes": balanced_ws(B)}
+
+
+@pytest.mark.parametrize("C", [65, 1000, 8192, 65536, 131072])
+@pytest.mark.parametrize("B", [1, 32, 4097])
+def test_chunked_auto_plan_is_consistent(B, C):
+    """Beyond 4096 requests, or with the fused merge, auto picks the chunked split."""
+    d = desc(batch=B, capacity=C)
+    if B <= 4096:
+        d.flags = b.GQA_FLAG_FUSED_COMBINE
+    p = b.gqa_plan(d)
     S, T = p["num_splits"], p["chunk_tokens"]
+    assert p["route"] == 1
     assert T % 16 == 0 and T % 64 == 0
     assert S == -(-C // T)
     assert p["num_workgroups"] == B * 8 * S

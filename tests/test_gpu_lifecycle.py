@@ -33,13 +33,14 @@ def _prepare(inp, out, num_splits=None, fused_combine=False):
 
 
 @pytest.mark.parametrize("kd", ["bf16", "fp8_e4m3"])
-@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
-def test_graph_replay_with_rewritten_lengths_matches_direct_launch(kd, fused):
+@pytest.mark.parametrize("plan", ["balanced", "chunked", "fused"])
+def test_graph_replay_with_rewritten_lengths_matches_direct_launch(kd, plan):
     b = binding()
     inp = _inputs(kd=kd)
     out = torch.empty_like(inp["q"])
-    prep = _prepare(inp, out, fused_combine=fused)
-    assert prep.plan["num_splits"] > 1 and prep.workspace_bytes > 0
+    prep = _prepare(inp, out, num_splits=None if plan == "balanced" else 8,
+                    fused_combine=plan == "fused")
+    assert prep.plan["route"] == (2 if plan == "balanced" else 1) and prep.workspace_bytes > 0
     lens = inp["seq_lens"]
 
     side = torch.cuda.Stream()

@@ -80,10 +80,43 @@ def test_fused_combine_variant(qd, kd, num_splits):
     lens = torch.tensor([1000, 999, 1, 64, 65], dtype=torch.int32)
     inp = make_inputs(w, device="cuda", seq_lens=lens)
     out, prep = run_decode(inp, "prepared", num_splits=num_splits, fused_combine=True)
+    assert prep.plan["route"] == 1
     compare(out, oracle_pairs(inp, all_pairs(w.batch)), inp, f"{w.name}/fused/S={num_splits}")
-    sep, _ = run_decode(inp, "prepared", num_splits=num_splits)
-    # Same chunk partials, same merge order: identical bits.
-    assert torch.equal(out.view(torch.int16), sep.view(torch.int16))
+    if num_splits is not None:
+        sep, _ = run_decode(inp, "prepared", num_splits=num_splits)
+        # Same chunk partials, same merge order: identical bits.
+        assert torch.equal(out.view(torch.int16), sep.view(torch.int16))
+
+
+@pytest.mark.parametrize("qd,kd", DTYPE_PAIRS)
+@pytest.mark.parametrize("case", ["fewer_slabs_than_workgroups", "one_long_head",
+                                  "mixed_with_empty", "many_requests"])
+def test_balanced_split_partitions(qd, kd, case):
+    """The balanced split covers every head exactly once whatever the mix of
+    lengths: heads shorter than a workgroup's share, one head spread over the
+    whole grid, empty requests in between, and many short requests."""
+    if case == "fewer_slabs_than_workgroups":   # 104 slabs for hundreds of workgroups
+        B, C, lens = 6, 4096, [1, 65, 200, 17, 128, 129]
+    elif case == "one_long_head":
+        B, C, lens = 1, 70000, [69999]
+    elif case == "mixed_with_empty":
+        B, C, lens = 7, 5000, [0, 4999, 1, 0, 5000, 2500, 64]
+    else:
+        B, C = 300, 320
+        lens = [(37 * i) % 321 for i in range(B)]
+    w = _small(qd, kd, C=C, B=B, seed=90 + len(case))
+    inp = make_inputs(w, device="cuda", seq_lens=torch.tensor(lens, dtype=torch.int32))
+    out = torch.full_like(inp["q"], float("nan"))
+    out, prep = run_decode(inp, "prepared", out=out)
+    assert prep.plan["route"] == 2
+    got = decoded_out(out, qd)
+    empty = [i for i, L in enumerate(lens) if L == 0]
+    for i in empty:
+        assert np.all(got[i] == 0), i
+    pairs = [(i, g) for i in range(B) if lens[i] > 0 for g in range(8)]
+    if len(pairs) > 240:
+        pairs = pairs[::7]
+    compare(out, oracle_pairs(inp, pairs), inp, f"balanced/{case}/{qd}/{kd}")
 
 
 @pytest.mark.parametrize("qd,kd", DTYPE_PAIRS)
