@@ -251,3 +251,72 @@ def test_rejects_lengths_outside_capacity(L):
     q, kv, _ = _rand_case(rng, 1, 4)
     with pytest.raises(ValueError):
         gqa_decode_reference(q, kv, [L])
+
+
+# ---------------------------------------------------------------- KV append (fp8 encode)
+from oracle.kv_append import encode_e4m3fn, kv_append_reference, quantise_fp8  # noqa: E402
+
+
+def test_e4m3fn_encode_round_trips_every_code():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(encode_e4m3fn(decode_e4m3fn_bits(codes)), codes)
+
+
+def test_e4m3fn_encode_matches_torch_inside_the_range():
+    """Library special case: torch's cast rounds to nearest-even; it agrees
+    with ours wherever it does not overflow (|x| <= 464)."""
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    for vals in (decode_f16_bits(bits), decode_bf16_bits(bits)):
+        vals = vals[np.isfinite(vals) & (np.abs(vals) <= 464.0)]
+        ref = torch.from_numpy(vals.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(encode_e4m3fn(vals), ref)
+
+
+def test_e4m3fn_encode_is_nearest_with_ties_to_even_brute_force():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    vals = decode_e4m3fn_bits(codes)
+    rng = np.random.default_rng(31)
+    pos = np.unique(vals[vals > 0])
+    midpoints = (pos[:-1] + pos[1:]) / 2          # exact ties between neighbouring codes
+    xs = np.concatenate([rng.uniform(-447.9, 447.9, 3000), rng.uniform(-0.02, 0.02, 3000),
+                         midpoints, -midpoints, [pos[0] / 2]])
+    got = encode_e4m3fn(xs)
+    for x, g in zip(xs, got):
+        d = np.abs(vals - x)
+        best = np.flatnonzero(d == d.min())
+        cand = codes[best]
+        if len(cand) > 1:   # a tie: the even mantissa wins (+0 and -0 are one value)
+            even = [c for c in cand if (c & 1) == 0 and (math.copysign(1, x) < 0) == bool(c & 0x80)]
+            cand = even or [c for c in cand if (c & 1) == 0]
+        assert g in cand, (x, hex(g), [hex(c) for c in cand])
+
+
+def test_e4m3fn_encode_saturates_and_keeps_nan():
+    x = np.array([448.0, 449.0, 464.0, 465.0, 1e30, np.inf, -448.5, -np.inf, np.nan, 0.0, -0.0])
+    assert [hex(c) for c in encode_e4m3fn(x)] == ["0x7e", "0x7e", "0x7e", "0x7e", "0x7e", "0x7e",
+                                                "0xfe", "0xfe", "0x7f", "0x0", "0x80"]
+
+
+def test_quantise_divides_in_fp32():
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal(20000).astype(np.float32)
+    scale = 0.0137
+    ref = (torch.from_numpy(x) / torch.tensor(scale, dtype=torch.float32)).clamp(-448, 448)
+    ref = ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(quantise_fp8(x, scale), ref)
+
+
+def test_kv_append_writes_only_the_target_slots():
+    rng = np.random.default_rng(33)
+    B, C = 3, 7
+    kv = rng.integers(0, 256, size=(B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=np.uint8)
+    k_new = rng.standard_normal((B, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    v_new = rng.standard_normal((B, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    pos = [6, -1, 7]          # request 1 and 2 fall outside [0, C): nothing written
+    out = kv_append_reference(kv, k_new, v_new, pos, "fp8_e4m3", 0.25, 0.5)
+    assert np.array_equal(out[1:], kv[1:])
+    mask = np.ones(C, dtype=bool)
+    mask[6] = False
+    assert np.array_equal(out[0][:, :, mask], kv[0][:, :, mask])
+    assert np.array_equal(out[0, 0, :, 6], quantise_fp8(k_new[0], 0.25))
+    assert np.array_equal(decode_e4m3fn_bits(out[0, 1, :, 6]), decode_e4m3fn_bits(quantise_fp8(v_new[0], 0.5)))
