@@ -204,6 +204,22 @@ def main():
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (attn_avg * 1e-3) / 1e9
 
+    # KV append (the cache write before each step): one token per request at
+    # slot L_b, past the valid prefix, so the decode inputs are unchanged.
+    k_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
+    v_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
+    slots = inp["seq_lens"].clamp(max=w.capacity - 1)
+    for _ in range(3):
+        b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
+    a_begin, a_end = new_event(), new_event()
+    torch.cuda.synchronize()
+    a_begin.record(stream)
+    for _ in range(K):
+        b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
+    a_end.record(stream)
+    torch.cuda.synchronize()
+    append_us = a_begin.elapsed_time(a_end) / K * 1e3
+
     # Cold-cache calls: a 512 MiB write evicts the caches before each timed call.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     cold = []
@@ -242,6 +258,7 @@ def main():
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_cold": {"p10": round(pct(cold, 10), 2), "p50": round(pct(cold, 50), 2),
                              "p90": round(pct(cold, 90), 2)} if cold else None,
+        "kv_append_us": round(append_us, 2),
         "kernels_us": {"attention_avg": round(attn_avg * 1e3, 2),
                        "attention_min": round(min(attn_ms) * 1e3, 2),
                        "combine_avg": round(statistics.fmean(comb_ms) * 1e3, 2)},

@@ -81,6 +81,7 @@ _prep_plan = _sig("gqa_prepared_plan", ctypes.c_int, [_vp, _PlanP])
 _validate = _sig("gqa_validate_args", ctypes.c_int, [_DescP, _vp, _vp, _vp, _f32, _vp, _i32])
 _plan = _sig("gqa_plan_decode", ctypes.c_int, [_DescP, _i32, _PlanP])
 _last_error = _sig("gqa_last_error", ctypes.c_char_p, [])
+_append = _sig("gqa_kv_append", ctypes.c_int, [_DescP, _vp, _vp, _vp, _vp, _vp])
 
 
 class GqaError(RuntimeError):
@@ -238,6 +239,30 @@ def launch_gqa_decode_prepared_timed(prepared: GqaPrepared, ev_start, ev_mid, ev
     hs = [None if e is None else e.cuda_event for e in (ev_start, ev_mid, ev_end)]
     _check(_launch_timed(prepared.handle, _stream_handle(stream, dev), *hs))
     return prepared.out
+
+
+def gqa_kv_append(kv: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                  positions: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
+                  stream=None) -> torch.Tensor:
+    """Write k_new/v_new [batch, 8, 128] at slot positions[b] of every KV head; returns kv."""
+    _check_devices(kv, k_new, v_new, positions)
+    if positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same shape and dtype")
+    if k_new.dim() != 3 or kv.dim() != 5 or k_new.shape[0] != kv.shape[0]:
+        raise ValueError("k_new/v_new must be [batch, 8, 128] and kv [batch, 2, 8, capacity, 128]")
+    desc = GqaDesc(batch=kv.shape[0], capacity=kv.shape[3], num_q_heads=NUM_Q_HEADS,
+                   num_kv_heads=k_new.shape[1], head_dim=k_new.shape[2],
+                   q_dtype=_dtype_code(k_new, "q"), kv_dtype=_dtype_code(kv, "kv"),
+                   k_scale=k_scale, v_scale=v_scale, flags=0)
+    if kv.shape[2] != k_new.shape[1] or kv.shape[4] != k_new.shape[2]:
+        raise ValueError("kv and k_new disagree on KV heads or head_dim")
+    with torch.cuda.device(kv.device):
+        st = _append(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(kv),
+                     _stream_handle(stream, kv.device))
+    _check(st)
+    return kv
 
 
 def gqa_validate_args(desc: GqaDesc, q_ptr: Optional[int], kv_ptr: Optional[int],

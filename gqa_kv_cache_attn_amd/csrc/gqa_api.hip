@@ -475,4 +475,38 @@ GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const voi
   return enqueue(step_args(desc, q, kv, seq_lens, q_scale, out, p, ws), desc, stream);
 }
 
+GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,
+                                   const int32_t* positions, void* kv, hipStream_t stream) {
+  gqa_status_t st = check_desc(desc);
+  if (st != GQA_OK) return st;
+  if (desc->batch == 0) return ok();
+  if (!k_new || !v_new || !positions || !kv)
+    return fail(GQA_ERR_INVALID_ARG, "k_new, v_new, positions and kv must be non-NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv, 16) || !aligned(positions, 4))
+    return fail(GQA_ERR_INVALID_ARG,
+                "k_new, v_new and kv must be 16-byte aligned and positions 4-byte aligned");
+  const size_t B = (size_t)desc->batch;
+  const size_t row_bytes = B * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * elem_bytes(desc->q_dtype);
+  const size_t kv_bytes =
+      B * 2 * GQA_NUM_KV_HEADS * (size_t)desc->capacity * GQA_HEAD_DIM * elem_bytes(desc->kv_dtype);
+  if (ranges_overlap(kv, kv_bytes, k_new, row_bytes) || ranges_overlap(kv, kv_bytes, v_new, row_bytes) ||
+      ranges_overlap(kv, kv_bytes, positions, B * sizeof(int32_t)))
+    return fail(GQA_ERR_ALIAS, "kv must not overlap k_new, v_new or positions");
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != GQA_OK) return st;
+  gqa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.positions = positions;
+  a.kv = kv;
+  a.batch = desc->batch;
+  a.capacity = desc->capacity;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
+  hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"

@@ -33,6 +33,20 @@ struct StepArgs {
   int32_t grid_wgs;          // > 0: balanced split with this many persistent workgroups
 };
 
+// Arguments of one KV append (one new token per request).
+struct AppendArgs {
+  const void* k_new;         // [batch, 8, 128] 16-bit
+  const void* v_new;         // [batch, 8, 128] 16-bit
+  const int32_t* positions;  // [batch] slot to write; outside [0, capacity) -> skipped
+  void* kv;                  // [batch, 2, 8, capacity, 128] kv dtype
+  int32_t batch;
+  int32_t capacity;
+  float k_scale;             // fp8 cache: stored code = e4m3(k / k_scale)
+  float v_scale;
+};
+
+hipError_t enqueue_kv_append(const AppendArgs& args, int src_dtype, int kv_dtype, hipStream_t stream);
+
 // Workgroups of the balanced split that the current device keeps resident at
 // once (CUs x resident workgroups per CU); 0 if the query fails.
 int balanced_grid_size(int q_dtype, int kv_dtype);

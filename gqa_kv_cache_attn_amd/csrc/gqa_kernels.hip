@@ -771,6 +771,73 @@ hipError_t enqueue_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mi
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// KV append: write one new token's K and V rows of every KV head at slot
+// positions[b] (the cache write that precedes each decode step). An fp8
+// cache stores e4m3(x / scale), per-tensor scales as in the Thor FP8-KV
+// notes; the division is an IEEE fp32 division and the code the nearest
+// E4M3FN value (ties to even), saturating at +-448.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32 f32_to_e4m3fn_sat(float x) {
+  const u32 bits = __float_as_uint(x);
+  const u32 sign = (bits >> 24) & 0x80u;
+  const u32 mag = bits & 0x7fffffffu;
+  if (mag > 0x7f800000u) return 0x7fu;           // NaN
+  if (mag >= 0x43e00000u) return sign | 0x7eu;   // |x| >= 448, infinities included
+  if (mag < 0x3c800000u) {                       // |x| < 2^-6: codes m * 2^-9, m = 0..8
+    const float v = __uint_as_float(mag) * 512.0f;   // exact
+    return sign | (u32)__builtin_rintf(v);            // round half to even
+  }
+  u32 e = (mag >> 23) - 120u;                    // exponent field 1..15
+  u32 q = (mag >> 20) & 7u;                      // top 3 mantissa bits
+  const u32 rest = mag & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (q & 1u))) ++q;
+  if (q == 8u) {
+    q = 0u;
+    ++e;
+  }
+  return sign | (e << 3) | q;
+}
+
+template <int QT, int KVT>
+__global__ __launch_bounds__(256) void gqa_kv_append_kernel(AppendArgs a) {
+  using E = Elem<QT>;
+  // one thread per 8 dims of one (request, plane, KV head) row
+  const int t = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (t >= a.batch * 2 * kKvHeads * (kHeadDim / 8)) return;
+  const int chunk = t % (kHeadDim / 8);
+  const int row = t / (kHeadDim / 8);
+  const int g = row % kKvHeads;
+  const int plane = (row / kKvHeads) % 2;
+  const int b = row / (2 * kKvHeads);
+  const int pos = a.positions[b];
+  if (pos < 0 || pos >= a.capacity) return;
+  const char* src = static_cast<const char*>(plane ? a.v_new : a.k_new) +
+                    (((size_t)b * kKvHeads + g) * kHeadDim + chunk * 8) * 2;
+  const u32x4 in = *reinterpret_cast<const u32x4*>(src);
+  const size_t dst = ((((size_t)b * 2 + plane) * kKvHeads + g) * a.capacity + pos) * kHeadDim + chunk * 8;
+  if constexpr (KVT == kFP8) {
+    const float scale = plane ? a.v_scale : a.k_scale;
+    u32 w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float x = (i & 1) ? E::hi(in[i >> 1]) : E::lo(in[i >> 1]);
+      w[i >> 2] |= f32_to_e4m3fn_sat(__fdiv_rn(x, scale)) << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x2*>(static_cast<char*>(a.kv) + dst) = (u32x2){w[0], w[1]};
+  } else {
+    *reinterpret_cast<u32x4*>(static_cast<char*>(a.kv) + dst * 2) = in;
+  }
+}
+
+template <int QT, int KVT>
+hipError_t enqueue_append_typed(const AppendArgs& a, hipStream_t stream) {
+  const int threads = a.batch * 2 * kKvHeads * (kHeadDim / 8);
+  hipLaunchKernelGGL((gqa_kv_append_kernel<QT, KVT>), dim3((threads + 255) / 256), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <int QT, int KVT>
 int balanced_grid_typed() {
   int dev = 0, cus = 0, per_cu = 0;
@@ -791,6 +858,14 @@ int balanced_grid_size(int q_dtype, int kv_dtype) {
   if (q_dtype == kBF16 && kv_dtype == kFP8) return balanced_grid_typed<kBF16, kFP8>();
   if (q_dtype == kF16 && kv_dtype == kFP8) return balanced_grid_typed<kF16, kFP8>();
   return 0;
+}
+
+hipError_t enqueue_kv_append(const AppendArgs& a, int src_dtype, int kv_dtype, hipStream_t stream) {
+  if (src_dtype == kBF16 && kv_dtype == kBF16) return enqueue_append_typed<kBF16, kBF16>(a, stream);
+  if (src_dtype == kF16 && kv_dtype == kF16) return enqueue_append_typed<kF16, kF16>(a, stream);
+  if (src_dtype == kBF16 && kv_dtype == kFP8) return enqueue_append_typed<kBF16, kFP8>(a, stream);
+  if (src_dtype == kF16 && kv_dtype == kFP8) return enqueue_append_typed<kF16, kFP8>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t enqueue_decode_step(const StepArgs& a, int q_dtype, int kv_dtype, hipStream_t stream,

@@ -188,6 +188,22 @@ GQA_API size_t gqa_prepared_workspace_bytes(const gqa_prepared_t* handle);
 /* Copy of the handle's launch plan; GQA_ERR_INVALID_ARG for NULL arguments. */
 GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* handle, gqa_plan_t* plan);
 
+/* Append one token per request to the cache: writes the K row k_new[b, g, :]
+ * and the V row v_new[b, g, :] of every KV head g at slot positions[b] of
+ * request b (the cache write that precedes each decode step; Thor Qwen3-VL
+ * doc, "Runtime architecture", RoPE and KV writes). Layouts: k_new, v_new
+ * [batch, 8, 128] in desc->q_dtype (F16 or BF16), 16-byte aligned; positions
+ * int32 [batch], read on the device only, 4-byte aligned; kv as for
+ * gqa_decode, written in place. A 16-bit cache (kv dtype == q dtype) stores
+ * the values as they are. An FP8_E4M3 cache stores e4m3(x / k_scale) for K
+ * and e4m3(x / v_scale) for V (Thor FP8-KV notes, section 1): IEEE fp32
+ * division, nearest E4M3FN code with ties to even, magnitudes >= 448
+ * saturating to +-448, NaN stored as 0x7F. Positions outside [0, capacity)
+ * write nothing. kv must not overlap k_new, v_new or positions
+ * (GQA_ERR_ALIAS). Asynchronous on `stream`; allocates nothing. */
+GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,
+                                   const int32_t* positions, void* kv, hipStream_t stream);
+
 /* Host-only validation of a call's arguments (never touches a device, so it
  * runs without a GPU). Same checks and status codes as prepare_gqa_decode,
  * except the device check. */

@@ -194,3 +194,14 @@ def test_error_message_is_thread_local_and_cleared_on_success():
     assert "q_scale" in b.last_error()
     assert v(desc()) == OK
     assert b.last_error() == ""
+
+
+def test_kv_append_rejects_bad_arguments_without_touching_a_device():
+    d = desc(batch=2, capacity=16)
+    K, V, P, KV_ = (1 << 30), (5 << 30), (3 << 30), (2 << 30)
+    app = b._append
+    assert app(ctypes.byref(d), None, V, P, KV_, None) == INVALID
+    assert app(ctypes.byref(d), K + 4, V, P, KV_, None) == INVALID      # misaligned
+    assert app(ctypes.byref(d), KV_ + 4096, V, P, KV_, None) == ALIAS    # k_new inside the cache
+    d0 = desc(batch=0)
+    assert app(ctypes.byref(d0), None, None, None, None, None) == OK

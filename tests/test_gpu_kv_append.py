@@ -1,0 +1,106 @@
+"""GPU parity of the KV append (cache write before each decode step): the cache
+after gqa_kv_append equals the oracle's, byte for byte."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import Workload, all_pairs, binding, compare, make_inputs, oracle_pairs, require_gpu
+from gqa_kv_cache_attn_amd.inputs import storage_bits
+from oracle import decode_storage
+from oracle.kv_append import kv_append_reference
+
+pytestmark = pytest.mark.gpu
+
+TORCH = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _expected(kv, k_new, v_new, positions, src, kd, ks, vs):
+    kv_bits = storage_bits(kv)
+    k_bits, v_bits = storage_bits(k_new), storage_bits(v_new)
+    with np.errstate(invalid="ignore"):      # NaN patterns stay NaN
+        k32 = decode_storage(k_bits, src).astype(np.float32)
+        v32 = decode_storage(v_bits, src).astype(np.float32)
+    return kv_append_reference(kv_bits, k32, v32, positions.cpu().numpy(), kd, ks, vs,
+                               new_bits=(k_bits, v_bits))
+
+
+@pytest.mark.parametrize("src,kd,ks,vs", [("f16", "f16", 1.0, 1.0), ("bf16", "bf16", 1.0, 1.0),
+                                          ("bf16", "fp8_e4m3", 1 / 64, 1 / 64),
+                                          ("f16", "fp8_e4m3", 0.0137, 0.75)])
+def test_append_is_byte_exact(src, kd, ks, vs):
+    B, C = 5, 300
+    w = Workload("append", B, C, 1, C, src, kd, k_scale=ks, v_scale=vs, seed=51)
+    inp = make_inputs(w, device="cuda")
+    kv = inp["kv"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(52)
+    k_new = (torch.randn(B, 8, 128, generator=gen, device="cuda") * 40).to(TORCH[src])
+    v_new = (torch.randn(B, 8, 128, generator=gen, device="cuda") * 3).to(TORCH[src])
+    k_new[0, 0, :6] = torch.tensor([float("nan"), float("inf"), -float("inf"), 0.0, -0.0, 1e-7])
+    positions = torch.tensor([0, 299, 17, -1, 300], dtype=torch.int32, device="cuda")
+    want = _expected(kv, k_new, v_new, positions, src, kd, ks, vs)
+    binding().gqa_kv_append(kv, k_new, v_new, positions, ks, vs)
+    torch.cuda.synchronize()
+    got = storage_bits(kv)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("src", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 1 / 64, 0.0137])
+def test_fp8_quantise_every_16bit_value(src, scale):
+    """Every one of the 65536 f16 (or bf16) bit patterns, through the device encoder."""
+    B = 64                                   # 64 * 8 * 128 = 65536 values per plane
+    bits = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16).view(torch.int16)
+    vals = bits.view(TORCH[src]).reshape(B, 8, 128).to("cuda")
+    kv = torch.zeros(B, 2, 8, 1, 128, dtype=torch.uint8, device="cuda")
+    positions = torch.zeros(B, dtype=torch.int32, device="cuda")
+    want = _expected(kv, vals, vals, positions, src, "fp8_e4m3", scale, scale)
+    binding().gqa_kv_append(kv, vals, vals.clone(), positions, scale, scale)
+    torch.cuda.synchronize()
+    got = storage_bits(kv)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} mismatches, first at {bad[:5]}"
+
+
+@pytest.mark.parametrize("src,kd", [("bf16", "bf16"), ("bf16", "fp8_e4m3")])
+def test_append_then_decode(src, kd):
+    """A decode step after appending token L at slot L attends over L + 1 tokens."""
+    B, C = 4, 2048
+    fp8 = kd == "fp8_e4m3"
+    w = Workload("append_decode", B, C, 1, C - 1, src, kd, q_scale=0.8,
+                 k_scale=1 / 64 if fp8 else 1.0, v_scale=1 / 64 if fp8 else 1.0, seed=53)
+    inp = make_inputs(w, device="cuda")
+    lens = inp["seq_lens"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(54)
+    k_new = torch.randn(B, 8, 128, generator=gen, device="cuda").to(TORCH[src])
+    v_new = torch.randn(B, 8, 128, generator=gen, device="cuda").to(TORCH[src])
+    b = binding()
+    b.gqa_kv_append(inp["kv"], k_new, v_new, lens, inp["k_scale"], inp["v_scale"])
+    lens += 1
+    out = b.gqa_decode(inp["q"], inp["kv"], lens, inp["q_scale"], k_scale=inp["k_scale"],
+                       v_scale=inp["v_scale"])
+    torch.cuda.synchronize()
+    compare(out, oracle_pairs(inp, all_pairs(B)), inp, f"append+decode {src}/{kd}")
+
+
+def test_append_argument_errors():
+    b = binding()
+    kv = torch.zeros(2, 2, 8, 16, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(2, 8, 128, dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):           # a scale on a 16-bit cache
+        b.gqa_kv_append(kv, k, k, pos, 0.5, 1.0)
+    with pytest.raises(ValueError):           # f16 rows into a bf16 cache
+        b.gqa_kv_append(kv, k.half(), k.half(), pos)
+    flat = kv.view(-1)
+    with pytest.raises(ValueError):           # k_new inside the cache
+        b.gqa_kv_append(kv, flat[:2 * 8 * 128].view(2, 8, 128), k, pos)
