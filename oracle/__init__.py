@@ -23,6 +23,7 @@ from .gqa_oracle import (  # noqa: F401
     decode_bf16_bits,
     decode_e4m3fn_bits,
     decode_f16_bits,
+    decode_int8_rows,
     decode_storage,
     gqa_decode_head,
     gqa_decode_reference,

@@ -14,7 +14,11 @@ What is computed (sources are the pages this project follows):
 * Head mapping. The kernel is handed ``q.view(batch, 8, 4, 128)`` transposed
   to ``[batch, 4, 8, 128]``, so query head ``h`` belongs to KV head ``h // 4``.
   [same article, "convenience API" (the q.view/transpose call) and the
-  launch-header description of EncodeQ.]
+  launch-header description of EncodeQ.] The 16-query-head geometry of the
+  INT8-KV decode (Orin Qwen3-VL doc, "INT8 KV cache": GQA 16Q/8KV) groups
+  2 query heads per KV head the same way: head ``h`` reads KV head ``h // 2``.
+* INT8 cache. One bf16 scale per (position, KV head) row: K = int8 * k_row_scale,
+  V = int8 * v_row_scale [same doc, same section]; decoded by decode_int8_rows.
 * Lengths. ``sequence_lengths[b]`` tokens of slot prefix ``[0, L)`` are the
   keys/values of request ``b``; slots ``>= L`` are not part of the attention.
   The pages make ``1 <= L <= capacity`` the caller's duty; the oracle raises
@@ -89,6 +93,18 @@ def decode_f16_bits(bits: np.ndarray) -> np.ndarray:
     return np.asarray(bits).astype(np.uint16).view(np.float16).astype(np.float64)
 
 
+def decode_int8_rows(values: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    """INT8 cache rows with one bf16 scale per row: value = int8 * scale.
+
+    The Orin Qwen3-VL doc ("INT8 KV cache") keeps INT8 mirrors of the cache
+    with one BF16 scale per (position, KV head) row. ``values`` [..., D] are
+    the int8 entries, ``scale_bits`` [...] the bf16 bit patterns of the row
+    scales; the product is exact in fp64.
+    """
+    v = np.asarray(values).astype(np.int8).astype(np.float64)
+    return v * decode_bf16_bits(scale_bits)[..., None]
+
+
 def decode_storage(bits: np.ndarray, dtype: str) -> np.ndarray:
     """Decode a raw stored array (``uint16`` for f16/bf16, ``uint8`` for fp8)."""
     if dtype == "f16":
@@ -136,8 +152,10 @@ def gqa_decode_head(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def _check_geometry(q: np.ndarray, kv: np.ndarray, seq_lens: np.ndarray):
-    if q.ndim != 3 or q.shape[1:] != (NUM_Q_HEADS, HEAD_DIM):
-        raise ValueError(f"q must be [batch, 32, 128], got {q.shape}")
+    # 32 query heads per request (4 per KV head), or 16 (2 per KV head, the
+    # INT8-KV decode geometry of the Orin Qwen3-VL doc).
+    if q.ndim != 3 or q.shape[1] not in (16, 32) or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [batch, 32 or 16, 128], got {q.shape}")
     if kv.ndim != 5 or kv.shape[1:3] != (2, NUM_KV_HEADS) or kv.shape[4] != HEAD_DIM:
         raise ValueError(f"kv must be [batch, 2, 8, capacity, 128], got {kv.shape}")
     if kv.shape[0] != q.shape[0] or np.shape(seq_lens) != (q.shape[0],):
@@ -156,11 +174,12 @@ def gqa_decode_reference(q: np.ndarray, kv: np.ndarray, seq_lens,
     q = np.asarray(q, dtype=np.float64)
     kv = np.asarray(kv, dtype=np.float64)
     lens = _check_geometry(q, kv, seq_lens)
+    group = q.shape[1] // NUM_KV_HEADS
     out = np.empty_like(q)
     for b in range(q.shape[0]):
         L = int(lens[b])
         for g in range(NUM_KV_HEADS):
-            rows = slice(GROUP * g, GROUP * (g + 1))   # heads h with h // 4 == g
+            rows = slice(group * g, group * (g + 1))   # heads h with h // group == g
             out[b, rows] = gqa_decode_head(q[b, rows], kv[b, 0, g, :L], kv[b, 1, g, :L],
                                            q_scale, k_scale, v_scale)
     return out
@@ -172,12 +191,13 @@ def gqa_decode_weights(q: np.ndarray, kv: np.ndarray, seq_lens,
     q = np.asarray(q, dtype=np.float64)
     kv = np.asarray(kv, dtype=np.float64)
     lens = _check_geometry(q, kv, seq_lens)
+    group = q.shape[1] // NUM_KV_HEADS
     res = []
     for b in range(q.shape[0]):
         L = int(lens[b])
-        w = np.empty((NUM_Q_HEADS, L))
+        w = np.empty((q.shape[1], L))
         for g in range(NUM_KV_HEADS):
-            rows = slice(GROUP * g, GROUP * (g + 1))
+            rows = slice(group * g, group * (g + 1))
             _, w[rows] = gqa_decode_head(q[b, rows], kv[b, 0, g, :L], kv[b, 1, g, :L],
                                          q_scale, k_scale, 1.0, return_weights=True)
         res.append(w)

@@ -320,3 +320,62 @@ def test_kv_append_writes_only_the_target_slots():
     assert np.array_equal(out[0][:, :, mask], kv[0][:, :, mask])
     assert np.array_equal(out[0, 0, :, 6], quantise_fp8(k_new[0], 0.25))
     assert np.array_equal(decode_e4m3fn_bits(out[0, 1, :, 6]), decode_e4m3fn_bits(quantise_fp8(v_new[0], 0.5)))
+
+
+# ---------------------------------------------------------------- INT8 KV, 16Q/8KV
+from oracle import decode_int8_rows  # noqa: E402
+
+
+def test_int8_row_decode_matches_torch():
+    rng = np.random.default_rng(41)
+    vals = rng.integers(-128, 128, size=(5, 7, HEAD_DIM)).astype(np.int8)
+    sbits = torch.randn(5, 7).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ref = (torch.from_numpy(vals).double() *
+           torch.from_numpy(sbits.view(np.int16)).view(torch.bfloat16).double()[..., None]).numpy()
+    assert np.array_equal(decode_int8_rows(vals, sbits), ref)
+
+
+def test_sixteen_query_heads_read_kv_head_h_div_2():
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((2, 16, HEAD_DIM))
+    kv = rng.standard_normal((2, 2, NUM_KV_HEADS, 9, HEAD_DIM))
+    for g in range(NUM_KV_HEADS):
+        kv[:, 1, g] = float(g)
+    out = gqa_decode_reference(q, kv, [9, 3])
+    for h in range(16):
+        np.testing.assert_allclose(out[:, h], float(h // 2), rtol=0, atol=1e-13)
+
+
+def test_sixteen_query_heads_match_sdpa_and_brute_force():
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((2, 16, HEAD_DIM))
+    kv = rng.standard_normal((2, 2, NUM_KV_HEADS, 6, HEAD_DIM))
+    lens = np.array([6, 2])
+    ref = gqa_decode_reference(q, kv, lens, 0.7)
+    brute = np.array(brute_decode(q.tolist(), kv.tolist(), lens.tolist(), 0.7))
+    np.testing.assert_allclose(ref, brute, rtol=0, atol=1e-12)
+    for b, L in enumerate(lens):
+        sd = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b]).view(1, 16, 1, HEAD_DIM),
+            torch.from_numpy(kv[b, 0, :, :L]).view(1, 8, L, HEAD_DIM),
+            torch.from_numpy(kv[b, 1, :, :L]).view(1, 8, L, HEAD_DIM),
+            scale=0.7 / math.sqrt(HEAD_DIM), enable_gqa=True)
+        np.testing.assert_allclose(ref[b], sd[0, :, 0].numpy(), rtol=0, atol=1e-12)
+
+
+def test_int8_row_scales_act_per_token():
+    """Closed form: two tokens with equal int8 keys but key scales s0 != s1 give
+    weights in ratio exp((s1 - s0) * q.k8 / sqrt(128)); V scales scale each row."""
+    k8 = np.zeros((2, HEAD_DIM), dtype=np.int8)
+    k8[:, 0] = 10
+    v8 = np.zeros((2, HEAD_DIM), dtype=np.int8)
+    v8[0, 1], v8[1, 1] = 20, -30
+    ks = torch.tensor([0.5, 0.25]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    vs = torch.tensor([2.0, 0.125]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    qrows = np.zeros((2, HEAD_DIM))
+    qrows[:, 0] = [1.0, -2.0]
+    out = gqa_decode_head(qrows, decode_int8_rows(k8, ks), decode_int8_rows(v8, vs))
+    for r in range(2):
+        gap = qrows[r, 0] * 10 * (0.25 - 0.5) / math.sqrt(HEAD_DIM)
+        w1 = 1 / (1 + math.exp(-gap))
+        assert out[r, 1] == pytest.approx((1 - w1) * 40.0 + w1 * (-3.75), rel=1e-14)
