@@ -55,10 +55,12 @@ def parse_args():
     return ap.parse_args()
 
 
-def algorithmic_bytes(lens, kv_dtype, batch):
-    """Valid K/V prefix bytes + q and out (16-bit) + int32 lengths; no padding, no workspace."""
-    e_kv = 1 if kv_dtype == "fp8_e4m3" else 2
-    return int(sum(lens)) * 8 * 2 * 128 * e_kv + batch * 32 * 128 * (2 + 2) + 4 * batch
+def algorithmic_bytes(lens, kv_dtype, batch, num_q_heads=32):
+    """Valid K/V prefix bytes (an INT8 cache's bf16 row scales included) + q and
+    out (16-bit) + int32 lengths; no padding, no workspace."""
+    from gqa_kv_cache_attn_amd.inputs import kv_slot_bytes
+    return (int(sum(lens)) * 8 * kv_slot_bytes(kv_dtype) + batch * num_q_heads * 128 * (2 + 2)
+            + 4 * batch)
 
 
 def kernel_source_digest():
@@ -94,8 +96,8 @@ def cpu_baseline(inp, w, budget_s):
     """Time the fp64 oracle (as it stands) on (request, KV head) pairs until the budget."""
     import numpy as np
 
-    from gqa_kv_cache_attn_amd.inputs import storage_bits
-    from oracle import decode_storage, gqa_decode_head
+    from gqa_kv_cache_attn_amd.inputs import kv_slot_bytes, storage_bits
+    from oracle import decode_int8_rows, decode_storage, gqa_decode_head
 
     try:
         from threadpoolctl import threadpool_info
@@ -103,20 +105,27 @@ def cpu_baseline(inp, w, budget_s):
     except Exception:   # pragma: no cover - threadpoolctl missing
         blas_threads = 1
     lens = inp["seq_lens"].cpu().numpy()
-    e_kv = 1 if w.kv_dtype == "fp8_e4m3" else 2
+    G = w.num_q_heads // 8
+    int8 = w.kv_dtype == "int8"
     pairs = [(b, g) for g in range(8) for b in range(w.batch)]
     spent, nbytes, done = 0.0, 0, 0
     for (b, g) in pairs:
         L = int(lens[b])
-        qb = storage_bits(inp["q"][b, 4 * g:4 * g + 4])          # D2H copies are not timed
+        qb = storage_bits(inp["q"][b, G * g:G * g + G])          # D2H copies are not timed
         kb = storage_bits(inp["kv"][b, 0, g, :L])
         vb = storage_bits(inp["kv"][b, 1, g, :L])
+        if int8:
+            ksb = storage_bits(inp["kv_scales"][b, 0, g, :L])
+            vsb = storage_bits(inp["kv_scales"][b, 1, g, :L])
         t0 = time.perf_counter()
-        out = gqa_decode_head(decode_storage(qb, w.q_dtype), decode_storage(kb, w.kv_dtype),
-                              decode_storage(vb, w.kv_dtype), w.q_scale, w.k_scale, w.v_scale)
+        if int8:
+            k, v = decode_int8_rows(kb, ksb), decode_int8_rows(vb, vsb)
+        else:
+            k, v = decode_storage(kb, w.kv_dtype), decode_storage(vb, w.kv_dtype)
+        out = gqa_decode_head(decode_storage(qb, w.q_dtype), k, v, w.q_scale, w.k_scale, w.v_scale)
         spent += time.perf_counter() - t0
         assert np.all(np.isfinite(out))
-        nbytes += L * 2 * 128 * e_kv + 4 * 128 * 4
+        nbytes += L * kv_slot_bytes(w.kv_dtype) + G * 128 * 4
         done += 1
         if spent >= budget_s:
             break
@@ -156,11 +165,17 @@ def main():
     print(f"[bench] device {arch}; workload {w.name}; generating inputs", file=sys.stderr, flush=True)
     inp = make_inputs(w, device=dev)
     lens = inp["seq_lens"].cpu().tolist()
-    nbytes = algorithmic_bytes(lens, w.kv_dtype, w.batch)
+    nbytes = algorithmic_bytes(lens, w.kv_dtype, w.batch, w.num_q_heads)
     out = torch.empty_like(inp["q"])
-    prep = b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
-                                num_splits=args.num_splits, k_scale=inp["k_scale"],
-                                v_scale=inp["v_scale"], fused_combine=args.fused_combine)
+    if w.kv_dtype == "int8":
+        prep = b.prepare_gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], out,
+                                         inp["q_scale"], num_splits=args.num_splits,
+                                         k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                                         fused_combine=args.fused_combine)
+    else:
+        prep = b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
+                                    num_splits=args.num_splits, k_scale=inp["k_scale"],
+                                    v_scale=inp["v_scale"], fused_combine=args.fused_combine)
     plan = prep.plan
     plan["combine"] = "fused (last workgroup)" if args.fused_combine else "separate kernel"
     stream = torch.cuda.current_stream(dev)
@@ -205,20 +220,23 @@ def main():
     achieved = nbytes / (attn_avg * 1e-3) / 1e9
 
     # KV append (the cache write before each step): one token per request at
-    # slot L_b, past the valid prefix, so the decode inputs are unchanged.
-    k_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
-    v_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
-    slots = inp["seq_lens"].clamp(max=w.capacity - 1)
-    for _ in range(3):
-        b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
-    a_begin, a_end = new_event(), new_event()
-    torch.cuda.synchronize()
-    a_begin.record(stream)
-    for _ in range(K):
-        b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
-    a_end.record(stream)
-    torch.cuda.synchronize()
-    append_us = a_begin.elapsed_time(a_end) / K * 1e3
+    # slot L_b, past the valid prefix, so the decode inputs are unchanged. An
+    # INT8 cache's rows and scales are written by the caller: not timed here.
+    append_us = None
+    if w.kv_dtype != "int8":
+        k_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
+        v_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
+        slots = inp["seq_lens"].clamp(max=w.capacity - 1)
+        for _ in range(3):
+            b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
+        a_begin, a_end = new_event(), new_event()
+        torch.cuda.synchronize()
+        a_begin.record(stream)
+        for _ in range(K):
+            b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
+        a_end.record(stream)
+        torch.cuda.synchronize()
+        append_us = round(a_begin.elapsed_time(a_end) / K * 1e3, 2)
 
     # Cold-cache calls: a 512 MiB write evicts the caches before each timed call.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -250,7 +268,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.kv_dtype if w.kv_dtype != "fp8_e4m3" else "fp8_e4m3->bf16",
+        "dtype": {"fp8_e4m3": "fp8_e4m3->bf16", "int8": f"int8+bf16 row scales->{w.q_dtype}"}
+                 .get(w.kv_dtype, w.kv_dtype),
         "data": "synthetic",
         "config": {**w.describe(), "seq_lens_sum": int(sum(lens)),
                    "algorithmic_bytes_per_step": nbytes, "plan": plan},
@@ -258,7 +277,7 @@ def main():
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_cold": {"p10": round(pct(cold, 10), 2), "p50": round(pct(cold, 50), 2),
                              "p90": round(pct(cold, 90), 2)} if cold else None,
-        "kv_append_us": round(append_us, 2),
+        "kv_append_us": append_us,
         "kernels_us": {"attention_avg": round(attn_avg * 1e3, 2),
                        "attention_min": round(min(attn_ms) * 1e3, 2),
                        "combine_avg": round(statistics.fmean(comb_ms) * 1e3, 2)},

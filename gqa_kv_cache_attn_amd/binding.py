@@ -28,9 +28,10 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_ALIAS, GQA_ERR_UNSUPPORTED_DEVICE = 0, 1, 2, 3
 GQA_ERR_CAPTURE, GQA_ERR_OUT_OF_MEMORY, GQA_ERR_HIP = 4, 5, 6
-GQA_F16, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
+GQA_F16, GQA_BF16, GQA_FP8_E4M3, GQA_INT8_ROWSCALE = 0, 1, 2, 3
 GQA_FLAG_FUSED_COMBINE = 1
 NUM_Q_HEADS, NUM_KV_HEADS, HEAD_DIM = 32, 8, 128
+NUM_Q_HEADS_2TO1 = 16
 
 STATUS_NAMES = {
     0: "GQA_OK", 1: "GQA_ERR_INVALID_ARG", 2: "GQA_ERR_ALIAS",
@@ -79,6 +80,11 @@ _destroy = _sig("gqa_prepared_destroy", None, [_vp])
 _ws_bytes = _sig("gqa_prepared_workspace_bytes", ctypes.c_size_t, [_vp])
 _prep_plan = _sig("gqa_prepared_plan", ctypes.c_int, [_vp, _PlanP])
 _validate = _sig("gqa_validate_args", ctypes.c_int, [_DescP, _vp, _vp, _vp, _f32, _vp, _i32])
+_gqa_decode_int8 = _sig("gqa_decode_int8", ctypes.c_int, [_DescP, _vp, _vp, _vp, _vp, _f32, _vp, _vp])
+_prepare_int8 = _sig("prepare_gqa_decode_int8", ctypes.c_int,
+                     [_DescP, _vp, _vp, _vp, _vp, _f32, _vp, _i32, ctypes.POINTER(_vp)])
+_validate_int8 = _sig("gqa_validate_args_int8", ctypes.c_int,
+                      [_DescP, _vp, _vp, _vp, _vp, _f32, _vp, _i32])
 _plan = _sig("gqa_plan_decode", ctypes.c_int, [_DescP, _i32, _PlanP])
 _last_error = _sig("gqa_last_error", ctypes.c_char_p, [])
 _append = _sig("gqa_kv_append", ctypes.c_int, [_DescP, _vp, _vp, _vp, _vp, _vp])
@@ -106,15 +112,17 @@ def _dtype_code(t: torch.Tensor, role: str) -> int:
         return GQA_BF16
     if role == "kv" and t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return GQA_FP8_E4M3
+    if role == "kv" and t.dtype == torch.int8:
+        return GQA_INT8_ROWSCALE
     raise ValueError(f"unsupported {role} dtype {t.dtype}")
 
 
 def make_desc(q: torch.Tensor, kv: torch.Tensor, k_scale: float = 1.0,
               v_scale: float = 1.0, fused_combine: bool = False) -> GqaDesc:
     if q.dim() != 3 or kv.dim() != 5:
-        raise ValueError("q must be [batch, 32, 128] and kv [batch, 2, 8, capacity, 128]")
-    if tuple(q.shape[1:]) != (NUM_Q_HEADS, HEAD_DIM):
-        raise ValueError(f"q must be [batch, 32, 128], got {tuple(q.shape)}")
+        raise ValueError("q must be [batch, Hq, 128] and kv [batch, 2, 8, capacity, 128]")
+    if q.shape[1] not in (NUM_Q_HEADS, NUM_Q_HEADS_2TO1) or q.shape[2] != HEAD_DIM:
+        raise ValueError(f"q must be [batch, 32 or 16, 128], got {tuple(q.shape)}")
     if kv.shape[1] != 2 or kv.shape[0] != q.shape[0]:
         raise ValueError(f"kv must be [batch, 2, 8, capacity, 128], got {tuple(kv.shape)}")
     return GqaDesc(batch=q.shape[0], capacity=kv.shape[3], num_q_heads=q.shape[1],
@@ -161,6 +169,35 @@ def gqa_decode(q: torch.Tensor, kv: torch.Tensor, seq_lens: torch.Tensor,
     with torch.cuda.device(q.device):
         st = _gqa_decode(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(seq_lens), q_scale,
                          _ptr(out), _stream_handle(stream, q.device))
+    _check(st)
+    return out
+
+
+def _check_scales(kv: torch.Tensor, kv_scales: torch.Tensor):
+    if kv.dtype != torch.int8:
+        raise ValueError("the _int8 entry points take an int8 kv")
+    if kv_scales.dtype != torch.bfloat16 or tuple(kv_scales.shape) != tuple(kv.shape[:4]):
+        raise ValueError(f"kv_scales must be bf16 [batch, 2, 8, capacity] = {tuple(kv.shape[:4])}, "
+                         f"got {kv_scales.dtype} {tuple(kv_scales.shape)}")
+
+
+def gqa_decode_int8(q: torch.Tensor, kv: torch.Tensor, kv_scales: torch.Tensor,
+                    seq_lens: torch.Tensor, q_scale: float = 1.0,
+                    out: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                    v_scale: float = 1.0, stream=None) -> torch.Tensor:
+    """gqa_decode over an int8 cache with bf16 row scales [batch, 2, 8, capacity]."""
+    if out is None:
+        out = torch.empty_like(q)
+    _check_devices(q, kv, kv_scales, seq_lens, out)
+    _check_scales(kv, kv_scales)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q's shape and dtype")
+    desc = make_desc(q, kv, k_scale, v_scale)
+    with torch.cuda.device(q.device):
+        st = _gqa_decode_int8(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(kv_scales),
+                              _ptr(seq_lens), q_scale, _ptr(out), _stream_handle(stream, q.device))
     _check(st)
     return out
 
@@ -224,6 +261,28 @@ def prepare_gqa_decode(q: torch.Tensor, kv: torch.Tensor, seq_lens: torch.Tensor
     return GqaPrepared(h.value, {"Q": q, "KV": kv, "sequence_lengths": seq_lens, "O": out}, desc)
 
 
+def prepare_gqa_decode_int8(q: torch.Tensor, kv: torch.Tensor, kv_scales: torch.Tensor,
+                            seq_lens: torch.Tensor, out: torch.Tensor, q_scale: float = 1.0,
+                            num_splits: Optional[int] = None, k_scale: float = 1.0,
+                            v_scale: float = 1.0, fused_combine: bool = False) -> GqaPrepared:
+    """prepare_gqa_decode over an int8 cache with bf16 row scales."""
+    _check_devices(q, kv, kv_scales, seq_lens, out)
+    _check_scales(kv, kv_scales)
+    if seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be int32")
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q's shape and dtype")
+    desc = make_desc(q, kv, k_scale, v_scale, fused_combine)
+    h = _vp()
+    with torch.cuda.device(q.device):
+        st = _prepare_int8(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(kv_scales), _ptr(seq_lens),
+                           q_scale, _ptr(out), 0 if num_splits is None else int(num_splits),
+                           ctypes.byref(h))
+    _check(st)
+    return GqaPrepared(h.value, {"Q": q, "KV": kv, "KV_scales": kv_scales,
+                                 "sequence_lengths": seq_lens, "O": out}, desc)
+
+
 def launch_gqa_decode_prepared(prepared: GqaPrepared, stream=None) -> torch.Tensor:
     """Enqueue the prepared step (no allocation, no host sync); returns O."""
     dev = prepared.out.device
@@ -271,6 +330,14 @@ def gqa_validate_args(desc: GqaDesc, q_ptr: Optional[int], kv_ptr: Optional[int]
     """Host-only validation (no device access); returns the raw status code."""
     return int(_validate(ctypes.byref(desc), q_ptr, kv_ptr, lens_ptr, q_scale, out_ptr,
                          num_splits))
+
+
+def gqa_validate_args_int8(desc: GqaDesc, q_ptr: Optional[int], kv_ptr: Optional[int],
+                           scales_ptr: Optional[int], lens_ptr: Optional[int], q_scale: float,
+                           out_ptr: Optional[int], num_splits: int = 0) -> int:
+    """Host-only validation of an int8-cache call; returns the raw status code."""
+    return int(_validate_int8(ctypes.byref(desc), q_ptr, kv_ptr, scales_ptr, lens_ptr, q_scale,
+                              out_ptr, num_splits))
 
 
 def gqa_plan(desc: GqaDesc, num_splits: int = 0) -> dict:

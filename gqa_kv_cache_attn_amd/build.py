@@ -36,7 +36,7 @@ def hipcc_path() -> str:
 
 def compile_command(out_path: str, sources=SOURCES) -> list:
     return [
-        hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        hipcc_path(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
         "-fvisibility=hidden", "-Wall", "-Wno-unused-command-line-argument",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE,

@@ -53,21 +53,27 @@ constexpr int64_t kFillWorkgroups = 768;
 constexpr int kNominalBalancedGrid = 768;
 constexpr int kMaxBalancedGrid = 4096;
 
-// Resident balanced-kernel workgroups per (device, dtype pair), queried once.
+// Resident balanced-kernel workgroups per (device, dtype pair, query heads),
+// queried once.
 std::mutex g_grid_mu;
 std::map<std::pair<int, int>, int> g_grid;
 
-int device_balanced_grid(int dev, int q_dtype, int kv_dtype) {
+int device_balanced_grid(int dev, const gqa_desc_t* d) {
   std::lock_guard<std::mutex> lk(g_grid_mu);
-  const std::pair<int, int> key{dev, q_dtype * 8 + kv_dtype};
+  const std::pair<int, int> key{dev, (d->num_q_heads * 8 + d->q_dtype) * 8 + d->kv_dtype};
   auto it = g_grid.find(key);
   if (it != g_grid.end()) return it->second;
-  const int G = gqa::balanced_grid_size(q_dtype, kv_dtype);
-  g_grid.emplace(key, G);
-  return G;
+  const int W = gqa::balanced_grid_size(d->q_dtype, d->kv_dtype, d->num_q_heads);
+  g_grid.emplace(key, W);
+  return W;
 }
 
-int elem_bytes(int dt) { return dt == GQA_FP8_E4M3 ? 1 : 2; }
+int elem_bytes(int dt) { return (dt == GQA_FP8_E4M3 || dt == GQA_INT8_ROWSCALE) ? 1 : 2; }
+
+// K+V bytes one cache slot of one KV head occupies (row scales included).
+int64_t slot_bytes(int dt) {
+  return 2 * (GQA_HEAD_DIM * (int64_t)elem_bytes(dt) + (dt == GQA_INT8_ROWSCALE ? 2 : 0));
+}
 
 bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -80,10 +86,10 @@ bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
 
 gqa_status_t check_desc(const gqa_desc_t* d) {
   if (d == nullptr) return fail(GQA_ERR_INVALID_ARG, "desc is NULL");
-  if (d->num_q_heads != GQA_NUM_Q_HEADS || d->num_kv_heads != GQA_NUM_KV_HEADS ||
-      d->head_dim != GQA_HEAD_DIM)
+  if ((d->num_q_heads != GQA_NUM_Q_HEADS && d->num_q_heads != GQA_NUM_Q_HEADS_2TO1) ||
+      d->num_kv_heads != GQA_NUM_KV_HEADS || d->head_dim != GQA_HEAD_DIM)
     return fail(GQA_ERR_INVALID_ARG,
-                "geometry is fixed at 32 query heads / 8 KV heads / head_dim 128 (got %d/%d/%d)",
+                "geometry must be 32 or 16 query heads / 8 KV heads / head_dim 128 (got %d/%d/%d)",
                 d->num_q_heads, d->num_kv_heads, d->head_dim);
   if (d->batch < 0) return fail(GQA_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", d->batch);
   if (d->capacity < 1 || d->capacity > GQA_MAX_CAPACITY)
@@ -91,23 +97,25 @@ gqa_status_t check_desc(const gqa_desc_t* d) {
                 d->capacity);
   if (d->q_dtype != GQA_F16 && d->q_dtype != GQA_BF16)
     return fail(GQA_ERR_INVALID_ARG, "q dtype must be F16 or BF16 (got %d)", d->q_dtype);
-  const bool kv_ok = d->kv_dtype == GQA_FP8_E4M3 || d->kv_dtype == d->q_dtype;
+  const bool kv_ok = d->kv_dtype == GQA_FP8_E4M3 || d->kv_dtype == GQA_INT8_ROWSCALE ||
+                     d->kv_dtype == d->q_dtype;
   if (!kv_ok)
     return fail(GQA_ERR_INVALID_ARG,
-                "unsupported (q, kv) dtype pair (%d, %d): kv must match q or be FP8_E4M3",
+                "unsupported (q, kv) dtype pair (%d, %d): kv must match q or be FP8_E4M3 or "
+                "INT8_ROWSCALE",
                 d->q_dtype, d->kv_dtype);
   if (!scale_ok(d->k_scale) || !scale_ok(d->v_scale))
     return fail(GQA_ERR_INVALID_ARG, "k_scale and v_scale must be finite and > 0");
-  if (d->kv_dtype != GQA_FP8_E4M3 && (d->k_scale != 1.0f || d->v_scale != 1.0f))
+  if (d->kv_dtype == d->q_dtype && (d->k_scale != 1.0f || d->v_scale != 1.0f))
     return fail(GQA_ERR_INVALID_ARG,
-                "k_scale/v_scale apply to an fp8 cache only; a 16-bit cache needs 1.0");
+                "k_scale/v_scale apply to an fp8 or int8 cache only; a 16-bit cache needs 1.0");
   if ((d->flags & ~GQA_FLAG_FUSED_COMBINE) != 0)
     return fail(GQA_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)d->flags);
   return GQA_OK;
 }
 
 // Workspace: part_o [R,128] f32 | part_ml [R,2] f32 | aux int32 array, where R
-// is the number of partial rows: chunked split R = B*32*S (head-major), aux =
+// is the number of partial rows: chunked split R = B*Hq*S (head-major), aux =
 // per-(request, KV head) counters [B*8] (fused merge only); balanced split
 // R = 2G*4 (two slots per workgroup, 4 query rows each), aux = slab prefix [B+1].
 struct WorkspaceLayout {
@@ -125,7 +133,7 @@ WorkspaceLayout workspace_layout(uint64_t rows, uint64_t aux_ints) {
 WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p) {
   if (p.route == 2)
     return workspace_layout(2ull * (uint64_t)p.num_workgroups * 4, (uint64_t)d->batch + 1);
-  return workspace_layout((uint64_t)d->batch * GQA_NUM_Q_HEADS * (uint64_t)p.num_splits,
+  return workspace_layout((uint64_t)d->batch * (uint64_t)d->num_q_heads * (uint64_t)p.num_splits,
                           (uint64_t)d->batch * GQA_NUM_KV_HEADS);
 }
 
@@ -161,7 +169,7 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, i
       // the grid still fills every CU once at full capacity.
       constexpr int64_t kStepGranules = 64 / GQA_CHUNK_GRANULE;
       const int64_t steps = (C + 63) / 64;
-      const int64_t step_bytes = 64 * 2 * GQA_HEAD_DIM * (int64_t)elem_bytes(d->kv_dtype);
+      const int64_t step_bytes = 64 * slot_bytes(d->kv_dtype);
       const int64_t by_bytes = std::max<int64_t>(1, kChunkBytes / step_bytes);
       const int64_t total = std::max<int64_t>(1, (int64_t)d->batch * GQA_NUM_KV_HEADS * steps);
       const int64_t by_fill = std::max<int64_t>(1, total / kFillWorkgroups);
@@ -192,24 +200,41 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, i
   return GQA_OK;
 }
 
-gqa_status_t check_args(const gqa_desc_t* d, const void* q, const void* kv, const int32_t* lens,
-                        float q_scale, const void* out) {
+// with_scales: the _int8 entry points (kv dtype INT8_ROWSCALE, scales given);
+// the plain ones reject an INT8 descriptor.
+gqa_status_t check_args(const gqa_desc_t* d, const void* q, const void* kv, const void* scales,
+                        bool with_scales, const int32_t* lens, float q_scale, const void* out) {
   gqa_status_t st = check_desc(d);
   if (st != GQA_OK) return st;
+  if (with_scales && d->kv_dtype != GQA_INT8_ROWSCALE)
+    return fail(GQA_ERR_INVALID_ARG, "the _int8 entry points need kv dtype INT8_ROWSCALE (got %d)",
+                d->kv_dtype);
+  if (!with_scales && d->kv_dtype == GQA_INT8_ROWSCALE)
+    return fail(GQA_ERR_INVALID_ARG,
+                "an INT8_ROWSCALE cache needs its row scales: use gqa_decode_int8 / "
+                "prepare_gqa_decode_int8");
   if (!scale_ok(q_scale))
     return fail(GQA_ERR_INVALID_ARG, "q_scale must be finite and > 0 (got %g)", (double)q_scale);
   if (d->batch == 0) return GQA_OK;
-  if (!q || !kv || !lens || !out) return fail(GQA_ERR_INVALID_ARG, "q, kv, seq_lens and out must be non-NULL");
-  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(lens, 4))
-    return fail(GQA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned and seq_lens 4-byte aligned");
+  if (!q || !kv || !lens || !out || (with_scales && !scales))
+    return fail(GQA_ERR_INVALID_ARG,
+                with_scales ? "q, kv, kv_scales, seq_lens and out must be non-NULL"
+                            : "q, kv, seq_lens and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16) || !aligned(lens, 4) ||
+      (with_scales && !aligned(scales, 16)))
+    return fail(GQA_ERR_INVALID_ARG,
+                "q, kv, kv_scales and out must be 16-byte aligned and seq_lens 4-byte aligned");
   const size_t B = (size_t)d->batch;
-  const size_t q_bytes = B * GQA_NUM_Q_HEADS * GQA_HEAD_DIM * elem_bytes(d->q_dtype);
+  const size_t q_bytes = B * (size_t)d->num_q_heads * GQA_HEAD_DIM * elem_bytes(d->q_dtype);
   const size_t kv_bytes =
       B * 2 * GQA_NUM_KV_HEADS * (size_t)d->capacity * GQA_HEAD_DIM * elem_bytes(d->kv_dtype);
+  const size_t sc_bytes = with_scales ? B * 2 * GQA_NUM_KV_HEADS * (size_t)d->capacity * 2 : 0;
   const size_t len_bytes = B * sizeof(int32_t);
   if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, kv, kv_bytes) ||
-      ranges_overlap(out, q_bytes, lens, len_bytes))
-    return fail(GQA_ERR_ALIAS, "out must not overlap q, kv or seq_lens");
+      ranges_overlap(out, q_bytes, lens, len_bytes) ||
+      (with_scales && ranges_overlap(out, q_bytes, scales, sc_bytes)))
+    return fail(GQA_ERR_ALIAS, with_scales ? "out must not overlap q, kv, kv_scales or seq_lens"
+                                           : "out must not overlap q, kv or seq_lens");
   return GQA_OK;
 }
 
@@ -239,11 +264,14 @@ gqa_status_t check_device(int* dev_out) {
   return GQA_OK;
 }
 
-gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, const int32_t* lens,
-                        float q_scale, void* out, const gqa_plan_t& p, void* ws) {
+gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, const void* scales,
+                        const int32_t* lens, float q_scale, void* out, const gqa_plan_t& p,
+                        void* ws) {
   gqa::StepArgs a;
   a.q = q;
   a.kv = kv;
+  a.kv_scales = scales;
+  a.num_q_heads = d->num_q_heads;
   a.seq_lens = lens;
   a.out = out;
   const WorkspaceLayout wl = plan_layout(d, p);
@@ -288,6 +316,7 @@ struct gqa_prepared {
   gqa_plan_t plan;
   const void* q;
   const void* kv;
+  const void* kv_scales;   // INT8 cache only
   const int32_t* seq_lens;
   void* out;
   float q_scale;
@@ -295,14 +324,12 @@ struct gqa_prepared {
   int device;
 };
 
-extern "C" {
+namespace {
 
-GQA_API const char* gqa_last_error(void) { return g_last_error.c_str(); }
-
-GQA_API gqa_status_t gqa_validate_args(const gqa_desc_t* desc, const void* q, const void* kv,
-                                       const int32_t* seq_lens, float q_scale, const void* out,
-                                       int32_t num_splits) {
-  gqa_status_t st = check_args(desc, q, kv, seq_lens, q_scale, out);
+gqa_status_t validate_impl(const gqa_desc_t* desc, const void* q, const void* kv,
+                           const void* scales, bool with_scales, const int32_t* seq_lens,
+                           float q_scale, const void* out, int32_t num_splits) {
+  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
   if (st != GQA_OK) return st;
   gqa_plan_t p;
   st = make_plan(desc, num_splits, &p);
@@ -310,21 +337,12 @@ GQA_API gqa_status_t gqa_validate_args(const gqa_desc_t* desc, const void* q, co
   return ok();
 }
 
-GQA_API gqa_status_t gqa_plan_decode(const gqa_desc_t* desc, int32_t num_splits, gqa_plan_t* plan) {
-  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
-  gqa_status_t st = check_desc(desc);
-  if (st != GQA_OK) return st;
-  st = make_plan(desc, num_splits, plan);
-  if (st != GQA_OK) return st;
-  return ok();
-}
-
-GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
-                                        const int32_t* seq_lens, float q_scale, void* out,
-                                        int32_t num_splits, gqa_prepared_t** handle) {
+gqa_status_t prepare_impl(const gqa_desc_t* desc, const void* q, const void* kv,
+                          const void* scales, bool with_scales, const int32_t* seq_lens,
+                          float q_scale, void* out, int32_t num_splits, gqa_prepared_t** handle) {
   if (handle == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
   *handle = nullptr;
-  gqa_status_t st = check_args(desc, q, kv, seq_lens, q_scale, out);
+  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
   if (st != GQA_OK) return st;
   gqa_plan_t p;
   st = make_plan(desc, num_splits, &p);
@@ -333,7 +351,7 @@ GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q, c
   st = check_device(&dev);
   if (st != GQA_OK) return st;
   if (p.route == 2) {   // size the balanced grid for this device
-    st = make_plan(desc, num_splits, &p, device_balanced_grid(dev, desc->q_dtype, desc->kv_dtype));
+    st = make_plan(desc, num_splits, &p, device_balanced_grid(dev, desc));
     if (st != GQA_OK) return st;
   }
   void* ws = nullptr;
@@ -360,6 +378,7 @@ GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q, c
   h->plan = p;
   h->q = q;
   h->kv = kv;
+  h->kv_scales = scales;
   h->seq_lens = seq_lens;
   h->out = out;
   h->q_scale = q_scale;
@@ -369,54 +388,10 @@ GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q, c
   return ok();
 }
 
-GQA_API gqa_status_t launch_gqa_decode_prepared_timed(gqa_prepared_t* h, hipStream_t stream,
-                                                      hipEvent_t ev_start, hipEvent_t ev_mid,
-                                                      hipEvent_t ev_end) {
-  if (h == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
-  if (h->desc.batch == 0) return ok();
-  int cur = -1;
-  hipError_t e = hipGetDevice(&cur);
-  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-  if (cur != h->device && (e = hipSetDevice(h->device)) != hipSuccess)
-    return fail(GQA_ERR_HIP, "hipSetDevice(%d) failed: %s", h->device, hipGetErrorString(e));
-  gqa_status_t st = GQA_OK;
-  if (ev_start != nullptr && (e = hipEventRecord(ev_start, stream)) != hipSuccess)
-    st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-  if (st == GQA_OK) {
-    const gqa::StepArgs a =
-        step_args(&h->desc, h->q, h->kv, h->seq_lens, h->q_scale, h->out, h->plan, h->workspace);
-    st = enqueue(a, &h->desc, stream, ev_mid);
-  }
-  if (st == GQA_OK && ev_end != nullptr && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
-    st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
-  if (cur != h->device) (void)hipSetDevice(cur);
-  return st;
-}
-
-GQA_API gqa_status_t launch_gqa_decode_prepared(gqa_prepared_t* h, hipStream_t stream) {
-  return launch_gqa_decode_prepared_timed(h, stream, nullptr, nullptr, nullptr);
-}
-
-GQA_API void gqa_prepared_destroy(gqa_prepared_t* h) {
-  if (h == nullptr) return;
-  if (h->workspace) (void)hipFree(h->workspace);
-  delete h;
-}
-
-GQA_API size_t gqa_prepared_workspace_bytes(const gqa_prepared_t* h) {
-  return (h && h->workspace) ? (size_t)h->plan.workspace_bytes : 0;
-}
-
-GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* h, gqa_plan_t* plan) {
-  if (h == nullptr || plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
-  *plan = h->plan;
-  return ok();
-}
-
-GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
-                                const int32_t* seq_lens, float q_scale, void* out,
-                                hipStream_t stream) {
-  gqa_status_t st = check_args(desc, q, kv, seq_lens, q_scale, out);
+gqa_status_t decode_impl(const gqa_desc_t* desc, const void* q, const void* kv,
+                         const void* scales, bool with_scales, const int32_t* seq_lens,
+                         float q_scale, void* out, hipStream_t stream) {
+  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
   if (st != GQA_OK) return st;
   gqa_plan_t p;
   st = make_plan(desc, 0, &p);
@@ -426,7 +401,7 @@ GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const voi
   st = check_device(&dev);
   if (st != GQA_OK) return st;
   if (p.route == 2) {
-    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc->q_dtype, desc->kv_dtype));
+    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc));
     if (st != GQA_OK) return st;
   }
 
@@ -472,13 +447,111 @@ GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const voi
     }
     ws = ce.ptr;
   }
-  return enqueue(step_args(desc, q, kv, seq_lens, q_scale, out, p, ws), desc, stream);
+  return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws), desc, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+GQA_API const char* gqa_last_error(void) { return g_last_error.c_str(); }
+
+GQA_API gqa_status_t gqa_validate_args(const gqa_desc_t* desc, const void* q, const void* kv,
+                                       const int32_t* seq_lens, float q_scale, const void* out,
+                                       int32_t num_splits) {
+  return validate_impl(desc, q, kv, nullptr, false, seq_lens, q_scale, out, num_splits);
+}
+
+GQA_API gqa_status_t gqa_validate_args_int8(const gqa_desc_t* desc, const void* q, const void* kv,
+                                            const void* kv_scales, const int32_t* seq_lens,
+                                            float q_scale, const void* out, int32_t num_splits) {
+  return validate_impl(desc, q, kv, kv_scales, true, seq_lens, q_scale, out, num_splits);
+}
+
+GQA_API gqa_status_t gqa_plan_decode(const gqa_desc_t* desc, int32_t num_splits, gqa_plan_t* plan) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  gqa_status_t st = check_desc(desc);
+  if (st != GQA_OK) return st;
+  st = make_plan(desc, num_splits, plan);
+  if (st != GQA_OK) return st;
+  return ok();
+}
+
+GQA_API gqa_status_t prepare_gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
+                                        const int32_t* seq_lens, float q_scale, void* out,
+                                        int32_t num_splits, gqa_prepared_t** handle) {
+  return prepare_impl(desc, q, kv, nullptr, false, seq_lens, q_scale, out, num_splits, handle);
+}
+
+GQA_API gqa_status_t prepare_gqa_decode_int8(const gqa_desc_t* desc, const void* q,
+                                             const void* kv, const void* kv_scales,
+                                             const int32_t* seq_lens, float q_scale, void* out,
+                                             int32_t num_splits, gqa_prepared_t** handle) {
+  return prepare_impl(desc, q, kv, kv_scales, true, seq_lens, q_scale, out, num_splits, handle);
+}
+
+GQA_API gqa_status_t launch_gqa_decode_prepared_timed(gqa_prepared_t* h, hipStream_t stream,
+                                                      hipEvent_t ev_start, hipEvent_t ev_mid,
+                                                      hipEvent_t ev_end) {
+  if (h == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  if (h->desc.batch == 0) return ok();
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (cur != h->device && (e = hipSetDevice(h->device)) != hipSuccess)
+    return fail(GQA_ERR_HIP, "hipSetDevice(%d) failed: %s", h->device, hipGetErrorString(e));
+  gqa_status_t st = GQA_OK;
+  if (ev_start != nullptr && (e = hipEventRecord(ev_start, stream)) != hipSuccess)
+    st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  if (st == GQA_OK) {
+    const gqa::StepArgs a = step_args(&h->desc, h->q, h->kv, h->kv_scales, h->seq_lens, h->q_scale,
+                                      h->out, h->plan, h->workspace);
+    st = enqueue(a, &h->desc, stream, ev_mid);
+  }
+  if (st == GQA_OK && ev_end != nullptr && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
+    st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
+  if (cur != h->device) (void)hipSetDevice(cur);
+  return st;
+}
+
+GQA_API gqa_status_t launch_gqa_decode_prepared(gqa_prepared_t* h, hipStream_t stream) {
+  return launch_gqa_decode_prepared_timed(h, stream, nullptr, nullptr, nullptr);
+}
+
+GQA_API void gqa_prepared_destroy(gqa_prepared_t* h) {
+  if (h == nullptr) return;
+  if (h->workspace) (void)hipFree(h->workspace);
+  delete h;
+}
+
+GQA_API size_t gqa_prepared_workspace_bytes(const gqa_prepared_t* h) {
+  return (h && h->workspace) ? (size_t)h->plan.workspace_bytes : 0;
+}
+
+GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* h, gqa_plan_t* plan) {
+  if (h == nullptr || plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "NULL argument");
+  *plan = h->plan;
+  return ok();
+}
+
+GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
+                                const int32_t* seq_lens, float q_scale, void* out,
+                                hipStream_t stream) {
+  return decode_impl(desc, q, kv, nullptr, false, seq_lens, q_scale, out, stream);
+}
+
+GQA_API gqa_status_t gqa_decode_int8(const gqa_desc_t* desc, const void* q, const void* kv,
+                                     const void* kv_scales, const int32_t* seq_lens,
+                                     float q_scale, void* out, hipStream_t stream) {
+  return decode_impl(desc, q, kv, kv_scales, true, seq_lens, q_scale, out, stream);
 }
 
 GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,
                                    const int32_t* positions, void* kv, hipStream_t stream) {
   gqa_status_t st = check_desc(desc);
   if (st != GQA_OK) return st;
+  if (desc->kv_dtype == GQA_INT8_ROWSCALE)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_kv_append does not write an INT8_ROWSCALE cache");
   if (desc->batch == 0) return ok();
   if (!k_new || !v_new || !positions || !kv)
     return fail(GQA_ERR_INVALID_ARG, "k_new, v_new, positions and kv must be non-NULL");

@@ -8,22 +8,24 @@
 
 namespace gqa {
 
-enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2 };
+enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2, kI8 = 3 };
 
 // The balanced split keeps the per-request slab prefix in LDS.
 constexpr int kMaxBalancedBatch = 4096;
 
 // Arguments of one decode step, passed to the kernels by value.
 struct StepArgs {
-  const void* q;             // [batch, 32, 128] q dtype
+  const void* q;             // [batch, Hq, 128] q dtype
   const void* kv;            // [batch, 2, 8, capacity, 128] kv dtype
+  const void* kv_scales;     // [batch, 2, 8, capacity] bf16 row scales (INT8 cache), else null
   const int32_t* seq_lens;   // [batch]
-  void* out;                 // [batch, 32, 128] q dtype
-  float* part_o;             // [batch, 32, num_splits, 128] unnormalised chunk outputs
-  float* part_ml;            // [batch, 32, num_splits, 2] chunk (max, sum), log2 domain
+  void* out;                 // [batch, Hq, 128] q dtype
+  float* part_o;             // [batch, Hq, num_splits, 128] unnormalised chunk outputs
+  float* part_ml;            // [batch, Hq, num_splits, 2] chunk (max, sum), log2 domain
   uint32_t* counters;        // [batch, 8] finished chunks per (request, KV head); 0 between launches
   int32_t* slab_prefix;      // [batch + 1] balanced split: 8 * slabs before each request
   int32_t batch;
+  int32_t num_q_heads;       // Hq: 32 (4 per KV head) or 16 (2 per KV head)
   int32_t capacity;
   int32_t num_splits;        // chunks per (request, KV head); 1 = normalise in place
   int32_t chunk_tokens;      // multiple of 16
@@ -49,7 +51,7 @@ hipError_t enqueue_kv_append(const AppendArgs& args, int src_dtype, int kv_dtype
 
 // Workgroups of the balanced split that the current device keeps resident at
 // once (CUs x resident workgroups per CU); 0 if the query fails.
-int balanced_grid_size(int q_dtype, int kv_dtype);
+int balanced_grid_size(int q_dtype, int kv_dtype, int num_q_heads);
 
 // Enqueue the attention kernel (and, for num_splits > 1, the combine kernel).
 // Returns the first launch error. Arguments are assumed validated. When given,

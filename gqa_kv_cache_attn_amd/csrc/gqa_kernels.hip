@@ -1,11 +1,15 @@
 // gfx950 kernels for single-token grouped-query decode attention.
 //
 // The step (FlashInfer sm110_gqa_decode article, "input contract" and
-// "convenience API"): 4 query rows of one request share one KV head; scores
-// are taken in the log2 domain, exp2(scale_log2 * s) with
+// "convenience API"): G = 4 query rows of one request share one KV head (or
+// G = 2 in the 16-query-head geometry of the Orin Qwen3-VL doc's INT8-KV
+// decode); scores are taken in the log2 domain, exp2(scale_log2 * s) with
 // scale_log2 = q_scale / sqrt(128) / ln 2 (times k_scale for an fp8 cache,
 // Thor FP8 KV notes, patch 2), and the output is the softmax-weighted sum of
-// the V rows of the valid prefix, times v_scale.
+// the V rows of the valid prefix, times v_scale. An INT8 cache carries one
+// bf16 scale per (position, KV head) row (Orin Qwen3-VL doc, "INT8 KV
+// cache"): the K row scale multiplies that token's score, the V row scale
+// its weight in the PV product.
 //
 // Work split. A workgroup (4 waves of 64 lanes) owns one chunk of one
 // (request, KV head): `chunk_tokens` consecutive cache slots. Within the
@@ -40,15 +44,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gqa_kernels.h"
 
 namespace gqa {
 namespace {
 
 constexpr int kHeadDim = 128;
-constexpr int kQHeads = 32;
 constexpr int kKvHeads = 8;
-constexpr int kGroup = 4;
+constexpr int kGroup = 4;               // MFMA rows carried per KV head (G <= 4 are real)
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 16;               // tokens per wave step
@@ -106,6 +111,12 @@ struct Elem<kBF16> {
   static __device__ __forceinline__ u32 from_fp8(u32 x) {
     return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, kHiWord));
   }
+  // Two signed int8 values (bytes 2*sel, 2*sel+1 of x) -> two bf16 (exact).
+  template <bool kHiWord>
+  static __device__ __forceinline__ u32 from_i8(u32 x) {
+    return pack((float)(signed char)(x >> (kHiWord ? 16 : 0)),
+                (float)(signed char)(x >> (kHiWord ? 24 : 8)));
+  }
   static __device__ __forceinline__ void store2(void* p, float a, float b) {
     *reinterpret_cast<u32*>(p) = pack(a, b);
   }
@@ -135,6 +146,11 @@ struct Elem<kF16> {
   static __device__ __forceinline__ u32 from_fp8(u32 x) {
     return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, kHiWord));
   }
+  template <bool kHiWord>
+  static __device__ __forceinline__ u32 from_i8(u32 x) {
+    return pack((float)(signed char)(x >> (kHiWord ? 16 : 0)),
+                (float)(signed char)(x >> (kHiWord ? 24 : 8)));
+  }
   static __device__ __forceinline__ void store2(void* p, float a, float b) {
     *reinterpret_cast<u32*>(p) = pack(a, b);
   }
@@ -148,11 +164,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // Dim-block (8 dims) that lane group `grp` feeds to QK instruction `i`.
 // 16-bit cache: block 4i+grp.
-// fp8 cache:    the lane's 16-byte chunk 4p+grp of a K row holds blocks
+// byte cache:   the lane's 16-byte chunk 4p+grp of a K row holds blocks
 //               8p + 2grp + {0,1}, fed to instructions 2p and 2p+1.
+// One-byte caches (fp8 e4m3, int8 with row scales) share the row layout and
+// the load/stage/widen path; only the widening and the row scales differ.
+template <int KVT>
+constexpr bool kByteKv = KVT == kFP8 || KVT == kI8;
+
 template <int KVT>
 __device__ __forceinline__ int qk_dim_block(int i, int grp) {
-  if constexpr (KVT == kFP8) {
+  if constexpr (kByteKv<KVT>) {
     return 8 * (i >> 1) + 2 * grp + (i & 1);
   } else {
     return 4 * i + grp;
@@ -177,12 +198,41 @@ struct Tile<kFP8> {
   u32x4 k[2];  // K: token 8u + lane/8, 16-byte chunk lane%8
   u32x2 v[4];  // V: token 4grp+e, dims [8 n16, 8 n16 + 8)
 };
+template <>
+struct Tile<kI8> : Tile<kFP8> {
+  u32x2 ks;    // bf16 K row scales of tokens 4grp .. 4grp+3
+  u32x2 vs;    // bf16 V row scales of the same tokens
+};
+
+// Buffer resources of the (request, KV head) planes a workgroup reads; each
+// ends at the range's last slot c1, so loads past it read 0 and cost nothing.
+struct Planes {
+  __amdgpu_buffer_rsrc_t k, v;    // K and V rows
+  __amdgpu_buffer_rsrc_t ks, vs;  // bf16 row scales (INT8 cache only)
+  int c1;                         // slots in range
+  bool quads;                     // scale planes 8-byte aligned (capacity % 4 == 0)
+};
+
+// Four consecutive bf16 row scales from slot `tok` (a multiple of 4) on;
+// slots at or past c1 read 0. A quad that straddles c1, or any quad of a
+// plane that is not 8-byte aligned, is read one scale at a time, so no load
+// reaches past the range's end whatever the hardware's range-check
+// granularity, and none is misaligned.
+__device__ __forceinline__ u32x2 load_scale_quad(__amdgpu_buffer_rsrc_t r, int tok, int c1,
+                                                 bool quads) {
+  if (quads && (tok + 4 <= c1 || tok >= c1))
+    return __builtin_amdgcn_raw_buffer_load_b64(r, tok * 2, 0, 0);
+  u32 h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = __builtin_amdgcn_raw_buffer_load_b16(r, (tok + i) * 2, 0, 0);
+  return (u32x2){h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
 
 template <int KVT>
-__device__ __forceinline__ void load_tile(Tile<KVT>& t, __amdgpu_buffer_rsrc_t rk,
-                                          __amdgpu_buffer_rsrc_t rv, int j0, int lane) {
+__device__ __forceinline__ void load_tile(Tile<KVT>& t, const Planes& pl, int j0, int lane) {
   const int n16 = lane & 15, grp = lane >> 4;
-  if constexpr (KVT == kFP8) {
+  const __amdgpu_buffer_rsrc_t rk = pl.k, rv = pl.v;
+  if constexpr (kByteKv<KVT>) {
     const int ko = (j0 + (lane >> 3)) * kHeadDim + 16 * (lane & 7);
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -191,6 +241,10 @@ __device__ __forceinline__ void load_tile(Tile<KVT>& t, __amdgpu_buffer_rsrc_t r
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       t.v[e] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + e * kHeadDim, 0, kLoadAux);
+    if constexpr (KVT == kI8) {
+      t.ks = load_scale_quad(pl.ks, j0 + 4 * grp, pl.c1, pl.quads);
+      t.vs = load_scale_quad(pl.vs, j0 + 4 * grp, pl.c1, pl.quads);
+    }
   } else {
     const int ko = (j0 + 4 * grp) * (2 * kHeadDim) + 16 * n16;
 #pragma unroll
@@ -218,14 +272,34 @@ struct Softmax {
   f32x4 o[8];   // O[row 4grp+r][dim 8 n16 + c] in o[c][r] (rows 0..3 live in grp 0)
 };
 
+// Two one-byte cache values (bytes 2*sel, 2*sel+1 of x) -> two MFMA operands
+// of type T.
+template <int T, int KVT, bool kHiWord>
+__device__ __forceinline__ u32 widen(u32 x) {
+  if constexpr (KVT == kFP8) {
+    return Elem<T>::template from_fp8<kHiWord>(x);
+  } else {
+    return Elem<T>::template from_i8<kHiWord>(x);
+  }
+}
+
+// Operand type of the PV product. An INT8 cache multiplies each weight by its
+// token's V row scale, whose range is not f16's, so its weights (and V) go in
+// as bf16 hi + lo pairs whatever the query dtype; otherwise the query dtype.
 template <int QT, int KVT>
+constexpr int kPvType = KVT == kI8 ? (int)kBF16 : QT;
+
+template <int QT, int KVT, int G>
 __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, const u32x4 (&qf)[4],
                                              u32x4* sk, int j0, int c1, int lane, float scale_log2) {
   using E = Elem<QT>;
+  constexpr int PT = kPvType<QT, KVT>;
+  using P = Elem<PT>;
+  using B16 = Elem<kBF16>;   // row scales are bf16 whatever the query dtype
   const int n16 = lane & 15, grp = lane >> 4;
   // ---- scores^T[token 4grp + r][row n16] ------------------------------------
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (KVT == kFP8) {
+  if constexpr (kByteKv<KVT>) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int tok = 8 * u + (lane >> 3);
@@ -237,8 +311,8 @@ __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, co
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const u32 w0 = k16[2 * h], w1 = k16[2 * h + 1];
-        u32x4 kk = {E::template from_fp8<false>(w0), E::template from_fp8<true>(w0),
-                    E::template from_fp8<false>(w1), E::template from_fp8<true>(w1)};
+        u32x4 kk = {widen<QT, KVT, false>(w0), widen<QT, KVT, true>(w0),
+                    widen<QT, KVT, false>(w1), widen<QT, KVT, true>(w1)};
         s = E::qk(kk, qf[2 * p + h], s);
       }
     }
@@ -255,6 +329,12 @@ __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, co
   // ---- online softmax, log2 domain -----------------------------------------
   float x[4];
   const int tok0 = j0 + 4 * grp;
+  if constexpr (KVT == kI8) {   // K row scale of each token multiplies its score
+    s[0] *= B16::lo(t.ks[0]);
+    s[1] *= B16::hi(t.ks[0]);
+    s[2] *= B16::lo(t.ks[1]);
+    s[3] *= B16::hi(t.ks[1]);
+  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) x[r] = (tok0 + r < c1) ? s[r] * scale_log2 : -INFINITY;
   float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
@@ -265,34 +345,41 @@ __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, co
   float p[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[r] - m_new);
-  const u32 p01 = E::pack(p[0], p[1]);
-  const u32 p23 = E::pack(p[2], p[3]);
+  // Weights the PV product sees: with an INT8 cache, each token's V row scale
+  // multiplies its weight (l still sums the plain weights).
+  float pw[4] = {p[0], p[1], p[2], p[3]};
+  if constexpr (KVT == kI8) {
+    pw[0] *= B16::lo(t.vs[0]);
+    pw[1] *= B16::hi(t.vs[0]);
+    pw[2] *= B16::lo(t.vs[1]);
+    pw[3] *= B16::hi(t.vs[1]);
+  }
+  const u32 p01 = P::pack(pw[0], pw[1]);
+  const u32 p23 = P::pack(pw[2], pw[3]);
   // bf16 keeps 8 significant bits of a weight; the PV product then takes the
   // weights as hi + lo bf16 pairs (16 bits), so only fp32 rounding is left and
   // l sums the fp32 weights. f16 weights (11 bits) go in one piece and l sums
   // the rounded weights the product sees.
   u32 q01 = 0u, q23 = 0u;
-  if constexpr (QT == kBF16) {
-    q01 = E::pack(p[0] - E::lo(p01), p[1] - E::hi(p01));
-    q23 = E::pack(p[2] - E::lo(p23), p[3] - E::hi(p23));
+  if constexpr (PT == kBF16) {
+    q01 = P::pack(pw[0] - P::lo(p01), pw[1] - P::hi(p01));
+    q23 = P::pack(pw[2] - P::lo(p23), pw[3] - P::hi(p23));
     st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
   } else {
-    st.l = st.l * alpha + ((E::lo(p01) + E::hi(p01)) + (E::lo(p23) + E::hi(p23)));
+    st.l = st.l * alpha + ((P::lo(p01) + P::hi(p01)) + (P::lo(p23) + P::hi(p23)));
   }
   st.m = m_new;
 
-  // Rows 0..3 of O live in lanes 0..15; they need alpha of rows 0..3.
-  const float al0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 0));
-  const float al1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 1));
-  const float al2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 2));
-  const float al3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), 3));
-  if (al0 != 1.f || al1 != 1.f || al2 != 1.f || al3 != 1.f) {
+  // Rows 0..G-1 of O live in lanes 0..15; they need alpha of rows 0..G-1.
+  float al[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    al[r] = r < G ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r)) : 1.f;
+  if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      st.o[c][0] *= al0;
-      st.o[c][1] *= al1;
-      st.o[c][2] *= al2;
-      st.o[c][3] *= al3;
+#pragma unroll
+      for (int r = 0; r < G; ++r) st.o[c][r] *= al[r];
     }
   }
 
@@ -300,11 +387,11 @@ __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, co
   const u32x2 pa = {p01, p23};
   const u32x2 pl = {q01, q23};
   auto pv = [&](f32x4 acc, u32x2 bv) {
-    acc = E::pv(pa, bv, acc);
-    if constexpr (QT == kBF16) acc = E::pv(pl, bv, acc);
+    acc = P::pv(pa, bv, acc);
+    if constexpr (PT == kBF16) acc = P::pv(pl, bv, acc);
     return acc;
   };
-  if constexpr (KVT == kFP8) {
+  if constexpr (kByteKv<KVT>) {
     // For dim 8 n16 + c the B operand is {V[tok0+0..3][c]}: interleave the
     // bytes of two tokens, then widen byte pairs.
 #pragma unroll
@@ -316,10 +403,10 @@ __device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, co
         lo_a[q] = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
         lo_b[q] = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
       }
-      const u32x2 b0 = {E::template from_fp8<false>(lo_a[0]), E::template from_fp8<false>(lo_a[1])};
-      const u32x2 b1 = {E::template from_fp8<true>(lo_a[0]), E::template from_fp8<true>(lo_a[1])};
-      const u32x2 b2 = {E::template from_fp8<false>(lo_b[0]), E::template from_fp8<false>(lo_b[1])};
-      const u32x2 b3 = {E::template from_fp8<true>(lo_b[0]), E::template from_fp8<true>(lo_b[1])};
+      const u32x2 b0 = {widen<PT, KVT, false>(lo_a[0]), widen<PT, KVT, false>(lo_a[1])};
+      const u32x2 b1 = {widen<PT, KVT, true>(lo_a[0]), widen<PT, KVT, true>(lo_a[1])};
+      const u32x2 b2 = {widen<PT, KVT, false>(lo_b[0]), widen<PT, KVT, false>(lo_b[1])};
+      const u32x2 b3 = {widen<PT, KVT, true>(lo_b[0]), widen<PT, KVT, true>(lo_b[1])};
       st.o[4 * w + 0] = pv(st.o[4 * w + 0], b0);
       st.o[4 * w + 1] = pv(st.o[4 * w + 1], b1);
       st.o[4 * w + 2] = pv(st.o[4 * w + 2], b2);
@@ -407,17 +494,18 @@ __device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, 
   E::store2(outp, o0 * inv, o1 * inv);
 }
 
-// Merge of the chunked split for the 4 query heads of (request b, KV head g):
-// wave r takes head 4g + r. Only the chunks that start below the current
+// Merge of the chunked split for the G query heads of (request b, KV head g):
+// wave r < G takes head G g + r. Only the chunks that start below the current
 // length are read, so partials left by an earlier launch with longer lengths
 // never enter the result.
-template <int QT>
+template <int QT, int G>
 __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int g, int L) {
   using E = Elem<QT>;
   const int lane = threadIdx.x & 63;
   const int r = threadIdx.x >> 6;
+  if (r >= G) return;
   const int S = a.num_splits;
-  const size_t head = (size_t)b * kQHeads + kGroup * g + r;
+  const size_t head = ((size_t)b * kKvHeads + g) * G + r;
   char* outp = static_cast<char*>(a.out) + (head * kHeadDim + 2 * lane) * 2;
   const int n = (L + a.chunk_tokens - 1) / a.chunk_tokens;
   if (n == 0) {
@@ -427,7 +515,8 @@ __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int
   merge_rows<QT>(a, n, [&](int k) -> size_t { return head * (size_t)S + k; }, outp);
 }
 
-// LDS of one workgroup: the 4 waves' K staging slices and the merge buffers.
+// LDS of one workgroup: the 4 waves' K staging slices and the merge buffers
+// (for the 4 MFMA rows; rows >= G carry zero queries and are never stored).
 struct WorkgroupLds {
   u32x4 k[kWaves][kKStageSlots];
   float o[kWaves][kGroup][kHeadDim];
@@ -435,16 +524,17 @@ struct WorkgroupLds {
   float l[kWaves][kGroup];
 };
 
-// One workgroup attends the 4 query rows of (request b, KV head g) over the
+// One workgroup attends the G query rows of (request b, KV head g) over the
 // cache slots [c0, c1) (c0 < c1 <= length). On return thread t holds, for
-// row t / 64 and dims 2 (t % 64) + {0, 1}: the chunk's log2-domain max M, its
-// sum of weights l and its unnormalised output (o0, o1). Ends with a barrier,
-// so the caller may call it again for another range.
-template <int QT, int KVT>
+// row t / 64 (meaningful for rows < G) and dims 2 (t % 64) + {0, 1}: the
+// chunk's log2-domain max M, its sum of weights l and its unnormalised output
+// (o0, o1). Ends with a barrier, so the caller may call it again for another
+// range.
+template <int QT, int KVT, int G>
 __device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, int c0, int c1,
                                              WorkgroupLds& lds, float& M, float& lsum, float& o0,
                                              float& o1) {
-  constexpr int kRowBytes = kHeadDim * ((KVT == kFP8) ? 1 : 2);
+  constexpr int kRowBytes = kHeadDim * (kByteKv<KVT> ? 1 : 2);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -455,19 +545,28 @@ __device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, in
   const size_t plane = (size_t)a.capacity * kRowBytes;
   const char* kplane = kvb + ((size_t)(b * 2 + 0) * kKvHeads + g) * plane;
   const char* vplane = kvb + ((size_t)(b * 2 + 1) * kKvHeads + g) * plane;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kplane, (u32)c1 * kRowBytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vplane, (u32)c1 * kRowBytes);
+  Planes pl;
+  pl.k = make_rsrc(kplane, (u32)c1 * kRowBytes);
+  pl.v = make_rsrc(vplane, (u32)c1 * kRowBytes);
+  pl.c1 = c1;
+  pl.quads = (a.capacity & 3) == 0;
+  if constexpr (KVT == kI8) {
+    const char* sb = static_cast<const char*>(a.kv_scales);
+    const size_t splane = (size_t)a.capacity * 2;
+    pl.ks = make_rsrc(sb + ((size_t)(b * 2 + 0) * kKvHeads + g) * splane, (u32)c1 * 2);
+    pl.vs = make_rsrc(sb + ((size_t)(b * 2 + 1) * kKvHeads + g) * splane, (u32)c1 * 2);
+  }
 
-  // Query fragment: B operand of the QK product, row n16 (< 4), dim block per
-  // instruction as the K loads deliver it. Rows 4..15 are zero.
+  // Query fragment: B operand of the QK product, row n16 (< G), dim block per
+  // instruction as the K loads deliver it. Rows G..15 are zero.
   u32x4 qf[4];
   {
     const char* qrow = static_cast<const char*>(a.q) +
-                       ((size_t)b * kQHeads + kGroup * g + (n16 & 3)) * (kHeadDim * 2);
+                       (((size_t)b * kKvHeads + g) * G + (n16 & (G - 1))) * (kHeadDim * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 16 * qk_dim_block<KVT>(i, grp));
-      qf[i] = (n16 < kGroup) ? v : (u32x4){0u, 0u, 0u, 0u};
+      qf[i] = (n16 < G) ? v : (u32x4){0u, 0u, 0u, 0u};
     }
   }
 
@@ -481,14 +580,14 @@ __device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, in
   if (j0 < c1) {
     u32x4* sk = lds.k[wave];
     Tile<KVT> ta, tb;
-    load_tile<KVT>(ta, rk, rv, j0, lane);
+    load_tile<KVT>(ta, pl, j0, lane);
     for (;;) {
-      load_tile<KVT>(tb, rk, rv, j0 + kStep, lane);   // past c1: reads 0, no traffic
-      process_tile<QT, KVT>(st, ta, qf, sk, j0, c1, lane, a.scale_log2);
+      load_tile<KVT>(tb, pl, j0 + kStep, lane);   // past c1: reads 0, no traffic
+      process_tile<QT, KVT, G>(st, ta, qf, sk, j0, c1, lane, a.scale_log2);
       j0 += kStep;
       if (j0 >= c1) break;
-      load_tile<KVT>(ta, rk, rv, j0 + kStep, lane);
-      process_tile<QT, KVT>(st, tb, qf, sk, j0, c1, lane, a.scale_log2);
+      load_tile<KVT>(ta, pl, j0 + kStep, lane);
+      process_tile<QT, KVT, G>(st, tb, qf, sk, j0, c1, lane, a.scale_log2);
       j0 += kStep;
       if (j0 >= c1) break;
     }
@@ -531,7 +630,7 @@ __device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, in
 
 // Chunked split: workgroup = one chunk of `chunk_tokens` slots of one
 // (request, KV head); grid B * 8 * num_splits.
-template <int QT, int KVT, int kMode>
+template <int QT, int KVT, int G, int kMode>
 __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attention_kernel(StepArgs a) {
   using E = Elem<QT>;
   __shared__ WorkgroupLds lds;
@@ -546,29 +645,33 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
   const int L = min(max(a.seq_lens[b], 0), a.capacity);
   const int c0 = split * a.chunk_tokens;
 
-  // Epilogue coordinates: 256 threads cover 4 rows x 64 dim pairs.
+  // Epilogue coordinates: 256 threads cover 4 rows x 64 dim pairs; rows < G
+  // are query heads G g + er.
   const int er = tid >> 6;
   const int ed = (tid & 63) * 2;
-  const size_t head = (size_t)b * kQHeads + kGroup * g + er;
+  const size_t head = ((size_t)b * kKvHeads + g) * G + er;
 
   if (c0 >= L) {
     // Chunks past the length take no part. An empty request (L = 0) has no
     // chunk at all: unless a combine kernel follows, chunk 0 writes its zeros.
-    if (kMode != kModeSplit && split == 0)
+    if (kMode != kModeSplit && split == 0 && er < G)
       E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, 0.f, 0.f);
     return;
   }
   const int c1 = min(c0 + a.chunk_tokens, L);
   float M, lsum, o0, o1;
-  attend_range<QT, KVT>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
+  attend_range<QT, KVT, G>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
 
   if constexpr (kMode == kModeDirect) {
     const float inv = a.v_scale / lsum;
-    E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
+    if (er < G)
+      E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
   } else {
     const size_t slot = head * (size_t)S + split;
-    *reinterpret_cast<float2*>(a.part_o + slot * kHeadDim + ed) = make_float2(o0, o1);
-    if ((tid & 63) == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(M, lsum);
+    if (er < G) {
+      *reinterpret_cast<float2*>(a.part_o + slot * kHeadDim + ed) = make_float2(o0, o1);
+      if ((tid & 63) == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(M, lsum);
+    }
     if constexpr (kMode == kModeSplitFused) {
       // Publish this chunk, count it, and let the head's last chunk combine.
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -583,26 +686,26 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
       __syncthreads();
       if (!s_last) return;
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      combine_head_group<QT>(a, b, g, L);
+      combine_head_group<QT, G>(a, b, g, L);
     }
   }
 }
 
 // Separate log-sum-exp combine for the chunked split: one workgroup per
 // (request, KV head).
-template <int QT>
+template <int QT, int G>
 __global__ __launch_bounds__(kThreads) void gqa_combine_kernel(StepArgs a) {
   const int bg = blockIdx.x;
   const int b = bg / kKvHeads;
   const int L = min(max(a.seq_lens[b], 0), a.capacity);
-  combine_head_group<QT>(a, b, bg % kKvHeads, L);
+  combine_head_group<QT, G>(a, b, bg % kKvHeads, L);
 }
 
 // ---------------------------------------------------------------------------
 // Balanced split. The work of a step is 8 * sum_b ceil(L_b / 64) slabs of 64
-// slots, ordered request-major then KV head. A persistent grid of G
+// slots, ordered request-major then KV head. A persistent grid of W
 // workgroups (as many as the device keeps resident) gives workgroup w the
-// slab range [w N / G, (w+1) N / G), so every workgroup streams the same
+// slab range [w N / W, (w+1) N / W), so every workgroup streams the same
 // number of bytes whatever the length mix. A range crosses (request, KV head)
 // boundaries: heads it covers whole are normalised and written directly; its
 // first and last piece, when they are only part of a head, become partials
@@ -641,7 +744,9 @@ __device__ __forceinline__ void build_slab_prefix(const StepArgs& a, int* pref, 
   __syncthreads();
 }
 
-template <int QT, int KVT>
+// Partial rows of the balanced split: slot k holds kGroup rows (rows >= G
+// unused), so the slot stride does not depend on the geometry.
+template <int QT, int KVT, int G>
 __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa_balanced_attention_kernel(
     StepArgs a) {
   using E = Elem<QT>;
@@ -653,7 +758,7 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
   const int B = a.batch;
   build_slab_prefix(a, s_pref, s_wave_tot);
   const int64_t N = s_pref[B];
-  const int G = (int)gridDim.x;
+  const int W = (int)gridDim.x;
   const int w = (int)blockIdx.x;
   if (w == 0)   // the combine kernel reads the same prefix
     for (int i = tid; i <= B; i += kThreads) a.slab_prefix[i] = s_pref[i];
@@ -661,8 +766,8 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
   const int er = tid >> 6;
   const int ed = (tid & 63) * 2;
   // Slab counts fit in int32 (checked when the plan is made).
-  const int s0 = (int)((int64_t)w * N / G);
-  const int s1 = (int)((int64_t)(w + 1) * N / G);
+  const int s0 = (int)((int64_t)w * N / W);
+  const int s1 = (int)((int64_t)(w + 1) * N / W);
   if (s0 == s1) {
     // Fewer slabs than workgroups: mark slot 2w empty for the combine, which
     // may look at it when this workgroup falls inside a head's range of workgroups.
@@ -689,11 +794,12 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
     const int c0 = (s - seg_start) * kSlab;
     const int c1 = min((pe - seg_start) * kSlab, L);
     float M, lsum, o0, o1;
-    attend_range<QT, KVT>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
-    const size_t head = (size_t)b * kQHeads + kGroup * g + er;
+    attend_range<QT, KVT, G>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
+    const size_t head = ((size_t)b * kKvHeads + g) * G + er;
     if (s == seg_start && pe == seg_end) {
       const float inv = a.v_scale / lsum;
-      E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
+      if (er < G)
+        E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
     } else {
       const size_t slot = 2 * (size_t)w + (s == s0 ? 0 : 1);
       const size_t row = slot * kGroup + er;
@@ -704,10 +810,10 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
   }
 }
 
-// Merge of the balanced split, one workgroup per (request, KV head); wave r
-// takes query head 4g + r. Heads that one workgroup covered whole were
+// Merge of the balanced split, one workgroup per (request, KV head); wave
+// r < G takes query head G g + r. Heads that one workgroup covered whole were
 // written by it; empty heads get zeros.
-template <int QT>
+template <int QT, int G>
 __global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs a) {
   using E = Elem<QT>;
   const int bg = blockIdx.x;
@@ -715,7 +821,8 @@ __global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs
   const int g = bg % kKvHeads;
   const int lane = threadIdx.x & 63;
   const int r = threadIdx.x >> 6;
-  const size_t head = (size_t)b * kQHeads + kGroup * g + r;
+  if (r >= G) return;
+  const size_t head = ((size_t)b * kKvHeads + g) * G + r;
   char* outp = static_cast<char*>(a.out) + (head * kHeadDim + 2 * lane) * 2;
   const int64_t N = a.slab_prefix[a.batch];
   const int nsb = (a.slab_prefix[b + 1] - a.slab_prefix[b]) / kKvHeads;
@@ -723,15 +830,15 @@ __global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs
     E::store2(outp, 0.f, 0.f);
     return;
   }
-  const int64_t G = a.grid_wgs;
+  const int64_t W = a.grid_wgs;
   const int64_t seg_start = a.slab_prefix[b] + (int64_t)g * nsb;
   const int64_t seg_end = seg_start + nsb;
-  // workgroup whose range holds slab t: the largest w with w N / G <= t
-  const int wf = (int)(((seg_start + 1) * G - 1) / N);
-  const int wl = (int)((seg_end * G - 1) / N);
+  // workgroup whose range holds slab t: the largest w with w N / W <= t
+  const int wf = (int)(((seg_start + 1) * W - 1) / N);
+  const int wl = (int)((seg_end * W - 1) / N);
   if (wf == wl) return;
   // wf's range may begin in an earlier head: then this head is its last piece
-  const int first_slot_bump = ((int64_t)wf * N / G < seg_start) ? 1 : 0;
+  const int first_slot_bump = ((int64_t)wf * N / W < seg_start) ? 1 : 0;
   merge_rows<QT>(a, wl - wf + 1,
                  [&](int k) -> size_t {
                    return (2 * (size_t)(wf + k) + (k == 0 ? first_slot_bump : 0)) * kGroup + r;
@@ -739,35 +846,35 @@ __global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs
                  outp);
 }
 
-template <int QT, int KVT>
+template <int QT, int KVT, int G>
 hipError_t enqueue_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
   hipError_t e;
   if (a.grid_wgs > 0) {   // balanced split
-    hipLaunchKernelGGL((gqa_balanced_attention_kernel<QT, KVT>), dim3(a.grid_wgs), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((gqa_balanced_attention_kernel<QT, KVT, G>), dim3(a.grid_wgs), dim3(kThreads),
+                       0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_mid != nullptr && (e = hipEventRecord(ev_mid, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((gqa_balanced_combine_kernel<QT>), dim3((unsigned)a.batch * kKvHeads),
+    hipLaunchKernelGGL((gqa_balanced_combine_kernel<QT, G>), dim3((unsigned)a.batch * kKvHeads),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();
   }
   const unsigned wgs = (unsigned)a.batch * kKvHeads * (unsigned)a.num_splits;
   const bool separate = a.num_splits > 1 && !a.fused_combine;
   if (a.num_splits == 1) {
-    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, kModeDirect>), dim3(wgs), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, G, kModeDirect>), dim3(wgs), dim3(kThreads), 0,
                        stream, a);
   } else if (separate) {
-    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, kModeSplit>), dim3(wgs), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, G, kModeSplit>), dim3(wgs), dim3(kThreads), 0,
                        stream, a);
   } else {
-    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, kModeSplitFused>), dim3(wgs), dim3(kThreads),
-                       0, stream, a);
+    hipLaunchKernelGGL((gqa_attention_kernel<QT, KVT, G, kModeSplitFused>), dim3(wgs),
+                       dim3(kThreads), 0, stream, a);
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev_mid != nullptr && (e = hipEventRecord(ev_mid, stream)) != hipSuccess) return e;
   if (!separate) return hipSuccess;
-  hipLaunchKernelGGL((gqa_combine_kernel<QT>), dim3((unsigned)a.batch * kKvHeads), dim3(kThreads), 0,
-                     stream, a);
+  hipLaunchKernelGGL((gqa_combine_kernel<QT, G>), dim3((unsigned)a.batch * kKvHeads), dim3(kThreads),
+                     0, stream, a);
   return hipGetLastError();
 }
 
@@ -838,26 +945,46 @@ hipError_t enqueue_append_typed(const AppendArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int QT, int KVT>
+template <int QT, int KVT, int G>
 int balanced_grid_typed() {
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&gqa_balanced_attention_kernel<QT, KVT>), kThreads,
-          0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(&gqa_balanced_attention_kernel<QT, KVT, G>),
+          kThreads, 0) != hipSuccess)
     return 0;
   return cus * per_cu;
 }
 
+// Calls f.template operator()<QT, KVT, G>() for a supported combination, else
+// returns `bad`.
+template <typename R, typename F>
+R dispatch(int q_dtype, int kv_dtype, int num_q_heads, R bad, F&& f) {
+  auto by_group = [&](auto qt, auto kvt) -> R {
+    constexpr int QT = decltype(qt)::value, KVT = decltype(kvt)::value;
+    if (num_q_heads == 4 * kKvHeads) return f.template operator()<QT, KVT, 4>();
+    if (num_q_heads == 2 * kKvHeads) return f.template operator()<QT, KVT, 2>();
+    return bad;
+  };
+  using BF = std::integral_constant<int, kBF16>;
+  using F16 = std::integral_constant<int, kF16>;
+  using F8 = std::integral_constant<int, kFP8>;
+  using I8 = std::integral_constant<int, kI8>;
+  if (q_dtype == kBF16 && kv_dtype == kBF16) return by_group(BF{}, BF{});
+  if (q_dtype == kF16 && kv_dtype == kF16) return by_group(F16{}, F16{});
+  if (q_dtype == kBF16 && kv_dtype == kFP8) return by_group(BF{}, F8{});
+  if (q_dtype == kF16 && kv_dtype == kFP8) return by_group(F16{}, F8{});
+  if (q_dtype == kBF16 && kv_dtype == kI8) return by_group(BF{}, I8{});
+  if (q_dtype == kF16 && kv_dtype == kI8) return by_group(F16{}, I8{});
+  return bad;
+}
+
 }  // namespace
 
-int balanced_grid_size(int q_dtype, int kv_dtype) {
-  if (q_dtype == kBF16 && kv_dtype == kBF16) return balanced_grid_typed<kBF16, kBF16>();
-  if (q_dtype == kF16 && kv_dtype == kF16) return balanced_grid_typed<kF16, kF16>();
-  if (q_dtype == kBF16 && kv_dtype == kFP8) return balanced_grid_typed<kBF16, kFP8>();
-  if (q_dtype == kF16 && kv_dtype == kFP8) return balanced_grid_typed<kF16, kFP8>();
-  return 0;
+int balanced_grid_size(int q_dtype, int kv_dtype, int num_q_heads) {
+  return dispatch(q_dtype, kv_dtype, num_q_heads, 0,
+                  []<int QT, int KVT, int G>() { return balanced_grid_typed<QT, KVT, G>(); });
 }
 
 hipError_t enqueue_kv_append(const AppendArgs& a, int src_dtype, int kv_dtype, hipStream_t stream) {
@@ -870,11 +997,8 @@ hipError_t enqueue_kv_append(const AppendArgs& a, int src_dtype, int kv_dtype, h
 
 hipError_t enqueue_decode_step(const StepArgs& a, int q_dtype, int kv_dtype, hipStream_t stream,
                                hipEvent_t ev_mid) {
-  if (q_dtype == kBF16 && kv_dtype == kBF16) return enqueue_typed<kBF16, kBF16>(a, stream, ev_mid);
-  if (q_dtype == kF16 && kv_dtype == kF16) return enqueue_typed<kF16, kF16>(a, stream, ev_mid);
-  if (q_dtype == kBF16 && kv_dtype == kFP8) return enqueue_typed<kBF16, kFP8>(a, stream, ev_mid);
-  if (q_dtype == kF16 && kv_dtype == kFP8) return enqueue_typed<kF16, kFP8>(a, stream, ev_mid);
-  return hipErrorInvalidValue;
+  return dispatch(q_dtype, kv_dtype, a.num_q_heads, hipErrorInvalidValue,
+                  [&]<int QT, int KVT, int G>() { return enqueue_typed<QT, KVT, G>(a, stream, ev_mid); });
 }
 
 }  // namespace gqa

@@ -7,16 +7,19 @@ HIP path and the CPU oracle can consume identical bytes.
 
 Workloads follow the shapes the pages describe: 32 query heads sharing 8 KV
 heads at head_dim 128, a ``[batch, 2, 8, capacity, 128]`` cache, per-request
-int32 lengths (FlashInfer sm110_gqa_decode article, "input contract"), and an
+int32 lengths (FlashInfer sm110_gqa_decode article, "input contract"), an
 fp8_e4m3 cache that stores ``x / scale`` as ``float8_e4m3fn`` bytes with
-per-tensor scales (Thor FP8 KV notes, section 1, patches 1 and 2).
+per-tensor scales (Thor FP8 KV notes, section 1, patches 1 and 2), and an
+INT8 cache with one bf16 scale per (position, KV head) row at 16 query heads
+(Qwen3-VL on Jetson Orin doc, "INT8 KV cache").
 
 Recipe: ``torch.Generator`` on the target device seeded with ``seed``; draw
 order is lengths (``randint(lo, hi + 1)``), then q (fp32 N(0,1), cast RNE),
 then the cache one request at a time (fp32 N(0,1) over both planes, cast RNE;
-for fp8 divided by the plane's scale, clamped to +-448, cast to e4m3fn).
-Slots past a request's length receive the same N(0,1) draw: garbage the
-kernel must never read.
+for fp8 divided by the plane's scale, clamped to +-448, cast to e4m3fn; for
+int8 each 128-value row gets the scale max|x| / 127 rounded to bf16, and the
+values round(x / scale) clamped to +-127). Slots past a request's length
+receive the same N(0,1) draw: garbage the kernel must never read.
 """
 
 from __future__ import annotations
@@ -42,23 +45,26 @@ class Workload:
     len_lo: int
     len_hi: int
     q_dtype: str            # "f16" | "bf16"; the output uses the same dtype
-    kv_dtype: str           # "f16" | "bf16" | "fp8_e4m3"
+    kv_dtype: str           # "f16" | "bf16" | "fp8_e4m3" | "int8"
     q_scale: float = 1.0
     k_scale: float = 1.0
     v_scale: float = 1.0
     seed: int = 0
+    num_q_heads: int = NUM_Q_HEADS   # 32, or 16 (2 query heads per KV head)
 
     def describe(self) -> dict:
         return {
             "workload": self.name, "batch": self.batch, "capacity": self.capacity,
-            "seq_len": [self.len_lo, self.len_hi], "q_heads": NUM_Q_HEADS,
+            "seq_len": [self.len_lo, self.len_hi], "q_heads": self.num_q_heads,
             "kv_heads": NUM_KV_HEADS, "head_dim": HEAD_DIM, "q_dtype": self.q_dtype,
             "kv_dtype": self.kv_dtype, "q_scale": self.q_scale,
             "k_scale": self.k_scale, "v_scale": self.v_scale, "seed": self.seed,
         }
 
 
-# The five workloads, in order. Seeds are 1000 + (1-based position).
+# The five workloads of the main geometry, then the INT8 row-scaled cache at
+# 16 query heads: the doc's 1581-token prompt in a 4096-slot cache, and a
+# long-context batch sized like the fp8 one. Seeds are 1000 + (1-based position).
 WORKLOADS = [
     Workload("gqa_decode_b1_c64_f16", 1, 64, 64, 64, "f16", "f16", seed=1001),
     Workload("gqa_decode_b1_c1024_f16", 1, 1024, 1024, 1024, "f16", "f16", seed=1002),
@@ -67,17 +73,33 @@ WORKLOADS = [
              q_scale=0.5, seed=1004),
     Workload("gqa_decode_b16_c131072_fp8kv_long", 16, 131072, 65536, 131072, "bf16",
              "fp8_e4m3", k_scale=1.0 / 64, v_scale=1.0 / 64, seed=1005),
+    Workload("gqa_decode_b1_c4096_int8kv_16q", 1, 4096, 1581, 1581, "bf16", "int8", seed=1006,
+             num_q_heads=16),
+    Workload("gqa_decode_b16_c131072_int8kv_16q_long", 16, 131072, 65536, 131072, "bf16", "int8",
+             seed=1007, num_q_heads=16),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS}
 
 
 def kv_elem_bytes(kv_dtype: str) -> int:
-    return 1 if kv_dtype == "fp8_e4m3" else 2
+    return 1 if kv_dtype in ("fp8_e4m3", "int8") else 2
+
+
+def kv_slot_bytes(kv_dtype: str) -> int:
+    """Bytes one cache slot of one KV head holds for K and V together (row scales included)."""
+    return 2 * (HEAD_DIM * kv_elem_bytes(kv_dtype) + (2 if kv_dtype == "int8" else 0))
 
 
 def _encode_fp8(x: torch.Tensor, scale: float) -> torch.Tensor:
     y = (x / scale).clamp_(-E4M3_MAX, E4M3_MAX)
     return y.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def _encode_int8_rows(x: torch.Tensor):
+    """Rows of x [..., 128] -> (int8 values, bf16 scales [...]): scale = max|x| / 127 in bf16."""
+    scale = (x.abs().amax(dim=-1) / 127.0).clamp_(min=2.0 ** -100).to(torch.bfloat16)
+    v = torch.round(x / scale.float().unsqueeze(-1)).clamp_(-127, 127).to(torch.int8)
+    return v, scale
 
 
 def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
@@ -99,11 +121,15 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
     lens = lens.to(torch.int32)
     if seq_lens is not None:
         lens = seq_lens.to(device=dev, dtype=torch.int32).clone()
-    q32 = torch.randn(B, NUM_Q_HEADS, HEAD_DIM, generator=gen, device=dev, dtype=torch.float32)
+    q32 = torch.randn(B, w.num_q_heads, HEAD_DIM, generator=gen, device=dev, dtype=torch.float32)
     q = q32.to(_TORCH_DTYPES[w.q_dtype])
     del q32
+    kv_scales = None
     if w.kv_dtype == "fp8_e4m3":
         kv = torch.empty(B, 2, NUM_KV_HEADS, C, HEAD_DIM, device=dev, dtype=torch.uint8)
+    elif w.kv_dtype == "int8":
+        kv = torch.empty(B, 2, NUM_KV_HEADS, C, HEAD_DIM, device=dev, dtype=torch.int8)
+        kv_scales = torch.empty(B, 2, NUM_KV_HEADS, C, device=dev, dtype=torch.bfloat16)
     else:
         kv = torch.empty(B, 2, NUM_KV_HEADS, C, HEAD_DIM, device=dev,
                          dtype=_TORCH_DTYPES[w.kv_dtype])
@@ -113,10 +139,12 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
         if w.kv_dtype == "fp8_e4m3":
             kv[b, 0] = _encode_fp8(x[0], w.k_scale)
             kv[b, 1] = _encode_fp8(x[1], w.v_scale)
+        elif w.kv_dtype == "int8":
+            kv[b], kv_scales[b] = _encode_int8_rows(x)
         else:
             kv[b] = x.to(kv.dtype)
         del x
-    return {"q": q, "kv": kv, "seq_lens": lens, "q_scale": w.q_scale,
+    return {"q": q, "kv": kv, "kv_scales": kv_scales, "seq_lens": lens, "q_scale": w.q_scale,
             "k_scale": w.k_scale, "v_scale": w.v_scale, "q_dtype": w.q_dtype,
             "kv_dtype": w.kv_dtype}
 
@@ -128,4 +156,6 @@ def storage_bits(t: torch.Tensor):
         return t.view(torch.int16).numpy().view("uint16")
     if t.dtype in (torch.uint8, torch.float8_e4m3fn):
         return t.view(torch.uint8).numpy()
+    if t.dtype == torch.int8:
+        return t.numpy()
     raise TypeError(f"unsupported storage dtype {t.dtype}")

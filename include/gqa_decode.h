@@ -2,13 +2,16 @@
  * gqa_decode.h — C ABI of the MI355X (gfx950) single-token grouped-query
  * decode-attention library (libgqa_decode.so).
  *
- * Operation. For every request b and query head h (32 per request, sharing
- * 8 KV heads, head dimension 128, so head h reads KV head h / 4):
+ * Operation. For every request b and query head h (Hq = 32 or 16 per
+ * request, sharing 8 KV heads, head dimension 128, so head h reads KV head
+ * h / G with G = Hq / 8):
  *
- *     s_j     = q_scale * k_scale / sqrt(128) * dot(q[b,h,:], K[b,h/4,j,:])
- *     out[b,h,:] = v_scale * sum_{j < L_b} softmax_j(s) * V[b,h/4,j,:]
+ *     s_j     = q_scale * k_scale / sqrt(128) * dot(q[b,h,:], K[b,h/G,j,:])
+ *     out[b,h,:] = v_scale * sum_{j < L_b} softmax_j(s) * V[b,h/G,j,:]
  *
- * with L_b = seq_lens[b]. Sources: the FlashInfer sm110_gqa_decode article
+ * with L_b = seq_lens[b]. For an INT8 cache, K[b,g,j,:] = k8[b,g,j,:] *
+ * ks[b,g,j] and V[b,g,j,:] = v8[b,g,j,:] * vs[b,g,j] with one bf16 scale per
+ * (position, KV head) row. Sources: the FlashInfer sm110_gqa_decode article
  * (cf-1.com news 5454068): "why a separate SM110 GQA decode path" (fixed
  * 32/8/128 geometry, one query token per request), "input contract" (layout
  * and the device-only lengths), "convenience API" (signature, the grouped
@@ -16,14 +19,20 @@
  * phase, the three differences, lifecycle and concurrency, num_splits and
  * the FP32 split workspace); and the Thor FP8 KV-cache porting notes
  * (kipfel.ltd), section 1, patches 1-2 (uint8 bytes reinterpreted as
- * float8_e4m3fn; scores *= k_scale, normalised output *= v_scale).
+ * float8_e4m3fn; scores *= k_scale, normalised output *= v_scale); and the
+ * Qwen3-VL on Jetson Orin doc (stargazers.cn, FlashRT), "INT8 KV cache"
+ * (INT8 mirrors with one BF16 scale per (position, KV head) row, decode
+ * geometry 16 query heads / 8 KV heads / head_dim 128).
  *
  * Layouts (all dense, contiguous, row-major, device memory, 16-byte aligned):
- *   q        [batch, 32, 128]                  q_dtype (F16 or BF16)
- *   kv       [batch, 2, 8, capacity, 128]      kv_dtype; plane 0 = K, 1 = V
- *                                              (FP8: OCP E4M3FN bytes)
- *   seq_lens [batch] int32, read on the device only (4-byte aligned)
- *   out      [batch, 32, 128]                  q_dtype (written by the call)
+ *   q         [batch, Hq, 128]                 q_dtype (F16 or BF16)
+ *   kv        [batch, 2, 8, capacity, 128]     kv_dtype; plane 0 = K, 1 = V
+ *                                              (FP8: OCP E4M3FN bytes;
+ *                                               INT8_ROWSCALE: int8 values)
+ *   kv_scales [batch, 2, 8, capacity]          bf16 row scales, INT8 only
+ *                                              (plane 0 = K, 1 = V)
+ *   seq_lens  [batch] int32, read on the device only (4-byte aligned)
+ *   out       [batch, Hq, 128]                 q_dtype (written by the call)
  *
  * Ownership. The caller owns q, kv, seq_lens and out and must keep them
  * alive until the enqueued work (and any captured graph containing it)
@@ -56,6 +65,8 @@ extern "C" {
 #define GQA_API __attribute__((visibility("default")))
 
 #define GQA_NUM_Q_HEADS 32
+/* The other accepted query-head count: 2 query heads per KV head. */
+#define GQA_NUM_Q_HEADS_2TO1 16
 #define GQA_NUM_KV_HEADS 8
 #define GQA_HEAD_DIM 128
 /* Capacities up to this value take the short route (one workgroup per
@@ -80,24 +91,28 @@ typedef enum gqa_status {
 typedef enum gqa_dtype {
   GQA_F16 = 0,
   GQA_BF16 = 1,
-  GQA_FP8_E4M3 = 2 /* KV only: OCP E4M3FN bytes (torch.float8_e4m3fn) */
+  GQA_FP8_E4M3 = 2,     /* KV only: OCP E4M3FN bytes (torch.float8_e4m3fn) */
+  GQA_INT8_ROWSCALE = 3 /* KV only: int8 values + one bf16 scale per (slot, KV head)
+                           row, passed separately (gqa_decode_int8) */
 } gqa_dtype_t;
 
 /* Problem descriptor. Fields are int32/float so the struct has one layout
  * for every caller. Accepted dtype pairs (q, kv): (F16, F16), (BF16, BF16),
- * (F16, FP8_E4M3), (BF16, FP8_E4M3). out has q's dtype. k_scale and v_scale
- * must be finite and > 0, and must equal 1.0 unless kv is FP8_E4M3 (a scale
- * on a 16-bit cache is rejected rather than silently ignored). */
+ * (F16, FP8_E4M3), (BF16, FP8_E4M3), (F16, INT8_ROWSCALE),
+ * (BF16, INT8_ROWSCALE); every pair with 32 or 16 query heads. out has q's
+ * dtype. k_scale and v_scale must be finite and > 0, and must equal 1.0 for
+ * a 16-bit cache (a scale there is rejected rather than silently ignored);
+ * on an INT8 cache they multiply on top of the row scales. */
 typedef struct gqa_desc {
   int32_t batch;        /* >= 0; 0 makes every call a no-op */
   int32_t capacity;     /* 1 .. GQA_MAX_CAPACITY (kv.shape[-2]) */
-  int32_t num_q_heads;  /* must be 32 */
+  int32_t num_q_heads;  /* 32 or 16 (GQA_NUM_Q_HEADS_2TO1) */
   int32_t num_kv_heads; /* must be 8 */
   int32_t head_dim;     /* must be 128 */
   int32_t q_dtype;      /* gqa_dtype_t */
   int32_t kv_dtype;     /* gqa_dtype_t */
-  float k_scale;        /* multiplies every score (fp8 cache) */
-  float v_scale;        /* multiplies the normalised output (fp8 cache) */
+  float k_scale;        /* multiplies every score (fp8 / int8 cache) */
+  float v_scale;        /* multiplies the normalised output (fp8 / int8 cache) */
   int32_t flags;        /* GQA_FLAG_* bits; 0 for the defaults */
 } gqa_desc_t;
 
@@ -179,6 +194,23 @@ GQA_API gqa_status_t launch_gqa_decode_prepared_timed(gqa_prepared_t* handle, hi
                                                       hipEvent_t ev_start, hipEvent_t ev_mid,
                                                       hipEvent_t ev_end);
 
+/* INT8 cache with per-row scales (Qwen3-VL on Jetson Orin doc, "INT8 KV
+ * cache"): as gqa_decode / prepare_gqa_decode, for desc->kv_dtype ==
+ * GQA_INT8_ROWSCALE only, with the bf16 row scales kv_scales [batch, 2, 8,
+ * capacity] (16-byte aligned, caller-owned like kv; slots at or beyond a
+ * request's length are never read). Token j's K scale multiplies its score,
+ * its V scale its softmax weight in the output sum. The plain entry points
+ * reject an INT8 descriptor (they have no scales argument); these reject any
+ * other kv dtype. out must not overlap kv_scales either. The handle runs with
+ * launch_gqa_decode_prepared like any other. */
+GQA_API gqa_status_t gqa_decode_int8(const gqa_desc_t* desc, const void* q, const void* kv,
+                                     const void* kv_scales, const int32_t* seq_lens,
+                                     float q_scale, void* out, hipStream_t stream);
+GQA_API gqa_status_t prepare_gqa_decode_int8(const gqa_desc_t* desc, const void* q,
+                                             const void* kv, const void* kv_scales,
+                                             const int32_t* seq_lens, float q_scale, void* out,
+                                             int32_t num_splits, gqa_prepared_t** handle);
+
 /* Free the workspace and the handle (after its work has retired). NULL is a no-op. */
 GQA_API void gqa_prepared_destroy(gqa_prepared_t* handle);
 
@@ -200,16 +232,21 @@ GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* handle, gqa_plan_t*
  * division, nearest E4M3FN code with ties to even, magnitudes >= 448
  * saturating to +-448, NaN stored as 0x7F. Positions outside [0, capacity)
  * write nothing. kv must not overlap k_new, v_new or positions
- * (GQA_ERR_ALIAS). Asynchronous on `stream`; allocates nothing. */
+ * (GQA_ERR_ALIAS). Asynchronous on `stream`; allocates nothing. An INT8
+ * cache is rejected (GQA_ERR_INVALID_ARG): its rows and scales are written
+ * by the caller. */
 GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,
                                    const int32_t* positions, void* kv, hipStream_t stream);
 
 /* Host-only validation of a call's arguments (never touches a device, so it
  * runs without a GPU). Same checks and status codes as prepare_gqa_decode,
- * except the device check. */
+ * except the device check; the _int8 form as prepare_gqa_decode_int8. */
 GQA_API gqa_status_t gqa_validate_args(const gqa_desc_t* desc, const void* q, const void* kv,
                                        const int32_t* seq_lens, float q_scale,
                                        const void* out, int32_t num_splits);
+GQA_API gqa_status_t gqa_validate_args_int8(const gqa_desc_t* desc, const void* q, const void* kv,
+                                            const void* kv_scales, const int32_t* seq_lens,
+                                            float q_scale, const void* out, int32_t num_splits);
 
 /* Host-only planning: the route, chunking and workspace a call would use
  * (num_splits as for prepare_gqa_decode). Runs without a GPU, so a balanced

@@ -8,10 +8,12 @@ import pytest
 import torch
 
 from gqa_kv_cache_attn_amd.inputs import Workload, make_inputs, storage_bits  # noqa: F401
-from oracle import decode_storage, gqa_decode_head
+from oracle import decode_int8_rows, decode_storage, gqa_decode_head
 
-# Contract tolerances: max-abs error on the output, by KV dtype.
-ATOL = {"f16": 2e-3, "bf16": 2e-3, "fp8_e4m3": 2e-2}
+# Contract tolerances: max-abs error on the output, by KV dtype. An INT8 cache
+# with bf16 row scales decodes exactly (int8 and bf16 both widen exactly), like
+# a 16-bit cache, so it is held to the 16-bit bound.
+ATOL = {"f16": 2e-3, "bf16": 2e-3, "fp8_e4m3": 2e-2, "int8": 2e-3}
 # Output ulp exponent offset (mantissa bits) by output dtype.
 _MANT = {"f16": 10, "bf16": 7}
 
@@ -28,35 +30,65 @@ def binding():
     return b
 
 
+def prepare(inp, out, num_splits=None, fused_combine=False):
+    """prepare_gqa_decode, or its _int8 form for an INT8 cache."""
+    b = binding()
+    if inp["kv_dtype"] == "int8":
+        return b.prepare_gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"],
+                                         out, inp["q_scale"], num_splits=num_splits,
+                                         k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                                         fused_combine=fused_combine)
+    return b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
+                                num_splits=num_splits, k_scale=inp["k_scale"],
+                                v_scale=inp["v_scale"], fused_combine=fused_combine)
+
+
 def run_decode(inp, path="convenience", num_splits=None, out=None, fused_combine=False):
     b = binding()
     if out is None:
         out = torch.empty_like(inp["q"])
     if path == "convenience":
-        b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], inp["q_scale"], out,
-                     k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+        if inp["kv_dtype"] == "int8":
+            b.gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"],
+                              inp["q_scale"], out, k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+        else:
+            b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], inp["q_scale"], out,
+                         k_scale=inp["k_scale"], v_scale=inp["v_scale"])
         torch.cuda.synchronize()
         return out, None
-    prep = b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
-                                num_splits=num_splits, k_scale=inp["k_scale"],
-                                v_scale=inp["v_scale"], fused_combine=fused_combine)
+    prep = prepare(inp, out, num_splits, fused_combine)
     b.launch_gqa_decode_prepared(prep)
     torch.cuda.synchronize()
     return out, prep
 
 
+def group_of(inp):
+    """Query heads per KV head (4 for 32 query heads, 2 for 16)."""
+    return inp["q"].shape[1] // 8
+
+
+def decoded_kv_rows(inp, b, plane, g, L):
+    """Decoded fp64 rows [L, 128] of one (request, plane, KV head) of the cache."""
+    kv = inp["kv"]
+    if inp["kv_dtype"] == "int8":
+        return decode_int8_rows(storage_bits(kv[b, plane, g, :L]),
+                                storage_bits(inp["kv_scales"][b, plane, g, :L]))
+    return decode_storage(storage_bits(kv[b, plane, g, :L]), inp["kv_dtype"])
+
+
 def oracle_pairs(inp, pairs):
-    """Oracle output rows [4, 128] (fp64) for each (request, KV head) pair."""
+    """Oracle output rows [G, 128] (fp64) for each (request, KV head) pair."""
     q, kv = inp["q"], inp["kv"]
     lens = inp["seq_lens"].cpu().numpy()
     C = kv.shape[3]
+    G = group_of(inp)
     res = {}
     for (b, g) in pairs:
         L = int(lens[b])
         assert 1 <= L <= C, "oracle needs 1 <= L <= capacity"
-        qrows = decode_storage(storage_bits(q[b, 4 * g:4 * g + 4]), inp["q_dtype"])
-        k = decode_storage(storage_bits(kv[b, 0, g, :L]), inp["kv_dtype"])
-        v = decode_storage(storage_bits(kv[b, 1, g, :L]), inp["kv_dtype"])
+        qrows = decode_storage(storage_bits(q[b, G * g:G * g + G]), inp["q_dtype"])
+        k = decoded_kv_rows(inp, b, 0, g, L)
+        v = decoded_kv_rows(inp, b, 1, g, L)
         res[(b, g)] = gqa_decode_head(qrows, k, v, inp["q_scale"], inp["k_scale"], inp["v_scale"])
     return res
 
@@ -86,9 +118,10 @@ def compare(out, ref_pairs, inp, label="", contract_only=False):
     of the absolute bound."""
     got_all = decoded_out(out, inp["q_dtype"])
     atol = ATOL[inp["kv_dtype"]]
+    G = group_of(inp)
     errs, refs, excess = [], [], []
     for (b, g), ref in ref_pairs.items():
-        got = got_all[b, 4 * g:4 * g + 4]
+        got = got_all[b, G * g:G * g + G]
         assert np.all(np.isfinite(got)), f"{label}: non-finite output at (b={b}, g={g})"
         err = np.abs(got - ref)
         errs.append(err.max())

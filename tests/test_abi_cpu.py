@@ -52,12 +52,15 @@ def v(d, q=Q, kv=KV, lens=LENS, qs=1.0, out=OUT, ns=0):
 
 def test_valid_arguments_pass():
     assert v(desc()) == OK
+    assert v(desc(hq=16)) == OK                      # 2 query heads per KV head
+    assert v(desc(hq=16, q=b.GQA_F16, kv=b.GQA_FP8_E4M3)) == OK
     assert v(desc(q=b.GQA_F16, kv=b.GQA_F16)) == OK
     assert v(desc(q=b.GQA_BF16, kv=b.GQA_FP8_E4M3, ks=1 / 64, vs=1 / 64)) == OK
     assert v(desc(q=b.GQA_F16, kv=b.GQA_FP8_E4M3)) == OK
 
 
-@pytest.mark.parametrize("field,value", [("num_q_heads", 16), ("num_kv_heads", 4), ("head_dim", 64),
+@pytest.mark.parametrize("field,value", [("num_q_heads", 24), ("num_q_heads", 8), ("num_q_heads", 64),
+                                         ("num_kv_heads", 4), ("head_dim", 64),
                                          ("capacity", 0), ("capacity", -3), ("batch", -1),
                                          ("capacity", (1 << 22) + 1)])
 def test_fixed_geometry_and_sizes(field, value):
@@ -69,6 +72,7 @@ def test_fixed_geometry_and_sizes(field, value):
 
 @pytest.mark.parametrize("q,kv", [(b.GQA_F16, b.GQA_BF16), (b.GQA_BF16, b.GQA_F16),
                                   (b.GQA_FP8_E4M3, b.GQA_FP8_E4M3), (7, b.GQA_BF16),
+                                  (b.GQA_INT8_ROWSCALE, b.GQA_INT8_ROWSCALE),
                                   (b.GQA_BF16, 9)])
 def test_unsupported_dtype_pairs(q, kv):
     assert v(desc(q=q, kv=kv)) == INVALID
@@ -205,3 +209,58 @@ def test_kv_append_rejects_bad_arguments_without_touching_a_device():
     assert app(ctypes.byref(d), KV_ + 4096, V, P, KV_, None) == ALIAS    # k_new inside the cache
     d0 = desc(batch=0)
     assert app(ctypes.byref(d0), None, None, None, None, None) == OK
+
+
+# ---------------------------------------------------------------- INT8 row-scaled cache
+SC = 5 * 1024 * MiB   # fake address of the row scales
+
+
+def v8(d, q=Q, kv=KV, sc=SC, lens=LENS, qs=1.0, out=OUT, ns=0):
+    return b.gqa_validate_args_int8(d, q, kv, sc, lens, qs, out, ns)
+
+
+@pytest.mark.parametrize("qd", [b.GQA_BF16, b.GQA_F16])
+@pytest.mark.parametrize("hq", [16, 32])
+def test_int8_valid_arguments_pass(qd, hq):
+    assert v8(desc(q=qd, kv=b.GQA_INT8_ROWSCALE, hq=hq)) == OK
+    # per-tensor scales multiply on top of the row scales
+    assert v8(desc(q=qd, kv=b.GQA_INT8_ROWSCALE, hq=hq, ks=0.5, vs=4.0)) == OK
+
+
+def test_int8_cache_needs_the_int8_entry_points_and_vice_versa():
+    assert v(desc(kv=b.GQA_INT8_ROWSCALE, hq=16)) == INVALID
+    assert "int8" in b.last_error()
+    assert v8(desc(kv=b.GQA_BF16, hq=16)) == INVALID
+    assert v8(desc(kv=b.GQA_FP8_E4M3, hq=16)) == INVALID
+
+
+def test_int8_scales_pointer_checks():
+    d = desc(batch=2, capacity=1024, kv=b.GQA_INT8_ROWSCALE, hq=16)
+    assert v8(d, sc=None) == INVALID
+    assert v8(d, sc=SC + 2) == INVALID                # scales must be 16-byte aligned
+    q_bytes = 2 * 16 * 128 * 2
+    sc_bytes = 2 * 2 * 8 * 1024 * 2
+    assert v8(d, out=SC + sc_bytes // 2) == ALIAS     # out inside the scales
+    assert v8(d, out=SC - q_bytes + 16) == ALIAS
+    assert v8(d, out=SC + sc_bytes) == OK
+    assert v8(desc(batch=0, kv=b.GQA_INT8_ROWSCALE), q=None, kv=None, sc=None, lens=None,
+              out=None) == OK
+
+
+@pytest.mark.parametrize("hq", [16, 32])
+@pytest.mark.parametrize("kv", [b.GQA_BF16, b.GQA_FP8_E4M3, b.GQA_INT8_ROWSCALE])
+def test_chunked_workspace_scales_with_query_heads(hq, kv):
+    d = desc(batch=3, capacity=5000, kv=kv, hq=hq)
+    p = b.gqa_plan(d, 7)
+    assert p["route"] == 1 and p["num_splits"] == 7
+    assert p["workspace_bytes"] == 3 * hq * 7 * 130 * 4 + 256
+    # the balanced split's partial slots do not depend on the geometry
+    assert b.gqa_plan(desc(batch=8, capacity=65536, kv=kv, hq=hq))["workspace_bytes"] == balanced_ws(8)
+
+
+def test_int8_chunk_sizing_counts_the_row_scales():
+    """Automatic chunks hold about 1 MiB of cache: 64-slot steps of
+    64 * 2 * (128 + 2) bytes for INT8 (the row scales included)."""
+    d = desc(batch=4097, capacity=65536, kv=b.GQA_INT8_ROWSCALE, hq=16)
+    p = b.gqa_plan(d)
+    assert p["route"] == 1 and p["chunk_tokens"] == 64 * ((1 << 20) // (64 * 2 * 130))

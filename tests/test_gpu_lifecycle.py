@@ -6,7 +6,8 @@ that must leave the output untouched."""
 import pytest
 import torch
 
-from gpu_util import Workload, all_pairs, binding, compare, make_inputs, oracle_pairs, require_gpu
+from gpu_util import Workload, all_pairs, binding, compare, make_inputs, oracle_pairs, prepare
+from gpu_util import require_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -18,25 +19,23 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _inputs(B=4, C=4096, qd="bf16", kd="bf16", seed=31):
+def _inputs(B=4, C=4096, qd="bf16", kd="bf16", seed=31, hq=32):
     fp8 = kd == "fp8_e4m3"
     w = Workload(f"life_{qd}_{kd}", B, C, 1, C, qd, kd, q_scale=0.9,
-                 k_scale=1 / 64 if fp8 else 1.0, v_scale=1 / 64 if fp8 else 1.0, seed=seed)
+                 k_scale=1 / 64 if fp8 else 1.0, v_scale=1 / 64 if fp8 else 1.0, seed=seed,
+                 num_q_heads=hq)
     return make_inputs(w, device="cuda")
 
 
 def _prepare(inp, out, num_splits=None, fused_combine=False):
-    b = binding()
-    return b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
-                                num_splits=num_splits, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
-                                fused_combine=fused_combine)
+    return prepare(inp, out, num_splits, fused_combine)
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kd,hq", [("bf16", 32), ("fp8_e4m3", 32), ("int8", 16)])
 @pytest.mark.parametrize("plan", ["balanced", "chunked", "fused"])
-def test_graph_replay_with_rewritten_lengths_matches_direct_launch(kd, plan):
+def test_graph_replay_with_rewritten_lengths_matches_direct_launch(kd, hq, plan):
     b = binding()
-    inp = _inputs(kd=kd)
+    inp = _inputs(kd=kd, hq=hq)
     out = torch.empty_like(inp["q"])
     prep = _prepare(inp, out, num_splits=None if plan == "balanced" else 8,
                     fused_combine=plan == "fused")
@@ -140,3 +139,23 @@ def test_invalid_calls_enqueue_nothing_and_leave_out_untouched():
         b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], 1.0, out, k_scale=0.5)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+def test_int8_entry_points_reject_mismatches_and_aliases():
+    b = binding()
+    inp = _inputs(B=2, C=512, kd="int8", hq=16)
+    out = torch.full_like(inp["q"], 7.0)
+    with pytest.raises(ValueError):   # an INT8 cache needs its row scales
+        b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], 1.0, out)
+    with pytest.raises(ValueError):
+        b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out)
+    alias = inp["kv_scales"].view(-1)[:out.numel()].view_as(out)
+    before = alias.clone()
+    with pytest.raises(ValueError):   # out overlapping kv_scales
+        b.gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], 1.0, alias)
+    with pytest.raises(ValueError):   # scales of the wrong shape
+        b.gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"][:, :, :, :100].contiguous(),
+                          inp["seq_lens"], 1.0, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    assert torch.equal(alias.view(torch.int16), before.view(torch.int16))
