@@ -535,6 +535,13 @@ __device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, in
                                              WorkgroupLds& lds, float& M, float& lsum, float& o0,
                                              float& o1) {
   constexpr int kRowBytes = kHeadDim * (kByteKv<KVT> ? 1 : 2);
+  // (b, g, c0, c1) are the same in every lane. Stating it keeps the buffer
+  // descriptors in scalar registers: one the compiler takes for divergent
+  // costs a waterfall loop around every load.
+  b = __builtin_amdgcn_readfirstlane(b);
+  g = __builtin_amdgcn_readfirstlane(g);
+  c0 = __builtin_amdgcn_readfirstlane(c0);
+  c1 = __builtin_amdgcn_readfirstlane(c1);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -757,7 +764,9 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
   const int tid = threadIdx.x;
   const int B = a.batch;
   build_slab_prefix(a, s_pref, s_wave_tot);
-  const int64_t N = s_pref[B];
+  // Values read from LDS are the same in every lane; saying so keeps the
+  // loop control in scalar registers.
+  const int64_t N = __builtin_amdgcn_readfirstlane(s_pref[B]);
   const int W = (int)gridDim.x;
   const int w = (int)blockIdx.x;
   if (w == 0)   // the combine kernel reads the same prefix
@@ -784,13 +793,14 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
       const int mid = (lo + hi) >> 1;
       if (s_pref[mid] <= s) lo = mid; else hi = mid;
     }
-    const int b = lo;
-    const int nsb = (s_pref[b + 1] - s_pref[b]) / kKvHeads;   // >= 1 here
-    const int g = (s - s_pref[b]) / nsb;
-    const int seg_start = s_pref[b] + g * nsb;
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int pref_b = __builtin_amdgcn_readfirstlane(s_pref[b]);
+    const int nsb = (__builtin_amdgcn_readfirstlane(s_pref[b + 1]) - pref_b) / kKvHeads;   // >= 1
+    const int g = (s - pref_b) / nsb;
+    const int seg_start = pref_b + g * nsb;
     const int seg_end = seg_start + nsb;
     const int pe = min(s1, seg_end);
-    const int L = min(max(a.seq_lens[b], 0), a.capacity);
+    const int L = min(max(__builtin_amdgcn_readfirstlane(a.seq_lens[b]), 0), a.capacity);
     const int c0 = (s - seg_start) * kSlab;
     const int c1 = min((pe - seg_start) * kSlab, L);
     float M, lsum, o0, o1;
