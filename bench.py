@@ -219,6 +219,47 @@ def main():
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (attn_avg * 1e-3) / 1e9
 
+    # The same step replayed from a captured HIP graph (one launch per graph,
+    # K replays back to back), and through the convenience call.
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        b.launch_gqa_decode_prepared(prep)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        b.launch_gqa_decode_prepared(prep)
+    graph.replay()
+    torch.cuda.synchronize()
+    g_begin, g_end = new_event(), new_event()
+    torch.cuda.synchronize()
+    g_begin.record(stream)
+    for _ in range(K):
+        graph.replay()
+    g_end.record(stream)
+    torch.cuda.synchronize()
+    graph_us = g_begin.elapsed_time(g_end) / K * 1e3
+    del graph
+
+    def convenience():
+        if w.kv_dtype == "int8":
+            b.gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], inp["q_scale"],
+                              out, k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+        else:
+            b.gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], inp["q_scale"], out,
+                         k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    for _ in range(3):
+        convenience()
+    c_begin, c_end = new_event(), new_event()
+    torch.cuda.synchronize()
+    c_begin.record(stream)
+    for _ in range(K):
+        convenience()
+    c_end.record(stream)
+    torch.cuda.synchronize()
+    convenience_us = c_begin.elapsed_time(c_end) / K * 1e3
+
     # KV append (the cache write before each step): one token per request at
     # slot L_b, past the valid prefix, so the decode inputs are unchanged. An
     # INT8 cache's rows and scales are written by the caller: not timed here.
@@ -275,6 +316,8 @@ def main():
                    "algorithmic_bytes_per_step": nbytes, "plan": plan},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "us_per_call": round(ms_per_step * 1e3, 2),
+        "us_per_call_graph_replay": round(graph_us, 2),
+        "us_per_call_convenience": round(convenience_us, 2),
         "us_per_call_cold": {"p10": round(pct(cold, 10), 2), "p50": round(pct(cold, 50), 2),
                              "p90": round(pct(cold, 90), 2)} if cold else None,
         "kv_append_us": append_us,
