@@ -9,8 +9,12 @@ Modules:
   gqa_oracle  vectorised fp64 numpy definition of the decode step, plus the
               exact decoders for the stored KV/query formats.
   brute       pure-Python loops (math.fsum / math.exp) for tiny inputs.
+  kv_append   the cache write before a decode step (fp8 quantise-on-write).
+  paged       decode over a paged cache (page pool + block table) with T
+              query tokens per request, causal among themselves.
 
-Every function is pinned by ``tests/test_oracle_pins.py`` against facts fixed
+Every function is pinned by ``tests/test_oracle_pins.py`` (and
+``tests/test_oracle_pins_paged.py`` for ``paged``) against facts fixed
 by the pages or by mathematics (closed forms, invariants, a library special
 case, brute force). No function here is "parity unpinned".
 """

@@ -1,0 +1,103 @@
+"""Reference for decode over a paged KV cache with several query tokens per
+request (the verify pass of speculative decoding).
+
+TEST INFRASTRUCTURE ONLY: used by tests, never by the product path. It shares
+no code with the HIP library; the per-(request, KV head) arithmetic is the
+pinned plain definition in ``gqa_oracle.gqa_decode_head``.
+
+What is computed.
+
+* Paged cache. The FreeToken Turing notes (change 2, the automatic attention
+  backend) name a paged-KV decode backend that runs under CUDA-graph capture;
+  the pages give no layout. Reading taken: a pool ``kv_pages`` of shape
+  ``[num_pages, 2, 8, page_size, 128]`` (each page holds the same
+  ``[2, 8, slots, 128]`` block as the contiguous cache of the GQA-decode
+  article's input contract, for ``page_size`` slots), and an int32 block table
+  ``[batch, max_pages]``: slot ``j`` of request ``b`` is row ``j % page_size``
+  of page ``block_table[b, j // page_size]``. An INT8 pool carries its row
+  scales as ``[num_pages, 2, 8, page_size]`` bf16 (Orin Qwen3-VL doc, "INT8 KV
+  cache": one scale per (position, KV head) row).
+* Several query tokens. The Thor vLLM notes on MTP (K draft tokens per step,
+  verified by the target model each step) imply a pass over K + 1 new tokens
+  per request. Reading taken: ``T`` query tokens per request, ``q`` of shape
+  ``[batch, T, Hq, 128]``; they are the last ``T`` of the ``L`` slots the
+  length counts (already written to the cache), and token ``t`` (0-based)
+  attends slots ``j < L - T + 1 + t``: causal among the new tokens, everything
+  before them visible. ``T = 1`` is the single-token decode.
+
+Everything else (head grouping h // (Hq / 8), the scales, the softmax) is the
+single-token definition applied to each (request, token, KV head).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .gqa_oracle import HEAD_DIM, NUM_KV_HEADS, gqa_decode_head
+
+
+def gather_pages(kv_pages: np.ndarray, table_row, length: int, page_size: int) -> np.ndarray:
+    """Logical rows [2, 8, length, ...] of one request, slot by slot."""
+    kv_pages = np.asarray(kv_pages)
+    if page_size < 1 or kv_pages.shape[3] != page_size:
+        raise ValueError("page_size must be >= 1 and match kv_pages.shape[3]")
+    num_pages = kv_pages.shape[0]
+    out = np.empty((2, kv_pages.shape[2], length) + kv_pages.shape[4:], dtype=kv_pages.dtype)
+    for j in range(length):
+        logical = j // page_size
+        if logical >= len(table_row):
+            raise ValueError(f"slot {j} needs page {logical}, beyond the block table row")
+        page = int(table_row[logical])
+        if not 0 <= page < num_pages:
+            raise ValueError(f"block table entry {page} outside [0, {num_pages})")
+        out[:, :, j] = kv_pages[page, :, :, j % page_size]
+    return out
+
+
+def gqa_decode_multi(q: np.ndarray, kv_rows, seq_lens, q_scale: float = 1.0,
+                     k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """q [B, T, Hq, 128]; kv_rows[b] = decoded logical rows [2, 8, >= L_b, 128].
+
+    Returns out [B, T, Hq, 128] (fp64): token t of request b attends slots
+    j < L_b - T + 1 + t. Raises when a token would see no slot (L_b < T).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if q.ndim != 4 or q.shape[2] not in (16, 32) or q.shape[3] != HEAD_DIM:
+        raise ValueError(f"q must be [batch, T, 32 or 16, 128], got {q.shape}")
+    B, T, Hq, _ = q.shape
+    group = Hq // NUM_KV_HEADS
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if lens.shape != (B,) or len(kv_rows) != B:
+        raise ValueError("batch mismatch between q, kv rows and sequence_lengths")
+    out = np.empty_like(q)
+    for b in range(B):
+        L = int(lens[b])
+        kvb = np.asarray(kv_rows[b], dtype=np.float64)
+        if L < T or L > kvb.shape[2]:
+            raise ValueError(f"request {b}: need T <= L <= its slots (T={T}, L={L})")
+        for t in range(T):
+            visible = L - T + 1 + t
+            for g in range(NUM_KV_HEADS):
+                rows = slice(group * g, group * (g + 1))
+                out[b, t, rows] = gqa_decode_head(q[b, t, rows], kvb[0, g, :visible],
+                                                  kvb[1, g, :visible], q_scale, k_scale, v_scale)
+    return out
+
+
+def gqa_decode_paged_reference(q: np.ndarray, kv_pages: np.ndarray, block_table, seq_lens,
+                               page_size: int, q_scale: float = 1.0, k_scale: float = 1.0,
+                               v_scale: float = 1.0) -> np.ndarray:
+    """q [B, T, Hq, 128]; kv_pages decoded fp64 [num_pages, 2, 8, page_size, 128];
+    block_table [B, max_pages] int; returns out [B, T, Hq, 128] (fp64)."""
+    kv_pages = np.asarray(kv_pages, dtype=np.float64)
+    if kv_pages.ndim != 5 or kv_pages.shape[1:3] != (2, NUM_KV_HEADS) or \
+            kv_pages.shape[4] != HEAD_DIM:
+        raise ValueError(f"kv_pages must be [num_pages, 2, 8, page_size, 128], got {kv_pages.shape}")
+    table = np.asarray(block_table)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if table.ndim != 2 or table.shape[0] != lens.shape[0]:
+        raise ValueError("block_table must be [batch, max_pages]")
+    if np.any(lens > table.shape[1] * page_size):
+        raise ValueError("a length exceeds max_pages * page_size")
+    rows = [gather_pages(kv_pages, table[b], int(lens[b]), page_size) for b in range(len(lens))]
+    return gqa_decode_multi(q, rows, lens, q_scale, k_scale, v_scale)

@@ -1,0 +1,154 @@
+"""Pins for the paged / multi-token oracle (oracle/paged.py): facts fixed by
+mathematics or by a library routine, each chosen so that a plausible mistake
+(slot j read from the wrong page or row, an off-by-one causal limit, token
+order reversed, grouping lost) fails at least one of them."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import HEAD_DIM, NUM_KV_HEADS, decode_int8_rows, gqa_decode_reference
+from oracle.brute import brute_decode
+from oracle.paged import gather_pages, gqa_decode_multi, gqa_decode_paged_reference
+
+
+def _scatter_case(rng, B, P, max_pages, lens, spare=3, dtype=np.float64):
+    """Contiguous rows X [B, 2, 8, max_pages*P, 128] written into a shuffled pool
+    by explicit loops (the inverse of the gather under test); unused pages NaN."""
+    C = P * max_pages
+    X = rng.standard_normal((B, 2, NUM_KV_HEADS, C, HEAD_DIM)).astype(dtype)
+    num_pages = B * max_pages + spare
+    ids = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages)
+    pool = np.full((num_pages, 2, NUM_KV_HEADS, P, HEAD_DIM), np.nan, dtype=dtype)
+    for b in range(B):
+        for p in range(max_pages):
+            for s in range(P):
+                pool[ids[b, p], :, :, s] = X[b, :, :, p * P + s]
+    return X, pool, ids.astype(np.int32), np.asarray(lens)
+
+
+@pytest.mark.parametrize("P", [16, 32, 48])
+def test_gather_inverts_an_explicit_scatter(P):
+    rng = np.random.default_rng(3)
+    X, pool, table, lens = _scatter_case(rng, 3, P, 4, [4 * P, 1, 2 * P + 5])
+    for b in range(3):
+        L = int(lens[b])
+        assert np.array_equal(gather_pages(pool, table[b], L, P), X[b, :, :, :L])
+
+
+def test_single_token_paged_equals_the_contiguous_definition():
+    rng = np.random.default_rng(5)
+    P = 16
+    X, pool, table, lens = _scatter_case(rng, 2, P, 3, [48, 17])
+    q = rng.standard_normal((2, 1, 32, HEAD_DIM))
+    got = gqa_decode_paged_reference(q, pool, table, lens, P, 0.8, 0.5, 2.0)
+    want = gqa_decode_reference(q[:, 0], X, lens, 0.8, 0.5, 2.0)
+    np.testing.assert_allclose(got[:, 0], want, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("Hq,T", [(32, 1), (32, 2), (32, 4), (16, 3), (16, 8)])
+def test_causal_rows_match_sdpa_with_a_boolean_mask(Hq, T):
+    """fp64 scaled_dot_product_attention with an explicit mask j <= L - T + t."""
+    rng = np.random.default_rng(7 + T)
+    P = 16
+    lens = [40, T + 3]
+    X, pool, table, lens = _scatter_case(rng, 2, P, 3, lens)
+    q = rng.standard_normal((2, T, Hq, HEAD_DIM))
+    qs, ks, vs = 0.9, 0.25, 3.0
+    got = gqa_decode_paged_reference(q, pool, table, lens, P, qs, ks, vs)
+    for b, L in enumerate(lens):
+        mask = torch.tensor([[j <= L - T + t for j in range(L)] for t in range(T)])
+        sd = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[b]).permute(1, 0, 2).unsqueeze(0),          # [1, Hq, T, D]
+            torch.from_numpy(X[b, 0, :, :L]).unsqueeze(0),                 # [1, 8, L, D]
+            torch.from_numpy(X[b, 1, :, :L]).unsqueeze(0),
+            attn_mask=mask, scale=qs * ks / math.sqrt(HEAD_DIM), enable_gqa=True)
+        want = vs * sd[0].permute(1, 0, 2).numpy()                          # [T, Hq, D]
+        np.testing.assert_allclose(got[b], want, rtol=0, atol=1e-12)
+
+
+def test_causal_rows_match_brute_force():
+    rng = np.random.default_rng(11)
+    B, T, C = 2, 3, 6
+    q = rng.standard_normal((B, T, 32, HEAD_DIM))
+    kv = rng.standard_normal((B, 2, NUM_KV_HEADS, C, HEAD_DIM))
+    lens = [6, 3]
+    got = gqa_decode_multi(q, [kv[b] for b in range(B)], lens, 0.7)
+    for t in range(T):
+        lt = [L - T + 1 + t for L in lens]
+        want = np.array(brute_decode(q[:, t].tolist(), kv.tolist(), lt, 0.7))
+        np.testing.assert_allclose(got[:, t], want, rtol=0, atol=1e-12)
+
+
+def test_identical_keys_give_the_mean_of_each_causal_prefix():
+    rng = np.random.default_rng(13)
+    T, L = 4, 20
+    kv = rng.standard_normal((1, 2, NUM_KV_HEADS, L, HEAD_DIM))
+    kv[0, 0] = kv[0, 0, :, :1]
+    q = rng.standard_normal((1, T, 32, HEAD_DIM))
+    got = gqa_decode_multi(q, [kv[0]], [L])
+    for t in range(T):
+        visible = L - T + 1 + t
+        for h in range(32):
+            np.testing.assert_allclose(got[0, t, h], kv[0, 1, h // 4, :visible].mean(0),
+                                       rtol=0, atol=1e-13)
+
+
+def test_last_token_sees_the_whole_length_and_first_token_one_less_per_step():
+    rng = np.random.default_rng(17)
+    T, L = 3, 30
+    kv = rng.standard_normal((1, 2, NUM_KV_HEADS, L, HEAD_DIM))
+    q = rng.standard_normal((1, T, 32, HEAD_DIM))
+    got = gqa_decode_multi(q, [kv[0]], [L], 1.3)
+    for t in range(T):
+        single = gqa_decode_reference(q[:, t], kv, [L - T + 1 + t], 1.3)
+        np.testing.assert_allclose(got[:, t], single, rtol=0, atol=1e-14)
+    # a token that saw one slot fewer differs (the causal limit matters)
+    assert not np.allclose(got[0, 0], gqa_decode_reference(q[:, 0], kv, [L], 1.3)[0])
+
+
+def test_page_relabelling_and_garbage_outside_the_prefix_do_not_matter():
+    rng = np.random.default_rng(19)
+    P = 32
+    X, pool, table, lens = _scatter_case(rng, 3, P, 3, [70, 33, 96], spare=5)
+    q = rng.standard_normal((3, 2, 16, HEAD_DIM))
+    base = gqa_decode_paged_reference(q, pool, table, lens, P)
+    assert np.all(np.isfinite(base))
+    perm = rng.permutation(pool.shape[0])           # new id of old page i is perm[i]
+    pool2 = np.empty_like(pool)
+    pool2[perm] = pool
+    np.testing.assert_array_equal(gqa_decode_paged_reference(q, pool2, perm[table], lens, P), base)
+    pool3 = pool.copy()                             # NaN past each length inside used pages
+    for b, L in enumerate(lens):
+        for j in range(L, 3 * P):
+            pool3[table[b, j // P], :, :, j % P] = np.nan
+    np.testing.assert_array_equal(gqa_decode_paged_reference(q, pool3, table, lens, P), base)
+
+
+def test_int8_pages_decode_each_row_with_its_own_scale():
+    """Two pages, one token each visible: the output is the V row times its own
+    row scale (int8 * bf16 exact), whichever page the slot sits in."""
+    P = 16
+    vals = np.zeros((2, 2, NUM_KV_HEADS, P, HEAD_DIM), dtype=np.int8)
+    vals[:, 1, :, :, 5] = [[[7] * P] * NUM_KV_HEADS, [[-3] * P] * NUM_KV_HEADS]
+    sbits = np.zeros((2, 2, NUM_KV_HEADS, P), dtype=np.uint16)
+    sbits[0] = np.uint16(0x3F00)   # 0.5
+    sbits[1] = np.uint16(0x4100)   # 8.0
+    pages = decode_int8_rows(vals, sbits)
+    q = np.zeros((2, 1, 32, HEAD_DIM))
+    out = gqa_decode_paged_reference(q, pages, np.array([[1], [0]]), [1, 1], P)
+    assert np.all(out[0, 0, :, 5] == -24.0) and np.all(out[1, 0, :, 5] == 3.5)
+
+
+def test_rejects_impossible_inputs():
+    rng = np.random.default_rng(23)
+    X, pool, table, lens = _scatter_case(rng, 1, 16, 2, [20])
+    q = rng.standard_normal((1, 4, 32, HEAD_DIM))
+    with pytest.raises(ValueError):          # L < T: the first token would see nothing
+        gqa_decode_paged_reference(q, pool, table, [3], 16)
+    with pytest.raises(ValueError):          # table entry outside the pool
+        gqa_decode_paged_reference(q, pool, np.array([[0, pool.shape[0]]]), [20], 16)
+    with pytest.raises(ValueError):          # length beyond max_pages * page_size
+        gqa_decode_paged_reference(q, pool, table, [33], 16)
