@@ -20,7 +20,6 @@ oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -34,7 +33,6 @@ if ROOT not in sys.path:
 METRIC = "GQA decode: achieved KV-read HBM GB/s (% of peak) and µs/call at 1 GPU"
 PEAK_HBM_GBPS = 8000.0
 DEFAULT_WORKLOAD = "gqa_decode_b8_c65536_bf16_long"
-KERNEL_SOURCE = os.path.join(ROOT, "gqa_kv_cache_attn_amd", "csrc", "gqa_kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -55,17 +53,19 @@ def parse_args():
     return ap.parse_args()
 
 
-def algorithmic_bytes(lens, kv_dtype, batch, num_q_heads=32):
+def algorithmic_bytes(lens, kv_dtype, batch, num_q_heads=32, q_tokens=1, page_size=0):
     """Valid K/V prefix bytes (an INT8 cache's bf16 row scales included) + q and
-    out (16-bit) + int32 lengths; no padding, no workspace."""
+    out (16-bit, q_tokens rows per head) + int32 lengths (+ the block-table
+    entries of the pages the prefixes occupy); no padding, no workspace."""
     from gqa_kv_cache_attn_amd.inputs import kv_slot_bytes
-    return (int(sum(lens)) * 8 * kv_slot_bytes(kv_dtype) + batch * num_q_heads * 128 * (2 + 2)
-            + 4 * batch)
+    table = 4 * sum(-(-int(L) // page_size) for L in lens) if page_size else 0
+    return (int(sum(lens)) * 8 * kv_slot_bytes(kv_dtype)
+            + batch * q_tokens * num_q_heads * 128 * (2 + 2) + 4 * batch + table)
 
 
-def kernel_source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_digest(kernel):
+    from gqa_kv_cache_attn_amd.profile_summary import kernel_source_digest as digest
+    return digest(kernel)
 
 
 def read_traffic(kernel, workload, num_splits):
@@ -82,7 +82,7 @@ def read_traffic(kernel, workload, num_splits):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_digest():
+    if kv.get("kernel_source_sha256_16") != kernel_source_digest(kernel):
         return None
     if int(kv.get("num_splits_requested", "0")) != num_splits:
         return None
@@ -90,6 +90,50 @@ def read_traffic(kernel, workload, num_splits):
         return int(float(kv["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def cpu_baseline_paged(inp, w, budget_s):
+    """Time the paged fp64 oracle (as it stands) one request at a time until the budget."""
+    import numpy as np
+
+    from gqa_kv_cache_attn_amd.inputs import kv_slot_bytes, storage_bits
+    from oracle import decode_int8_rows, decode_storage
+    from oracle.paged import gqa_decode_paged_reference
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:   # pragma: no cover - threadpoolctl missing
+        blas_threads = 1
+    lens = inp["seq_lens"].cpu().numpy()
+    P = w.page_size
+    spent, nbytes, done = 0.0, 0, 0
+    for b in range(w.batch):
+        L = int(lens[b])
+        n = -(-L // P)
+        ids = inp["block_table"][b, :n].long()
+        pages = storage_bits(inp["kv_pages"].index_select(0, ids))   # D2H copies are not timed
+        sc = storage_bits(inp["kv_scales"].index_select(0, ids)) if w.kv_dtype == "int8" else None
+        qb = storage_bits(inp["q"][b:b + 1])
+        t0 = time.perf_counter()
+        dec = decode_int8_rows(pages, sc) if sc is not None else decode_storage(pages, w.kv_dtype)
+        out = gqa_decode_paged_reference(decode_storage(qb, w.q_dtype), dec, np.arange(n)[None, :],
+                                         [L], P, w.q_scale, w.k_scale, w.v_scale)
+        spent += time.perf_counter() - t0
+        assert np.all(np.isfinite(out))
+        nbytes += L * 8 * kv_slot_bytes(w.kv_dtype) + w.q_tokens * w.num_q_heads * 128 * 4
+        done += 1
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(nbytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.batch} requests of {w.name}, {nbytes / 1e6:.1f} MB of algorithmic "
+                  f"bytes, {spent:.2f} s (fp64 numpy incl. decoding the stored pages and the "
+                  f"slot-by-slot gather; D2H copy excluded)",
+    }
 
 
 def cpu_baseline(inp, w, budget_s):
@@ -153,7 +197,7 @@ def main():
     import torch
 
     from gqa_kv_cache_attn_amd import binding as b
-    from gqa_kv_cache_attn_amd.inputs import WORKLOADS_BY_NAME, make_inputs
+    from gqa_kv_cache_attn_amd.inputs import WORKLOADS_BY_NAME, make_inputs, make_paged_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -163,11 +207,20 @@ def main():
     arch = torch.cuda.get_device_properties(dev).gcnArchName
     w = WORKLOADS_BY_NAME[args.workload]
     print(f"[bench] device {arch}; workload {w.name}; generating inputs", file=sys.stderr, flush=True)
-    inp = make_inputs(w, device=dev)
+    paged = w.page_size > 0
+    inp = make_paged_inputs(w, device=dev) if paged else make_inputs(w, device=dev)
     lens = inp["seq_lens"].cpu().tolist()
-    nbytes = algorithmic_bytes(lens, w.kv_dtype, w.batch, w.num_q_heads)
+    nbytes = algorithmic_bytes(lens, w.kv_dtype, w.batch, w.num_q_heads, w.q_tokens, w.page_size)
     out = torch.empty_like(inp["q"])
-    if w.kv_dtype == "int8":
+    if paged:
+        if args.fused_combine:
+            print("the paged entry points have no one-launch merge", file=sys.stderr)
+            sys.exit(2)
+        prep = b.prepare_gqa_decode_paged(inp["q"], inp["kv_pages"], inp["block_table"],
+                                          inp["seq_lens"], out, inp["q_scale"],
+                                          num_splits=args.num_splits, k_scale=inp["k_scale"],
+                                          v_scale=inp["v_scale"], kv_scales=inp["kv_scales"])
+    elif w.kv_dtype == "int8":
         prep = b.prepare_gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], out,
                                          inp["q_scale"], num_splits=args.num_splits,
                                          k_scale=inp["k_scale"], v_scale=inp["v_scale"],
@@ -243,7 +296,11 @@ def main():
     del graph
 
     def convenience():
-        if w.kv_dtype == "int8":
+        if paged:
+            b.gqa_decode_paged(inp["q"], inp["kv_pages"], inp["block_table"], inp["seq_lens"],
+                               inp["q_scale"], out, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                               kv_scales=inp["kv_scales"])
+        elif w.kv_dtype == "int8":
             b.gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], inp["q_scale"],
                               out, k_scale=inp["k_scale"], v_scale=inp["v_scale"])
         else:
@@ -264,7 +321,7 @@ def main():
     # slot L_b, past the valid prefix, so the decode inputs are unchanged. An
     # INT8 cache's rows and scales are written by the caller: not timed here.
     append_us = None
-    if w.kv_dtype != "int8":
+    if w.kv_dtype != "int8" and not paged:
         k_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
         v_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
         slots = inp["seq_lens"].clamp(max=w.capacity - 1)
@@ -296,7 +353,10 @@ def main():
     def pct(xs, p):
         return xs[min(len(xs) - 1, int(round(p / 100 * (len(xs) - 1))))] if xs else None
 
-    kernel = "gqa_balanced_attention_kernel" if plan["route"] == 2 else "gqa_attention_kernel"
+    if paged:
+        kernel = "gqa_paged_balanced_kernel" if plan["route"] == 2 else "gqa_paged_attention_kernel"
+    else:
+        kernel = "gqa_balanced_attention_kernel" if plan["route"] == 2 else "gqa_attention_kernel"
     traffic = read_traffic(kernel, w.name, args.num_splits) if not args.fused_combine else None
     result = {
         "metric": METRIC,
@@ -338,7 +398,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_seconds)
+        result["cpu_baseline"] = (cpu_baseline_paged if paged else cpu_baseline)(inp, w,
+                                                                                args.cpu_seconds)
     prep.destroy()
     print(json.dumps(result), flush=True)
 

@@ -50,6 +50,18 @@ class GqaDesc(ctypes.Structure):
     ]
 
 
+class GqaPagedDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("q_tokens", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32), ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float), ("flags", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+    ]
+
+
 class GqaPlan(ctypes.Structure):
     _fields_ = [
         ("route", ctypes.c_int32), ("num_splits", ctypes.c_int32),
@@ -63,6 +75,7 @@ class GqaPlan(ctypes.Structure):
 
 _vp, _i32, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
 _DescP, _PlanP = ctypes.POINTER(GqaDesc), ctypes.POINTER(GqaPlan)
+_PDescP = ctypes.POINTER(GqaPagedDesc)
 
 
 def _sig(name, restype, argtypes):
@@ -86,6 +99,13 @@ _prepare_int8 = _sig("prepare_gqa_decode_int8", ctypes.c_int,
 _validate_int8 = _sig("gqa_validate_args_int8", ctypes.c_int,
                       [_DescP, _vp, _vp, _vp, _vp, _f32, _vp, _i32])
 _plan = _sig("gqa_plan_decode", ctypes.c_int, [_DescP, _i32, _PlanP])
+_decode_paged = _sig("gqa_decode_paged", ctypes.c_int,
+                     [_PDescP, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp])
+_prepare_paged = _sig("prepare_gqa_decode_paged", ctypes.c_int,
+                      [_PDescP, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32, ctypes.POINTER(_vp)])
+_validate_paged = _sig("gqa_validate_args_paged", ctypes.c_int,
+                       [_PDescP, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _i32])
+_plan_paged = _sig("gqa_plan_decode_paged", ctypes.c_int, [_PDescP, _i32, _PlanP])
 _last_error = _sig("gqa_last_error", ctypes.c_char_p, [])
 _append = _sig("gqa_kv_append", ctypes.c_int, [_DescP, _vp, _vp, _vp, _vp, _vp])
 
@@ -283,6 +303,76 @@ def prepare_gqa_decode_int8(q: torch.Tensor, kv: torch.Tensor, kv_scales: torch.
                                  "sequence_lengths": seq_lens, "O": out}, desc)
 
 
+def make_paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.Tensor,
+                    k_scale: float = 1.0, v_scale: float = 1.0) -> GqaPagedDesc:
+    """q [batch, T, Hq, 128]; kv_pages [num_pages, 2, 8, page_size, 128];
+    block_table [batch, max_pages] int32."""
+    if q.dim() != 4 or kv_pages.dim() != 5 or block_table.dim() != 2:
+        raise ValueError("q must be [batch, T, Hq, 128], kv_pages [num_pages, 2, 8, page_size, 128] "
+                         "and block_table [batch, max_pages]")
+    if kv_pages.shape[1] != 2 or block_table.shape[0] != q.shape[0]:
+        raise ValueError(f"bad shapes: q {tuple(q.shape)}, kv_pages {tuple(kv_pages.shape)}, "
+                         f"block_table {tuple(block_table.shape)}")
+    return GqaPagedDesc(batch=q.shape[0], q_tokens=q.shape[1], num_q_heads=q.shape[2],
+                        num_kv_heads=kv_pages.shape[2], head_dim=q.shape[3],
+                        q_dtype=_dtype_code(q, "q"), kv_dtype=_dtype_code(kv_pages, "kv"),
+                        k_scale=k_scale, v_scale=v_scale, flags=0, page_size=kv_pages.shape[3],
+                        num_pages=kv_pages.shape[0], max_pages=block_table.shape[1])
+
+
+def _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out):
+    ts = [q, kv_pages, block_table, seq_lens, out] + ([kv_scales] if kv_scales is not None else [])
+    _check_devices(*ts)
+    if seq_lens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("seq_lens and block_table must be int32")
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q's shape and dtype")
+    if (kv_scales is None) != (kv_pages.dtype != torch.int8):
+        raise ValueError("kv_scales is required for (and only for) an int8 page pool")
+    if kv_scales is not None and (kv_scales.dtype != torch.bfloat16 or
+                                  tuple(kv_scales.shape) != tuple(kv_pages.shape[:4])):
+        raise ValueError(f"kv_scales must be bf16 {tuple(kv_pages.shape[:4])}")
+
+
+def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, q_scale: float = 1.0,
+                     out: Optional[torch.Tensor] = None, k_scale: float = 1.0,
+                     v_scale: float = 1.0, kv_scales: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Decode (T query tokens per request, causal among themselves) over a page pool."""
+    if out is None:
+        out = torch.empty_like(q)
+    _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out)
+    desc = make_paged_desc(q, kv_pages, block_table, k_scale, v_scale)
+    with torch.cuda.device(q.device):
+        st = _decode_paged(ctypes.byref(desc), _ptr(q), _ptr(kv_pages), _ptr(kv_scales),
+                           _ptr(block_table), _ptr(seq_lens), q_scale, _ptr(out),
+                           _stream_handle(stream, q.device))
+    _check(st)
+    return out
+
+
+def prepare_gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.Tensor,
+                             seq_lens: torch.Tensor, out: torch.Tensor, q_scale: float = 1.0,
+                             num_splits: Optional[int] = None, k_scale: float = 1.0,
+                             v_scale: float = 1.0,
+                             kv_scales: Optional[torch.Tensor] = None) -> GqaPrepared:
+    """Prepare a paged decode step (workspace allocated once, outside capture)."""
+    _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out)
+    desc = make_paged_desc(q, kv_pages, block_table, k_scale, v_scale)
+    h = _vp()
+    with torch.cuda.device(q.device):
+        st = _prepare_paged(ctypes.byref(desc), _ptr(q), _ptr(kv_pages), _ptr(kv_scales),
+                            _ptr(block_table), _ptr(seq_lens), q_scale, _ptr(out),
+                            0 if num_splits is None else int(num_splits), ctypes.byref(h))
+    _check(st)
+    tensors = {"Q": q, "KV_pages": kv_pages, "block_table": block_table,
+               "sequence_lengths": seq_lens, "O": out}
+    if kv_scales is not None:
+        tensors["KV_scales"] = kv_scales
+    return GqaPrepared(h.value, tensors, desc)
+
+
 def launch_gqa_decode_prepared(prepared: GqaPrepared, stream=None) -> torch.Tensor:
     """Enqueue the prepared step (no allocation, no host sync); returns O."""
     dev = prepared.out.device
@@ -338,6 +428,20 @@ def gqa_validate_args_int8(desc: GqaDesc, q_ptr: Optional[int], kv_ptr: Optional
     """Host-only validation of an int8-cache call; returns the raw status code."""
     return int(_validate_int8(ctypes.byref(desc), q_ptr, kv_ptr, scales_ptr, lens_ptr, q_scale,
                               out_ptr, num_splits))
+
+
+def gqa_validate_args_paged(desc: GqaPagedDesc, q_ptr, pool_ptr, scales_ptr, table_ptr, lens_ptr,
+                            q_scale: float, out_ptr, num_splits: int = 0) -> int:
+    """Host-only validation of a paged call; returns the raw status code."""
+    return int(_validate_paged(ctypes.byref(desc), q_ptr, pool_ptr, scales_ptr, table_ptr, lens_ptr,
+                               q_scale, out_ptr, num_splits))
+
+
+def gqa_plan_paged(desc: GqaPagedDesc, num_splits: int = 0) -> dict:
+    """Host-only launch plan for a paged descriptor."""
+    p = GqaPlan()
+    _check(_plan_paged(ctypes.byref(desc), num_splits, ctypes.byref(p)))
+    return p.as_dict()
 
 
 def gqa_plan(desc: GqaDesc, num_splits: int = 0) -> dict:

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["gqa_kernels.hip", "gqa_api.hip"]
+SOURCES = ["gqa_kernels.hip", "gqa_paged.hip", "gqa_api.hip"]
 # HBM read-ceiling / copy-calibration kernels (measurement only, separate library).
 PROBE_SOURCES = ["hbm_probe.hip"]
 PROBE_LIB_PATH = os.path.join(PKG_DIR, "libgqa_hbm_probe.so")

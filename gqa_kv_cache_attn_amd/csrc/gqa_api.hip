@@ -44,6 +44,17 @@ gqa_status_t ok() {
   return GQA_OK;
 }
 
+// Paged cache and query tokens (zero-initialised: the contiguous cache with
+// one query token per request).
+struct Paging {
+  bool on = false;
+  int32_t q_tokens = 1;
+  int32_t page_shift = 0;
+  int32_t num_pages = 0;
+  int32_t max_pages = 0;
+  const int32_t* block_table = nullptr;
+};
+
 // Automatic split planning (measured on MI355X: ~1 MiB of K+V per chunk was
 // best for 16-bit and fp8 caches alike; 768 = 256 CUs x 3 resident workgroups).
 constexpr int64_t kChunkBytes = 1 << 20;
@@ -58,12 +69,13 @@ constexpr int kMaxBalancedGrid = 4096;
 std::mutex g_grid_mu;
 std::map<std::pair<int, int>, int> g_grid;
 
-int device_balanced_grid(int dev, const gqa_desc_t* d) {
+int device_balanced_grid(int dev, const gqa_desc_t* d, bool paged) {
   std::lock_guard<std::mutex> lk(g_grid_mu);
-  const std::pair<int, int> key{dev, (d->num_q_heads * 8 + d->q_dtype) * 8 + d->kv_dtype};
+  const std::pair<int, int> key{dev, ((d->num_q_heads * 8 + d->q_dtype) * 8 + d->kv_dtype) * 2 + paged};
   auto it = g_grid.find(key);
   if (it != g_grid.end()) return it->second;
-  const int W = gqa::balanced_grid_size(d->q_dtype, d->kv_dtype, d->num_q_heads);
+  const int W = paged ? gqa::paged_balanced_grid_size(d->q_dtype, d->kv_dtype, d->num_q_heads)
+                      : gqa::balanced_grid_size(d->q_dtype, d->kv_dtype, d->num_q_heads);
   g_grid.emplace(key, W);
   return W;
 }
@@ -115,9 +127,10 @@ gqa_status_t check_desc(const gqa_desc_t* d) {
 }
 
 // Workspace: part_o [R,128] f32 | part_ml [R,2] f32 | aux int32 array, where R
-// is the number of partial rows: chunked split R = B*Hq*S (head-major), aux =
-// per-(request, KV head) counters [B*8] (fused merge only); balanced split
-// R = 2G*4 (two slots per workgroup, 4 query rows each), aux = slab prefix [B+1].
+// is the number of partial rows: chunked split R = B*T*Hq*S (query-row-major;
+// T = 1 for the contiguous cache), aux = per-(request, KV head) counters
+// [B*8] (fused merge only); balanced split R = 2W*4 (two slots per
+// workgroup, 4 query rows each; 16 for the paged cache), aux = slab prefix [B+1].
 struct WorkspaceLayout {
   uint64_t ml_offset, aux_offset, total;
 };
@@ -130,16 +143,19 @@ WorkspaceLayout workspace_layout(uint64_t rows, uint64_t aux_ints) {
   return w;
 }
 
-WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p) {
+WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p, const Paging& pg) {
   if (p.route == 2)
-    return workspace_layout(2ull * (uint64_t)p.num_workgroups * 4, (uint64_t)d->batch + 1);
-  return workspace_layout((uint64_t)d->batch * (uint64_t)d->num_q_heads * (uint64_t)p.num_splits,
+    return workspace_layout(2ull * (uint64_t)p.num_workgroups * (pg.on ? gqa::kPagedSlotRows : 4),
+                            (uint64_t)d->batch + 1);
+  return workspace_layout((uint64_t)d->batch * (uint64_t)pg.q_tokens * (uint64_t)d->num_q_heads *
+                              (uint64_t)p.num_splits,
                           (uint64_t)d->batch * GQA_NUM_KV_HEADS);
 }
 
 // grid_wgs: resident workgroups of the balanced kernel on the target device
 // (0: the nominal kNominalBalancedGrid, for host-only planning).
-gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, int grid_wgs = 0) {
+gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, int grid_wgs = 0,
+                       const Paging& pg = Paging()) {
   const int64_t C = d->capacity;
   if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", num_splits);
   const int64_t slabs_per_head = (C + 63) / 64;
@@ -154,7 +170,7 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, i
     p->num_splits = 0;
     p->chunk_tokens = 64;
     p->num_workgroups = G;
-    p->workspace_bytes = d->batch > 0 ? plan_layout(d, *p).total : 0;
+    p->workspace_bytes = d->batch > 0 ? plan_layout(d, *p, pg).total : 0;
     return GQA_OK;
   }
   const int64_t granules = (C + GQA_CHUNK_GRANULE - 1) / GQA_CHUNK_GRANULE;
@@ -196,7 +212,7 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, i
   p->num_splits = (int32_t)S;
   p->chunk_tokens = (int32_t)chunk;
   p->num_workgroups = (int32_t)wgs;
-  p->workspace_bytes = S > 1 ? plan_layout(d, *p).total : 0;
+  p->workspace_bytes = S > 1 ? plan_layout(d, *p, pg).total : 0;
   return GQA_OK;
 }
 
@@ -266,7 +282,7 @@ gqa_status_t check_device(int* dev_out) {
 
 gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, const void* scales,
                         const int32_t* lens, float q_scale, void* out, const gqa_plan_t& p,
-                        void* ws) {
+                        void* ws, const Paging& pg) {
   gqa::StepArgs a;
   a.q = q;
   a.kv = kv;
@@ -274,7 +290,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.num_q_heads = d->num_q_heads;
   a.seq_lens = lens;
   a.out = out;
-  const WorkspaceLayout wl = plan_layout(d, p);
+  const WorkspaceLayout wl = plan_layout(d, p, pg);
   char* base = static_cast<char*>(ws);
   a.part_o = ws ? reinterpret_cast<float*>(base) : nullptr;
   a.part_ml = ws ? reinterpret_cast<float*>(base + wl.ml_offset) : nullptr;
@@ -291,12 +307,18 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
                        std::log(2.0);
   a.scale_log2 = (float)scale;
   a.v_scale = d->v_scale;
+  a.block_table = pg.block_table;
+  a.max_pages = pg.max_pages;
+  a.page_shift = pg.page_shift;
+  a.num_pages = pg.num_pages;
+  a.q_tokens = pg.q_tokens;
   return a;
 }
 
-gqa_status_t enqueue(const gqa::StepArgs& a, const gqa_desc_t* d, hipStream_t stream,
+gqa_status_t enqueue(const gqa::StepArgs& a, const gqa_desc_t* d, bool paged, hipStream_t stream,
                      hipEvent_t ev_mid = nullptr) {
-  hipError_t e = gqa::enqueue_decode_step(a, d->q_dtype, d->kv_dtype, stream, ev_mid);
+  hipError_t e = paged ? gqa::enqueue_paged_decode_step(a, d->q_dtype, d->kv_dtype, stream, ev_mid)
+                       : gqa::enqueue_decode_step(a, d->q_dtype, d->kv_dtype, stream, ev_mid);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -322,36 +344,24 @@ struct gqa_prepared {
   float q_scale;
   void* workspace;
   int device;
+  Paging pg;               // paged cache / several query tokens
 };
 
 namespace {
 
-gqa_status_t validate_impl(const gqa_desc_t* desc, const void* q, const void* kv,
-                           const void* scales, bool with_scales, const int32_t* seq_lens,
-                           float q_scale, const void* out, int32_t num_splits) {
-  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
-  if (st != GQA_OK) return st;
+// The steps after argument checking, shared by the contiguous and the paged
+// entry points (pg: paging and query tokens; default = contiguous, one token).
+gqa_status_t prepare_checked(const gqa_desc_t* desc, const void* q, const void* kv,
+                             const void* scales, const int32_t* seq_lens, float q_scale, void* out,
+                             int32_t num_splits, const Paging& pg, gqa_prepared_t** handle) {
   gqa_plan_t p;
-  st = make_plan(desc, num_splits, &p);
-  if (st != GQA_OK) return st;
-  return ok();
-}
-
-gqa_status_t prepare_impl(const gqa_desc_t* desc, const void* q, const void* kv,
-                          const void* scales, bool with_scales, const int32_t* seq_lens,
-                          float q_scale, void* out, int32_t num_splits, gqa_prepared_t** handle) {
-  if (handle == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
-  *handle = nullptr;
-  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
-  if (st != GQA_OK) return st;
-  gqa_plan_t p;
-  st = make_plan(desc, num_splits, &p);
+  gqa_status_t st = make_plan(desc, num_splits, &p, 0, pg);
   if (st != GQA_OK) return st;
   int dev = -1;
   st = check_device(&dev);
   if (st != GQA_OK) return st;
   if (p.route == 2) {   // size the balanced grid for this device
-    st = make_plan(desc, num_splits, &p, device_balanced_grid(dev, desc));
+    st = make_plan(desc, num_splits, &p, device_balanced_grid(dev, desc, pg.on), pg);
     if (st != GQA_OK) return st;
   }
   void* ws = nullptr;
@@ -384,24 +394,23 @@ gqa_status_t prepare_impl(const gqa_desc_t* desc, const void* q, const void* kv,
   h->q_scale = q_scale;
   h->workspace = ws;
   h->device = dev;
+  h->pg = pg;
   *handle = h;
   return ok();
 }
 
-gqa_status_t decode_impl(const gqa_desc_t* desc, const void* q, const void* kv,
-                         const void* scales, bool with_scales, const int32_t* seq_lens,
-                         float q_scale, void* out, hipStream_t stream) {
-  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
-  if (st != GQA_OK) return st;
+gqa_status_t decode_checked(const gqa_desc_t* desc, const void* q, const void* kv,
+                            const void* scales, const int32_t* seq_lens, float q_scale, void* out,
+                            const Paging& pg, hipStream_t stream) {
   gqa_plan_t p;
-  st = make_plan(desc, 0, &p);
+  gqa_status_t st = make_plan(desc, 0, &p, 0, pg);
   if (st != GQA_OK) return st;
   if (desc->batch == 0) return ok();
   int dev = -1;
   st = check_device(&dev);
   if (st != GQA_OK) return st;
   if (p.route == 2) {
-    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc));
+    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc, pg.on), pg);
     if (st != GQA_OK) return st;
   }
 
@@ -418,8 +427,8 @@ gqa_status_t decode_impl(const gqa_desc_t* desc, const void* q, const void* kv,
       }
       if (cs != hipStreamCaptureStatusNone)
         return fail(GQA_ERR_CAPTURE,
-                    "gqa_decode would allocate %llu workspace bytes while the stream is "
-                    "capturing; use prepare_gqa_decode/launch_gqa_decode_prepared",
+                    "the convenience call would allocate %llu workspace bytes while the stream "
+                    "is capturing; use the prepare / launch_gqa_decode_prepared pair",
                     (unsigned long long)p.workspace_bytes);
       if (ce.ptr) {
         // Work already enqueued on this stream may still use the old buffer.
@@ -447,7 +456,115 @@ gqa_status_t decode_impl(const gqa_desc_t* desc, const void* q, const void* kv,
     }
     ws = ce.ptr;
   }
-  return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws), desc, stream);
+  return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws, pg), desc, pg.on,
+                 stream);
+}
+
+gqa_status_t validate_impl(const gqa_desc_t* desc, const void* q, const void* kv,
+                           const void* scales, bool with_scales, const int32_t* seq_lens,
+                           float q_scale, const void* out, int32_t num_splits) {
+  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
+  if (st != GQA_OK) return st;
+  gqa_plan_t p;
+  st = make_plan(desc, num_splits, &p);
+  if (st != GQA_OK) return st;
+  return ok();
+}
+
+gqa_status_t prepare_impl(const gqa_desc_t* desc, const void* q, const void* kv,
+                          const void* scales, bool with_scales, const int32_t* seq_lens,
+                          float q_scale, void* out, int32_t num_splits, gqa_prepared_t** handle) {
+  if (handle == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  *handle = nullptr;
+  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
+  if (st != GQA_OK) return st;
+  return prepare_checked(desc, q, kv, scales, seq_lens, q_scale, out, num_splits, Paging(), handle);
+}
+
+gqa_status_t decode_impl(const gqa_desc_t* desc, const void* q, const void* kv,
+                         const void* scales, bool with_scales, const int32_t* seq_lens,
+                         float q_scale, void* out, hipStream_t stream) {
+  gqa_status_t st = check_args(desc, q, kv, scales, with_scales, seq_lens, q_scale, out);
+  if (st != GQA_OK) return st;
+  return decode_checked(desc, q, kv, scales, seq_lens, q_scale, out, Paging(), stream);
+}
+
+// --- paged cache ---------------------------------------------------------------
+// Checks a paged descriptor and its buffers; on success fills the equivalent
+// contiguous descriptor (capacity = max_pages * page_size, the longest length
+// a block-table row can address) and the paging record.
+gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const void* pool,
+                              const void* scales, const int32_t* table, const int32_t* lens,
+                              float q_scale, const void* out, gqa_desc_t* d, Paging* pg) {
+  if (pd == nullptr) return fail(GQA_ERR_INVALID_ARG, "desc is NULL");
+  const int P = pd->page_size;
+  if (P < 16 || P > GQA_MAX_PAGE_SIZE || (P & (P - 1)) != 0)
+    return fail(GQA_ERR_INVALID_ARG, "page_size must be a power of two in [16, %d] (got %d)",
+                GQA_MAX_PAGE_SIZE, P);
+  if (pd->num_pages < 1 || pd->max_pages < 1)
+    return fail(GQA_ERR_INVALID_ARG, "num_pages and max_pages must be >= 1 (got %d, %d)",
+                pd->num_pages, pd->max_pages);
+  if ((int64_t)pd->max_pages * P > GQA_MAX_CAPACITY)
+    return fail(GQA_ERR_INVALID_ARG, "max_pages * page_size must be <= %d (got %lld)",
+                GQA_MAX_CAPACITY, (long long)pd->max_pages * P);
+  if (pd->flags != 0)
+    return fail(GQA_ERR_INVALID_ARG, "the paged entry points take no flags (got 0x%x)",
+                (unsigned)pd->flags);
+  *d = gqa_desc_t{};
+  d->batch = pd->batch;
+  d->capacity = pd->max_pages * P;
+  d->num_q_heads = pd->num_q_heads;
+  d->num_kv_heads = pd->num_kv_heads;
+  d->head_dim = pd->head_dim;
+  d->q_dtype = pd->q_dtype;
+  d->kv_dtype = pd->kv_dtype;
+  d->k_scale = pd->k_scale;
+  d->v_scale = pd->v_scale;
+  d->flags = 0;
+  gqa_status_t st = check_desc(d);
+  if (st != GQA_OK) return st;
+  const int group = pd->num_q_heads / GQA_NUM_KV_HEADS;
+  if (pd->q_tokens < 1 || pd->q_tokens * group > GQA_PAGED_MAX_ROWS)
+    return fail(GQA_ERR_INVALID_ARG,
+                "q_tokens must be in [1, %d] for %d query heads (q_tokens x query heads per KV "
+                "head <= %d; got %d)",
+                GQA_PAGED_MAX_ROWS / group, pd->num_q_heads, GQA_PAGED_MAX_ROWS, pd->q_tokens);
+  if (!scale_ok(q_scale))
+    return fail(GQA_ERR_INVALID_ARG, "q_scale must be finite and > 0 (got %g)", (double)q_scale);
+  const bool int8 = pd->kv_dtype == GQA_INT8_ROWSCALE;
+  pg->on = true;
+  pg->q_tokens = pd->q_tokens;
+  pg->page_shift = __builtin_ctz((unsigned)P);
+  pg->num_pages = pd->num_pages;
+  pg->max_pages = pd->max_pages;
+  pg->block_table = table;
+  if (pd->batch == 0) return GQA_OK;
+  if (!q || !pool || !table || !lens || !out || (int8 && !scales))
+    return fail(GQA_ERR_INVALID_ARG, int8 ? "q, kv_pages, kv_scales, block_table, seq_lens and out "
+                                            "must be non-NULL"
+                                          : "q, kv_pages, block_table, seq_lens and out must be "
+                                            "non-NULL");
+  if (!int8 && scales)
+    return fail(GQA_ERR_INVALID_ARG, "kv_scales must be NULL unless the cache is INT8_ROWSCALE");
+  if (!aligned(q, 16) || !aligned(pool, 16) || !aligned(out, 16) || !aligned(table, 4) ||
+      !aligned(lens, 4) || (int8 && !aligned(scales, 16)))
+    return fail(GQA_ERR_INVALID_ARG,
+                "q, kv_pages, kv_scales and out must be 16-byte aligned, block_table and "
+                "seq_lens 4-byte aligned");
+  const size_t B = (size_t)pd->batch;
+  const size_t q_bytes =
+      B * (size_t)pd->q_tokens * (size_t)pd->num_q_heads * GQA_HEAD_DIM * elem_bytes(pd->q_dtype);
+  const size_t rows = (size_t)pd->num_pages * 2 * GQA_NUM_KV_HEADS * (size_t)P;
+  const size_t pool_bytes = rows * GQA_HEAD_DIM * elem_bytes(pd->kv_dtype);
+  const size_t sc_bytes = int8 ? rows * 2 : 0;
+  const size_t table_bytes = B * (size_t)pd->max_pages * sizeof(int32_t);
+  if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, pool, pool_bytes) ||
+      ranges_overlap(out, q_bytes, lens, B * sizeof(int32_t)) ||
+      ranges_overlap(out, q_bytes, table, table_bytes) ||
+      (int8 && ranges_overlap(out, q_bytes, scales, sc_bytes)))
+    return fail(GQA_ERR_ALIAS,
+                "out must not overlap q, kv_pages, kv_scales, block_table or seq_lens");
+  return GQA_OK;
 }
 
 }  // namespace
@@ -505,8 +622,8 @@ GQA_API gqa_status_t launch_gqa_decode_prepared_timed(gqa_prepared_t* h, hipStre
     st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
   if (st == GQA_OK) {
     const gqa::StepArgs a = step_args(&h->desc, h->q, h->kv, h->kv_scales, h->seq_lens, h->q_scale,
-                                      h->out, h->plan, h->workspace);
-    st = enqueue(a, &h->desc, stream, ev_mid);
+                                      h->out, h->plan, h->workspace, h->pg);
+    st = enqueue(a, &h->desc, h->pg.on, stream, ev_mid);
   }
   if (st == GQA_OK && ev_end != nullptr && (e = hipEventRecord(ev_end, stream)) != hipSuccess)
     st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
@@ -544,6 +661,67 @@ GQA_API gqa_status_t gqa_decode_int8(const gqa_desc_t* desc, const void* q, cons
                                      const void* kv_scales, const int32_t* seq_lens,
                                      float q_scale, void* out, hipStream_t stream) {
   return decode_impl(desc, q, kv, kv_scales, true, seq_lens, q_scale, out, stream);
+}
+
+GQA_API gqa_status_t gqa_validate_args_paged(const gqa_paged_desc_t* desc, const void* q,
+                                             const void* kv_pages, const void* kv_scales,
+                                             const int32_t* block_table, const int32_t* seq_lens,
+                                             float q_scale, const void* out, int32_t num_splits) {
+  gqa_desc_t d;
+  Paging pg;
+  gqa_status_t st = check_paged_args(desc, q, kv_pages, kv_scales, block_table, seq_lens, q_scale,
+                                     out, &d, &pg);
+  if (st != GQA_OK) return st;
+  gqa_plan_t p;
+  st = make_plan(&d, num_splits, &p, 0, pg);
+  if (st != GQA_OK) return st;
+  return ok();
+}
+
+GQA_API gqa_status_t gqa_plan_decode_paged(const gqa_paged_desc_t* desc, int32_t num_splits,
+                                           gqa_plan_t* plan) {
+  if (plan == nullptr) return fail(GQA_ERR_INVALID_ARG, "plan is NULL");
+  gqa_desc_t d;
+  Paging pg;
+  // Descriptor checks only: with batch 0 no buffer is looked at.
+  gqa_paged_desc_t probe = desc ? *desc : gqa_paged_desc_t{};
+  const int32_t batch = probe.batch;
+  probe.batch = 0;
+  gqa_status_t st = check_paged_args(desc ? &probe : nullptr, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, 1.0f, nullptr, &d, &pg);
+  if (st != GQA_OK) return st;
+  if (batch < 0) return fail(GQA_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  d.batch = batch;
+  st = make_plan(&d, num_splits, plan, 0, pg);
+  if (st != GQA_OK) return st;
+  return ok();
+}
+
+GQA_API gqa_status_t prepare_gqa_decode_paged(const gqa_paged_desc_t* desc, const void* q,
+                                              const void* kv_pages, const void* kv_scales,
+                                              const int32_t* block_table, const int32_t* seq_lens,
+                                              float q_scale, void* out, int32_t num_splits,
+                                              gqa_prepared_t** handle) {
+  if (handle == nullptr) return fail(GQA_ERR_INVALID_ARG, "handle is NULL");
+  *handle = nullptr;
+  gqa_desc_t d;
+  Paging pg;
+  gqa_status_t st = check_paged_args(desc, q, kv_pages, kv_scales, block_table, seq_lens, q_scale,
+                                     out, &d, &pg);
+  if (st != GQA_OK) return st;
+  return prepare_checked(&d, q, kv_pages, kv_scales, seq_lens, q_scale, out, num_splits, pg, handle);
+}
+
+GQA_API gqa_status_t gqa_decode_paged(const gqa_paged_desc_t* desc, const void* q,
+                                      const void* kv_pages, const void* kv_scales,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      float q_scale, void* out, hipStream_t stream) {
+  gqa_desc_t d;
+  Paging pg;
+  gqa_status_t st = check_paged_args(desc, q, kv_pages, kv_scales, block_table, seq_lens, q_scale,
+                                     out, &d, &pg);
+  if (st != GQA_OK) return st;
+  return decode_checked(&d, q, kv_pages, kv_scales, seq_lens, q_scale, out, pg, stream);
 }
 
 GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,

@@ -33,6 +33,13 @@ struct StepArgs {
   float v_scale;
   int32_t fused_combine;     // 1: last workgroup of a head combines; 0: separate combine kernel
   int32_t grid_wgs;          // > 0: balanced split with this many persistent workgroups
+  // Paged cache (gqa_paged.hip only; kv then is the page pool
+  // [num_pages, 2, 8, page_size, 128] and kv_scales [num_pages, 2, 8, page_size]).
+  const int32_t* block_table;  // [batch, max_pages]: page of each request's page-sized run of slots
+  int32_t max_pages;
+  int32_t page_shift;        // log2(page_size)
+  int32_t num_pages;
+  int32_t q_tokens;          // T query tokens per request (q, out: [batch, T, Hq, 128]); 1 otherwise
 };
 
 // Arguments of one KV append (one new token per request).
@@ -58,5 +65,12 @@ int balanced_grid_size(int q_dtype, int kv_dtype, int num_q_heads);
 // `ev_mid` is recorded between the two kernels (or after the only one).
 hipError_t enqueue_decode_step(const StepArgs& args, int q_dtype, int kv_dtype,
                                hipStream_t stream, hipEvent_t ev_mid = nullptr);
+
+// Paged cache, T query tokens per request (gqa_paged.hip). The balanced split
+// keeps 16 partial rows per slot (kPagedSlotRows).
+constexpr int kPagedSlotRows = 16;
+int paged_balanced_grid_size(int q_dtype, int kv_dtype, int num_q_heads);
+hipError_t enqueue_paged_decode_step(const StepArgs& args, int q_dtype, int kv_dtype,
+                                     hipStream_t stream, hipEvent_t ev_mid = nullptr);
 
 }  // namespace gqa

@@ -46,453 +46,11 @@
 
 #include <type_traits>
 
+#include "gqa_device.h"
 #include "gqa_kernels.h"
 
 namespace gqa {
 namespace {
-
-constexpr int kHeadDim = 128;
-constexpr int kKvHeads = 8;
-constexpr int kGroup = 4;               // MFMA rows carried per KV head (G <= 4 are real)
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 16;               // tokens per wave step
-constexpr int kStep = kTile * kWaves;   // tokens per workgroup step
-constexpr int kSlab = kStep;            // unit of work of the balanced split
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
-
-// Build-time tuning knobs (defaults are the measured best on MI355X).
-#ifndef GQA_MIN_WAVES_PER_SIMD
-#define GQA_MIN_WAVES_PER_SIMD 2
-#endif
-#ifndef GQA_BALANCED_MIN_WAVES_PER_SIMD
-#define GQA_BALANCED_MIN_WAVES_PER_SIMD 2
-#endif
-#ifndef GQA_KV_LOAD_POLICY
-#define GQA_KV_LOAD_POLICY 2   // cache-policy bits of the K/V loads: 2 = non-temporal
-#endif
-constexpr int kLoadAux = GQA_KV_LOAD_POLICY;
-
-typedef uint32_t u32;
-typedef u32 u32x4 __attribute__((ext_vector_type(4)));
-typedef u32 u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------------------
-// Element-type traits for the MFMA operand type (= query dtype).
-// ---------------------------------------------------------------------------
-template <int QT>
-struct Elem;
-
-template <>
-struct Elem<kBF16> {
-  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
-                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 pv(u32x2 p, u32x2 v, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, p),
-                                                     __builtin_bit_cast(i16x4, v), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ u32 pack(float a, float b) {
-    bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(u32, v);
-  }
-  static __device__ __forceinline__ float lo(u32 x) { return __uint_as_float(x << 16); }
-  static __device__ __forceinline__ float hi(u32 x) { return __uint_as_float(x & 0xffff0000u); }
-  // Two e4m3 codes (bytes 2*sel, 2*sel+1 of x) -> two bf16 (exact).
-  template <bool kHiWord>
-  static __device__ __forceinline__ u32 from_fp8(u32 x) {
-    return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, kHiWord));
-  }
-  // Two signed int8 values (bytes 2*sel, 2*sel+1 of x) -> two bf16 (exact).
-  template <bool kHiWord>
-  static __device__ __forceinline__ u32 from_i8(u32 x) {
-    return pack((float)(signed char)(x >> (kHiWord ? 16 : 0)),
-                (float)(signed char)(x >> (kHiWord ? 24 : 8)));
-  }
-  static __device__ __forceinline__ void store2(void* p, float a, float b) {
-    *reinterpret_cast<u32*>(p) = pack(a, b);
-  }
-};
-
-template <>
-struct Elem<kF16> {
-  static __device__ __forceinline__ f32x4 qk(u32x4 k, u32x4 q, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
-                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ f32x4 pv(u32x2 p, u32x2 v, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, p),
-                                                 __builtin_bit_cast(f16x4, v), c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ u32 pack(float a, float b) {
-    f16x2 v = {(_Float16)a, (_Float16)b};
-    return __builtin_bit_cast(u32, v);
-  }
-  static __device__ __forceinline__ float lo(u32 x) {
-    return (float)__builtin_bit_cast(f16x2, x)[0];
-  }
-  static __device__ __forceinline__ float hi(u32 x) {
-    return (float)__builtin_bit_cast(f16x2, x)[1];
-  }
-  template <bool kHiWord>
-  static __device__ __forceinline__ u32 from_fp8(u32 x) {
-    return __builtin_bit_cast(u32, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, kHiWord));
-  }
-  template <bool kHiWord>
-  static __device__ __forceinline__ u32 from_i8(u32 x) {
-    return pack((float)(signed char)(x >> (kHiWord ? 16 : 0)),
-                (float)(signed char)(x >> (kHiWord ? 24 : 8)));
-  }
-  static __device__ __forceinline__ void store2(void* p, float a, float b) {
-    *reinterpret_cast<u32*>(p) = pack(a, b);
-  }
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, u32 bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Dim-block (8 dims) that lane group `grp` feeds to QK instruction `i`.
-// 16-bit cache: block 4i+grp.
-// byte cache:   the lane's 16-byte chunk 4p+grp of a K row holds blocks
-//               8p + 2grp + {0,1}, fed to instructions 2p and 2p+1.
-// One-byte caches (fp8 e4m3, int8 with row scales) share the row layout and
-// the load/stage/widen path; only the widening and the row scales differ.
-template <int KVT>
-constexpr bool kByteKv = KVT == kFP8 || KVT == kI8;
-
-template <int KVT>
-__device__ __forceinline__ int qk_dim_block(int i, int grp) {
-  if constexpr (kByteKv<KVT>) {
-    return 8 * (i >> 1) + 2 * grp + (i & 1);
-  } else {
-    return 4 * i + grp;
-  }
-}
-
-// Registers of one 16-token tile, as loaded. Every load instruction reads
-// whole cache rows (K and V alike): a 16-bit row is 256 bytes = 16 lanes x 16
-// bytes, an fp8 row 128 bytes = 8 lanes x 16 bytes (K) or 16 lanes x 8 bytes (V).
-template <int KVT>
-struct Tile;
-
-template <>
-struct Tile<kF16> {
-  u32x4 k[4];  // K: token 4grp+e, 16-byte chunk n16 (dims [8 n16, 8 n16 + 8))
-  u32x4 v[4];  // V: token 4grp+e, dims [8 n16, 8 n16 + 8)
-};
-template <>
-struct Tile<kBF16> : Tile<kF16> {};
-template <>
-struct Tile<kFP8> {
-  u32x4 k[2];  // K: token 8u + lane/8, 16-byte chunk lane%8
-  u32x2 v[4];  // V: token 4grp+e, dims [8 n16, 8 n16 + 8)
-};
-template <>
-struct Tile<kI8> : Tile<kFP8> {
-  u32x2 ks;    // bf16 K row scales of tokens 4grp .. 4grp+3
-  u32x2 vs;    // bf16 V row scales of the same tokens
-};
-
-// Buffer resources of the (request, KV head) planes a workgroup reads; each
-// ends at the range's last slot c1, so loads past it read 0 and cost nothing.
-struct Planes {
-  __amdgpu_buffer_rsrc_t k, v;    // K and V rows
-  __amdgpu_buffer_rsrc_t ks, vs;  // bf16 row scales (INT8 cache only)
-  int c1;                         // slots in range
-  bool quads;                     // scale planes 8-byte aligned (capacity % 4 == 0)
-};
-
-// Four consecutive bf16 row scales from slot `tok` (a multiple of 4) on;
-// slots at or past c1 read 0. A quad that straddles c1, or any quad of a
-// plane that is not 8-byte aligned, is read one scale at a time, so no load
-// reaches past the range's end whatever the hardware's range-check
-// granularity, and none is misaligned.
-__device__ __forceinline__ u32x2 load_scale_quad(__amdgpu_buffer_rsrc_t r, int tok, int c1,
-                                                 bool quads) {
-  if (quads && (tok + 4 <= c1 || tok >= c1))
-    return __builtin_amdgcn_raw_buffer_load_b64(r, tok * 2, 0, 0);
-  u32 h[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] = __builtin_amdgcn_raw_buffer_load_b16(r, (tok + i) * 2, 0, 0);
-  return (u32x2){h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-}
-
-template <int KVT>
-__device__ __forceinline__ void load_tile(Tile<KVT>& t, const Planes& pl, int j0, int lane) {
-  const int n16 = lane & 15, grp = lane >> 4;
-  const __amdgpu_buffer_rsrc_t rk = pl.k, rv = pl.v;
-  if constexpr (kByteKv<KVT>) {
-    const int ko = (j0 + (lane >> 3)) * kHeadDim + 16 * (lane & 7);
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      t.k[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + u * 8 * kHeadDim, 0, kLoadAux);
-    const int vo = (j0 + 4 * grp) * kHeadDim + 8 * n16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      t.v[e] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + e * kHeadDim, 0, kLoadAux);
-    if constexpr (KVT == kI8) {
-      t.ks = load_scale_quad(pl.ks, j0 + 4 * grp, pl.c1, pl.quads);
-      t.vs = load_scale_quad(pl.vs, j0 + 4 * grp, pl.c1, pl.quads);
-    }
-  } else {
-    const int ko = (j0 + 4 * grp) * (2 * kHeadDim) + 16 * n16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      t.k[e] = __builtin_amdgcn_raw_buffer_load_b128(rk, ko + e * (2 * kHeadDim), 0, kLoadAux);
-    const int vo = ko;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      t.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + e * (2 * kHeadDim), 0, kLoadAux);
-  }
-}
-
-// The QK product wants K with one token per lane (lane n16 = token, 8 dims
-// per lane), the opposite of the row-per-16-lanes layout the coalesced loads
-// deliver. The wave passes its K tile through its own LDS slice: token t's
-// 16-byte chunk c is stored at slot c ^ f(t) of row t, with f(t) = t for
-// 16-bit rows (16 chunks) and f(t) = (t >> 1) & 7 for fp8 rows (8 chunks), so
-// both the stores (16 lanes = one row) and the loads (16 lanes = 16 rows, one
-// chunk each) hit 16 distinct 16-byte bank groups.
-constexpr int kKStageSlots = 16 * 16;  // 16-byte slots per wave (one 16-bit tile)
-// Running state of one wave.
-struct Softmax {
-  float m;      // running max of log2-domain scores of row n16 (uniform per row)
-  float l;      // this lane's share of the running sum
-  f32x4 o[8];   // O[row 4grp+r][dim 8 n16 + c] in o[c][r] (rows 0..3 live in grp 0)
-};
-
-// Two one-byte cache values (bytes 2*sel, 2*sel+1 of x) -> two MFMA operands
-// of type T.
-template <int T, int KVT, bool kHiWord>
-__device__ __forceinline__ u32 widen(u32 x) {
-  if constexpr (KVT == kFP8) {
-    return Elem<T>::template from_fp8<kHiWord>(x);
-  } else {
-    return Elem<T>::template from_i8<kHiWord>(x);
-  }
-}
-
-// Operand type of the PV product. An INT8 cache multiplies each weight by its
-// token's V row scale, whose range is not f16's, so its weights (and V) go in
-// as bf16 hi + lo pairs whatever the query dtype; otherwise the query dtype.
-template <int QT, int KVT>
-constexpr int kPvType = KVT == kI8 ? (int)kBF16 : QT;
-
-template <int QT, int KVT, int G>
-__device__ __forceinline__ void process_tile(Softmax& st, const Tile<KVT>& t, const u32x4 (&qf)[4],
-                                             u32x4* sk, int j0, int c1, int lane, float scale_log2) {
-  using E = Elem<QT>;
-  constexpr int PT = kPvType<QT, KVT>;
-  using P = Elem<PT>;
-  using B16 = Elem<kBF16>;   // row scales are bf16 whatever the query dtype
-  const int n16 = lane & 15, grp = lane >> 4;
-  // ---- scores^T[token 4grp + r][row n16] ------------------------------------
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (kByteKv<KVT>) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int tok = 8 * u + (lane >> 3);
-      sk[tok * 8 + ((lane & 7) ^ ((tok >> 1) & 7))] = t.k[u];
-    }
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const u32x4 k16 = sk[n16 * 8 + ((4 * p + grp) ^ ((n16 >> 1) & 7))];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32 w0 = k16[2 * h], w1 = k16[2 * h + 1];
-        u32x4 kk = {widen<QT, KVT, false>(w0), widen<QT, KVT, true>(w0),
-                    widen<QT, KVT, false>(w1), widen<QT, KVT, true>(w1)};
-        s = E::qk(kk, qf[2 * p + h], s);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tok = 4 * grp + e;
-      sk[tok * 16 + (n16 ^ tok)] = t.k[e];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s = E::qk(sk[n16 * 16 + ((4 * i + grp) ^ n16)], qf[i], s);
-  }
-
-  // ---- online softmax, log2 domain -----------------------------------------
-  float x[4];
-  const int tok0 = j0 + 4 * grp;
-  if constexpr (KVT == kI8) {   // K row scale of each token multiplies its score
-    s[0] *= B16::lo(t.ks[0]);
-    s[1] *= B16::hi(t.ks[0]);
-    s[2] *= B16::lo(t.ks[1]);
-    s[3] *= B16::hi(t.ks[1]);
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) x[r] = (tok0 + r < c1) ? s[r] * scale_log2 : -INFINITY;
-  float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);   // finite: the tile holds >= 1 valid token
-  const float alpha = fast_exp2(st.m - m_new);
-  float p[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[r] - m_new);
-  // Weights the PV product sees: with an INT8 cache, each token's V row scale
-  // multiplies its weight (l still sums the plain weights).
-  float pw[4] = {p[0], p[1], p[2], p[3]};
-  if constexpr (KVT == kI8) {
-    pw[0] *= B16::lo(t.vs[0]);
-    pw[1] *= B16::hi(t.vs[0]);
-    pw[2] *= B16::lo(t.vs[1]);
-    pw[3] *= B16::hi(t.vs[1]);
-  }
-  const u32 p01 = P::pack(pw[0], pw[1]);
-  const u32 p23 = P::pack(pw[2], pw[3]);
-  // bf16 keeps 8 significant bits of a weight; the PV product then takes the
-  // weights as hi + lo bf16 pairs (16 bits), so only fp32 rounding is left and
-  // l sums the fp32 weights. f16 weights (11 bits) go in one piece and l sums
-  // the rounded weights the product sees.
-  u32 q01 = 0u, q23 = 0u;
-  if constexpr (PT == kBF16) {
-    q01 = P::pack(pw[0] - P::lo(p01), pw[1] - P::hi(p01));
-    q23 = P::pack(pw[2] - P::lo(p23), pw[3] - P::hi(p23));
-    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  } else {
-    st.l = st.l * alpha + ((P::lo(p01) + P::hi(p01)) + (P::lo(p23) + P::hi(p23)));
-  }
-  st.m = m_new;
-
-  // Rows 0..G-1 of O live in lanes 0..15; they need alpha of rows 0..G-1.
-  float al[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-    al[r] = r < G ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), r)) : 1.f;
-  if (al[0] != 1.f || al[1] != 1.f || al[2] != 1.f || al[3] != 1.f) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int r = 0; r < G; ++r) st.o[c][r] *= al[r];
-    }
-  }
-
-  // ---- O += P x V ------------------------------------------------------------
-  const u32x2 pa = {p01, p23};
-  const u32x2 pl = {q01, q23};
-  auto pv = [&](f32x4 acc, u32x2 bv) {
-    acc = P::pv(pa, bv, acc);
-    if constexpr (PT == kBF16) acc = P::pv(pl, bv, acc);
-    return acc;
-  };
-  if constexpr (kByteKv<KVT>) {
-    // For dim 8 n16 + c the B operand is {V[tok0+0..3][c]}: interleave the
-    // bytes of two tokens, then widen byte pairs.
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      u32 lo_a[2], lo_b[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const u32 x0 = t.v[2 * q][w], x1 = t.v[2 * q + 1][w];
-        lo_a[q] = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.b0 x1.b0 x0.b1 x1.b1
-        lo_b[q] = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.b2 x1.b2 x0.b3 x1.b3
-      }
-      const u32x2 b0 = {widen<PT, KVT, false>(lo_a[0]), widen<PT, KVT, false>(lo_a[1])};
-      const u32x2 b1 = {widen<PT, KVT, true>(lo_a[0]), widen<PT, KVT, true>(lo_a[1])};
-      const u32x2 b2 = {widen<PT, KVT, false>(lo_b[0]), widen<PT, KVT, false>(lo_b[1])};
-      const u32x2 b3 = {widen<PT, KVT, true>(lo_b[0]), widen<PT, KVT, true>(lo_b[1])};
-      st.o[4 * w + 0] = pv(st.o[4 * w + 0], b0);
-      st.o[4 * w + 1] = pv(st.o[4 * w + 1], b1);
-      st.o[4 * w + 2] = pv(st.o[4 * w + 2], b2);
-      st.o[4 * w + 3] = pv(st.o[4 * w + 3], b3);
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const u32 v0 = t.v[0][w], v1 = t.v[1][w], v2 = t.v[2][w], v3 = t.v[3][w];
-      const u32x2 be = {(v0 & 0xffffu) | (v1 << 16), (v2 & 0xffffu) | (v3 << 16)};
-      const u32x2 bo = {(v0 >> 16) | (v1 & 0xffff0000u), (v2 >> 16) | (v3 & 0xffff0000u)};
-      st.o[2 * w + 0] = pv(st.o[2 * w + 0], be);
-      st.o[2 * w + 1] = pv(st.o[2 * w + 1], bo);
-    }
-  }
-}
-
-// How a workgroup finishes its chunk.
-enum Mode : int {
-  kModeDirect = 0,      // single chunk per head: normalise and write the output
-  kModeSplit = 1,       // write the chunk partial; a separate kernel combines
-  kModeSplitFused = 2,  // write the partial; the head's last workgroup combines
-};
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// Log-sum-exp merge of n partial rows of one query head, run by one wave
-// (lane l owns dims 2l and 2l + 1):
-//   M = max_k m_k,  out = v_scale * sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k
-// row(k) gives the k-th partial row. A row whose max is -inf is empty (a
-// workgroup that had no slabs marked it): it gets weight 0 and its O row,
-// possibly stale, is never read. The (m, l) pairs of 64 rows at a time are
-// loaded one per lane, so the whole merge costs two dependent loads.
-template <int QT, typename RowFn>
-__device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, char* outp) {
-  using E = Elem<QT>;
-  const int lane = threadIdx.x & 63;
-  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
-  const float2* po = reinterpret_cast<const float2*>(a.part_o);
-  float mloc = -INFINITY;
-  for (int k = lane; k < n; k += 64) mloc = fmaxf(mloc, ml[row(k)].x);
-  const float M = wave_max(mloc);   // finite: at least one row holds data
-  const size_t fallback = row(0);   // a row that holds data, read with weight 0
-  float lloc = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int base = 0; base < n; base += 64) {
-    const int k = base + lane;
-    float wk = 0.f;
-    if (k < n) {
-      const float2 v = ml[row(k)];
-      if (v.x != -INFINITY) {
-        wk = fast_exp2(v.x - M);
-        lloc += wk * v.y;
-      }
-    }
-    const int cnt = min(64, n - base);
-    for (int j0 = 0; j0 < cnt; j0 += 8) {   // 8 independent row loads in flight
-      float f[8];
-      float2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u;
-        f[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), min(j, 63)));
-        if (j >= cnt) f[u] = 0.f;
-        const size_t r = f[u] != 0.f ? row(base + j) : fallback;
-        v[u] = po[r * (kHeadDim / 2) + lane];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        o0 += f[u] * v[u].x;
-        o1 += f[u] * v[u].y;
-      }
-    }
-  }
-  const float inv = a.v_scale / wave_sum(lloc);
-  E::store2(outp, o0 * inv, o1 * inv);
-}
 
 // Merge of the chunked split for the G query heads of (request b, KV head g):
 // wave r < G takes head G g + r. Only the chunks that start below the current
@@ -514,15 +72,6 @@ __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int
   }
   merge_rows<QT>(a, n, [&](int k) -> size_t { return head * (size_t)S + k; }, outp);
 }
-
-// LDS of one workgroup: the 4 waves' K staging slices and the merge buffers
-// (for the 4 MFMA rows; rows >= G carry zero queries and are never stored).
-struct WorkgroupLds {
-  u32x4 k[kWaves][kKStageSlots];
-  float o[kWaves][kGroup][kHeadDim];
-  float m[kWaves][kGroup];
-  float l[kWaves][kGroup];
-};
 
 // One workgroup attends the G query rows of (request b, KV head g) over the
 // cache slots [c0, c1) (c0 < c1 <= length). On return thread t holds, for
@@ -718,39 +267,6 @@ __global__ __launch_bounds__(kThreads) void gqa_combine_kernel(StepArgs a) {
 // first and last piece, when they are only part of a head, become partials
 // in slots 2w and 2w + 1, which the balanced combine merges per head.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int slabs_of(int len, int capacity) {
-  return (min(max(len, 0), capacity) + kSlab - 1) / kSlab;
-}
-
-// pref[b] = 8 * sum_{b' < b} slabs(b'), b = 0..B (B <= kMaxBalancedBatch).
-__device__ __forceinline__ void build_slab_prefix(const StepArgs& a, int* pref, int* wave_tot) {
-  const int B = a.batch;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int per = (B + kThreads - 1) / kThreads;
-  const int lo = min(tid * per, B);
-  const int hi = min(lo + per, B);
-  int own = 0;
-  for (int i = lo; i < hi; ++i) own += slabs_of(a.seq_lens[i], a.capacity);
-  int x = own;   // inclusive scan across the wave
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) wave_tot[wave] = x;
-  __syncthreads();
-  int run = x - own;
-  for (int w = 0; w < wave; ++w) run += wave_tot[w];
-  for (int i = lo; i < hi; ++i) {
-    pref[i] = kKvHeads * run;
-    run += slabs_of(a.seq_lens[i], a.capacity);
-  }
-  if (tid == kThreads - 1) pref[B] = kKvHeads * run;
-  __syncthreads();
-}
-
 // Partial rows of the balanced split: slot k holds kGroup rows (rows >= G
 // unused), so the slot stride does not depend on the geometry.
 template <int QT, int KVT, int G>
@@ -965,29 +481,6 @@ int balanced_grid_typed() {
           kThreads, 0) != hipSuccess)
     return 0;
   return cus * per_cu;
-}
-
-// Calls f.template operator()<QT, KVT, G>() for a supported combination, else
-// returns `bad`.
-template <typename R, typename F>
-R dispatch(int q_dtype, int kv_dtype, int num_q_heads, R bad, F&& f) {
-  auto by_group = [&](auto qt, auto kvt) -> R {
-    constexpr int QT = decltype(qt)::value, KVT = decltype(kvt)::value;
-    if (num_q_heads == 4 * kKvHeads) return f.template operator()<QT, KVT, 4>();
-    if (num_q_heads == 2 * kKvHeads) return f.template operator()<QT, KVT, 2>();
-    return bad;
-  };
-  using BF = std::integral_constant<int, kBF16>;
-  using F16 = std::integral_constant<int, kF16>;
-  using F8 = std::integral_constant<int, kFP8>;
-  using I8 = std::integral_constant<int, kI8>;
-  if (q_dtype == kBF16 && kv_dtype == kBF16) return by_group(BF{}, BF{});
-  if (q_dtype == kF16 && kv_dtype == kF16) return by_group(F16{}, F16{});
-  if (q_dtype == kBF16 && kv_dtype == kFP8) return by_group(BF{}, F8{});
-  if (q_dtype == kF16 && kv_dtype == kFP8) return by_group(F16{}, F8{});
-  if (q_dtype == kBF16 && kv_dtype == kI8) return by_group(BF{}, I8{});
-  if (q_dtype == kF16 && kv_dtype == kI8) return by_group(F16{}, I8{});
-  return bad;
 }
 
 }  // namespace

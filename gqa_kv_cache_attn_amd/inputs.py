@@ -20,6 +20,12 @@ for fp8 divided by the plane's scale, clamped to +-448, cast to e4m3fn; for
 int8 each 128-value row gets the scale max|x| / 127 rounded to bf16, and the
 values round(x / scale) clamped to +-127). Slots past a request's length
 receive the same N(0,1) draw: garbage the kernel must never read.
+
+Paged workloads (page_size > 0) draw lengths, then q [B, T, Hq, 128], then a
+block table (a random permutation of the pool's page ids, so consecutive
+slots of a request sit in scattered pages), then the pool page by page with
+the same per-dtype encoding; the pool holds a few spare pages no request
+uses.
 """
 
 from __future__ import annotations
@@ -51,15 +57,20 @@ class Workload:
     v_scale: float = 1.0
     seed: int = 0
     num_q_heads: int = NUM_Q_HEADS   # 32, or 16 (2 query heads per KV head)
+    page_size: int = 0               # > 0: paged pool of this many slots per page
+    q_tokens: int = 1                # query tokens per request (paged workloads)
 
     def describe(self) -> dict:
-        return {
+        d = {
             "workload": self.name, "batch": self.batch, "capacity": self.capacity,
             "seq_len": [self.len_lo, self.len_hi], "q_heads": self.num_q_heads,
             "kv_heads": NUM_KV_HEADS, "head_dim": HEAD_DIM, "q_dtype": self.q_dtype,
             "kv_dtype": self.kv_dtype, "q_scale": self.q_scale,
             "k_scale": self.k_scale, "v_scale": self.v_scale, "seed": self.seed,
         }
+        if self.page_size:
+            d.update(page_size=self.page_size, q_tokens=self.q_tokens)
+        return d
 
 
 # The five workloads of the main geometry, then the INT8 row-scaled cache at
@@ -78,7 +89,17 @@ WORKLOADS = [
     Workload("gqa_decode_b16_c131072_int8kv_16q_long", 16, 131072, 65536, 131072, "bf16", "int8",
              seed=1007, num_q_heads=16),
 ]
-WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS}
+
+# Paged pool, several query tokens per request: the verify pass of a step
+# with 2 draft tokens (T = 3) over 16-slot pages, the 64k bf16 shape; and a
+# single-token fp8 pool of 64-slot pages, the 128k fp8 shape.
+PAGED_WORKLOADS = [
+    Workload("gqa_decode_paged_b8_c65536_p16_bf16_t3", 8, 65536, 32768, 65536, "bf16", "bf16",
+             q_scale=0.5, seed=1008, page_size=16, q_tokens=3),
+    Workload("gqa_decode_paged_b16_c131072_p64_fp8kv_t1", 16, 131072, 65536, 131072, "bf16",
+             "fp8_e4m3", k_scale=1.0 / 64, v_scale=1.0 / 64, seed=1009, page_size=64, q_tokens=1),
+]
+WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + PAGED_WORKLOADS}
 
 
 def kv_elem_bytes(kv_dtype: str) -> int:
@@ -147,6 +168,58 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
     return {"q": q, "kv": kv, "kv_scales": kv_scales, "seq_lens": lens, "q_scale": w.q_scale,
             "k_scale": w.k_scale, "v_scale": w.v_scale, "q_dtype": w.q_dtype,
             "kv_dtype": w.kv_dtype}
+
+
+def _encode_block(x: torch.Tensor, w: Workload):
+    """fp32 N(0,1) block [..., 2, 8, S, 128] -> (stored values, bf16 row scales or None)."""
+    if w.kv_dtype == "fp8_e4m3":
+        return torch.stack([_encode_fp8(x[..., 0, :, :, :], w.k_scale),
+                            _encode_fp8(x[..., 1, :, :, :], w.v_scale)], dim=-4), None
+    if w.kv_dtype == "int8":
+        return _encode_int8_rows(x)
+    return x.to(_TORCH_DTYPES[w.kv_dtype]), None
+
+
+def make_paged_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
+                      seq_lens: Optional[torch.Tensor] = None, spare_pages: int = 5,
+                      pages_per_draw: int = 4096):
+    """Draw one paged workload: q [B, T, Hq, 128], the pool [num_pages, 2, 8, P, 128]
+    (+ row scales for int8), block_table [B, max_pages] int32 and the lengths."""
+    assert w.page_size > 0
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed if seed is None else seed)
+    B, C, P, T = w.batch, w.capacity, w.page_size, w.q_tokens
+    lo, hi = min(w.len_lo, C), min(w.len_hi, C)
+    lens = torch.randint(lo, hi + 1, (B,), generator=gen, device=dev, dtype=torch.int64)
+    lens = lens.to(torch.int32)
+    if seq_lens is not None:
+        lens = seq_lens.to(device=dev, dtype=torch.int32).clone()
+    q32 = torch.randn(B, T, w.num_q_heads, HEAD_DIM, generator=gen, device=dev,
+                      dtype=torch.float32)
+    q = q32.to(_TORCH_DTYPES[w.q_dtype])
+    del q32
+    max_pages = (C + P - 1) // P
+    num_pages = B * max_pages + spare_pages
+    perm = torch.randperm(num_pages, generator=gen, device=dev)
+    table = perm[:B * max_pages].reshape(B, max_pages).to(torch.int32).contiguous()
+    store = {"fp8_e4m3": torch.uint8, "int8": torch.int8}.get(w.kv_dtype)
+    pool = torch.empty(num_pages, 2, NUM_KV_HEADS, P, HEAD_DIM, device=dev,
+                       dtype=store if store is not None else _TORCH_DTYPES[w.kv_dtype])
+    scales = (torch.empty(num_pages, 2, NUM_KV_HEADS, P, device=dev, dtype=torch.bfloat16)
+              if w.kv_dtype == "int8" else None)
+    for p0 in range(0, num_pages, pages_per_draw):
+        n = min(pages_per_draw, num_pages - p0)
+        x = torch.randn(n, 2, NUM_KV_HEADS, P, HEAD_DIM, generator=gen, device=dev,
+                        dtype=torch.float32)
+        vals, sc = _encode_block(x, w)
+        pool[p0:p0 + n] = vals
+        if scales is not None:
+            scales[p0:p0 + n] = sc
+        del x, vals, sc
+    return {"q": q, "kv_pages": pool, "kv_scales": scales, "block_table": table,
+            "seq_lens": lens, "q_scale": w.q_scale, "k_scale": w.k_scale, "v_scale": w.v_scale,
+            "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype, "page_size": P}
 
 
 def storage_bits(t: torch.Tensor):

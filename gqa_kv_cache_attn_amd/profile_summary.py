@@ -24,13 +24,23 @@ import statistics
 
 from .build import CSRC
 
-KERNEL_MATCH = "attention_kernel"   # gqa_attention_kernel or gqa_balanced_attention_kernel
 COPY_MATCH = "copy_stream_kernel"
 
 
-def kernel_source_digest() -> str:
-    with open(os.path.join(CSRC, "gqa_kernels.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+# Sources each kernel family is compiled from (the digest covers all of them).
+_SOURCES = {
+    "contiguous": ("gqa_kernels.h", "gqa_device.h", "gqa_kernels.hip"),
+    "paged": ("gqa_kernels.h", "gqa_device.h", "gqa_paged.hip"),
+}
+
+
+def kernel_source_digest(kernel: str = "gqa_balanced_attention_kernel") -> str:
+    """Digest of the sources the named kernel is built from."""
+    h = hashlib.sha256()
+    for name in _SOURCES["paged" if "paged" in kernel else "contiguous"]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _counter_avg(path, match):
@@ -52,15 +62,16 @@ def cmd_stats(a):
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
     lines.append("")
-    lines.append(f"kernel_source_sha256_16 = {kernel_source_digest()}")
+    lines.append(f"kernel_source_sha256_16 = {kernel_source_digest(a.kernel)}")
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
 def cmd_traffic(a):
-    fetch, nf = _counter_avg(a.fetch, KERNEL_MATCH)
-    write, nw = _counter_avg(a.write, KERNEL_MATCH)
+    match = f"::{a.kernel}<"            # exact kernel name within the demangled signature
+    fetch, nf = _counter_avg(a.fetch, match)
+    write, nw = _counter_avg(a.write, match)
     cfetch, _ = _counter_avg(a.copy_fetch, COPY_MATCH)
     cwrite, _ = _counter_avg(a.copy_write, COPY_MATCH)
     fscale = a.copy_bytes / cfetch          # bytes per FETCH_SIZE unit
@@ -83,7 +94,7 @@ def cmd_traffic(a):
         f"hbm_bytes_per_launch = {fb + wb:.0f}",
         f"algorithmic_bytes_per_launch = {a.algorithmic_bytes}",
         f"fetch_over_algorithmic = {fb / a.algorithmic_bytes:.4f}",
-        f"kernel_source_sha256_16 = {kernel_source_digest()}",
+        f"kernel_source_sha256_16 = {kernel_source_digest(a.kernel)}",
     ]
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -99,6 +110,8 @@ def main():
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
     s.add_argument("--only-gqa", action="store_true")
+    s.add_argument("--kernel", default="gqa_balanced_attention_kernel",
+                   help="kernel whose source digest is recorded")
     t = sub.add_parser("traffic")
     for k in ("workload", "fetch", "write", "copy_fetch", "copy_write", "command", "out"):
         t.add_argument("--" + k.replace("_", "-"), required=True)

@@ -211,6 +211,71 @@ GQA_API gqa_status_t prepare_gqa_decode_int8(const gqa_desc_t* desc, const void*
                                              const int32_t* seq_lens, float q_scale, void* out,
                                              int32_t num_splits, gqa_prepared_t** handle);
 
+/* ---- Paged cache, several query tokens per request -------------------------
+ * The decode step over a page pool, for one or more query tokens per request
+ * (the verify pass of speculative decoding). The pages name a paged-KV decode
+ * backend (FreeToken Turing notes, change 2) and a draft-and-verify loop of K
+ * draft tokens per step (Thor vLLM notes, MTP) without fixing a layout; the
+ * one below is this library's reading.
+ *
+ * Layouts (device memory):
+ *   q           [batch, q_tokens, Hq, 128]       q_dtype, 16-byte aligned
+ *   kv_pages    [num_pages, 2, 8, page_size, 128] kv_dtype (plane 0 = K), 16-byte aligned
+ *   kv_scales   [num_pages, 2, 8, page_size]     bf16, INT8_ROWSCALE only (else NULL)
+ *   block_table [batch, max_pages] int32: request b's slot j is row j % page_size of
+ *               page block_table[b][j / page_size]; read on the device only
+ *   seq_lens    [batch] int32, device only: L_b counts the q_tokens new slots
+ *   out         [batch, q_tokens, Hq, 128]       q_dtype
+ * Query token t of request b is at slot L_b - q_tokens + t and attends slots
+ * j < L_b - q_tokens + 1 + t (causal among the new tokens; q_tokens = 1 is
+ * the plain decode step). Lengths are clamped to [0, max_pages * page_size];
+ * a token whose limit leaves no slot (L_b < q_tokens) gets zeros. Block-table
+ * entries for slots below L_b must name pages of the pool; the kernels clamp
+ * entries into [0, num_pages), so a bad entry yields a wrong result, never an
+ * access outside the pool. Entries past a request's last page are never read.
+ * A contiguous cache [batch, 2, 8, C, 128] with C a power of two >= 16 is the
+ * pool with page_size = C and block_table[b] = {b}. */
+#define GQA_MAX_PAGE_SIZE (1 << 16)
+/* q_tokens x (query heads per KV head) may not exceed this (one MFMA tile). */
+#define GQA_PAGED_MAX_ROWS 16
+
+typedef struct gqa_paged_desc {
+  int32_t batch;        /* >= 0; 0 makes every call a no-op */
+  int32_t q_tokens;     /* >= 1; q_tokens * num_q_heads / 8 <= GQA_PAGED_MAX_ROWS */
+  int32_t num_q_heads;  /* 32 or 16 */
+  int32_t num_kv_heads; /* must be 8 */
+  int32_t head_dim;     /* must be 128 */
+  int32_t q_dtype;      /* gqa_dtype_t, as for gqa_desc_t */
+  int32_t kv_dtype;     /* gqa_dtype_t, as for gqa_desc_t */
+  float k_scale;        /* as for gqa_desc_t */
+  float v_scale;
+  int32_t flags;        /* must be 0 (the one-launch merge is not offered here) */
+  int32_t page_size;    /* slots per page: a power of two in [16, GQA_MAX_PAGE_SIZE] */
+  int32_t num_pages;    /* pages in the pool, >= 1 */
+  int32_t max_pages;    /* block_table row length, >= 1; max_pages * page_size <= GQA_MAX_CAPACITY */
+} gqa_paged_desc_t;
+
+/* As gqa_decode / prepare_gqa_decode / gqa_validate_args / gqa_plan_decode
+ * (same routes, num_splits rules, workspace ownership, capture rules and
+ * status codes), over a page pool. The prepared handle runs with
+ * launch_gqa_decode_prepared. out must not overlap q, kv_pages, kv_scales,
+ * block_table or seq_lens (GQA_ERR_ALIAS). */
+GQA_API gqa_status_t gqa_decode_paged(const gqa_paged_desc_t* desc, const void* q,
+                                      const void* kv_pages, const void* kv_scales,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      float q_scale, void* out, hipStream_t stream);
+GQA_API gqa_status_t prepare_gqa_decode_paged(const gqa_paged_desc_t* desc, const void* q,
+                                              const void* kv_pages, const void* kv_scales,
+                                              const int32_t* block_table, const int32_t* seq_lens,
+                                              float q_scale, void* out, int32_t num_splits,
+                                              gqa_prepared_t** handle);
+GQA_API gqa_status_t gqa_validate_args_paged(const gqa_paged_desc_t* desc, const void* q,
+                                             const void* kv_pages, const void* kv_scales,
+                                             const int32_t* block_table, const int32_t* seq_lens,
+                                             float q_scale, const void* out, int32_t num_splits);
+GQA_API gqa_status_t gqa_plan_decode_paged(const gqa_paged_desc_t* desc, int32_t num_splits,
+                                           gqa_plan_t* plan);
+
 /* Free the workspace and the handle (after its work has retired). NULL is a no-op. */
 GQA_API void gqa_prepared_destroy(gqa_prepared_t* handle);
 

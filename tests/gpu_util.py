@@ -138,3 +138,58 @@ def compare(out, ref_pairs, inp, label="", contract_only=False):
         assert max(excess) <= atol, f"{label}: |err| - 1 ulp = {max(excess):.3e} > {atol} ({diag})"
     return diag
 
+
+
+# ------------------------------------------------------------------ paged cache
+def run_paged(inp, path="prepared", num_splits=None, out=None):
+    """Run the paged entry points on make_paged_inputs() tensors; returns (out, prepared)."""
+    b = binding()
+    if out is None:
+        out = torch.empty_like(inp["q"])
+    args = (inp["q"], inp["kv_pages"], inp["block_table"], inp["seq_lens"])
+    kw = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"], kv_scales=inp["kv_scales"])
+    if path == "convenience":
+        b.gqa_decode_paged(*args, inp["q_scale"], out, **kw)
+        torch.cuda.synchronize()
+        return out, None
+    prep = b.prepare_gqa_decode_paged(*args, out, inp["q_scale"], num_splits=num_splits, **kw)
+    b.launch_gqa_decode_prepared(prep)
+    torch.cuda.synchronize()
+    return out, prep
+
+
+def paged_oracle_request(inp, b, seq_len=None):
+    """Oracle output [T, Hq, 128] (fp64) of request b: its pages decoded from the
+    stored bits and relabelled 0..n-1 (relabelling is a pinned invariance)."""
+    from oracle.paged import gqa_decode_paged_reference
+    P = inp["page_size"]
+    L = int(inp["seq_lens"][b]) if seq_len is None else seq_len
+    n = max(1, -(-L // P))
+    ids = inp["block_table"][b, :n].long()
+    pages = inp["kv_pages"].index_select(0, ids)
+    if inp["kv_dtype"] == "int8":
+        dec = decode_int8_rows(storage_bits(pages), storage_bits(inp["kv_scales"].index_select(0, ids)))
+    else:
+        dec = decode_storage(storage_bits(pages), inp["kv_dtype"])
+    q = decode_storage(storage_bits(inp["q"][b:b + 1]), inp["q_dtype"])
+    ref = gqa_decode_paged_reference(q, dec, np.arange(n)[None, :], [L], P, inp["q_scale"],
+                                     inp["k_scale"], inp["v_scale"])
+    return ref[0]
+
+
+def compare_paged(out, inp, requests, label=""):
+    """Every row of the listed requests against the oracle, to the contract
+    bound plus one output ulp (as compare())."""
+    got_all = decoded_out(out, inp["q_dtype"])
+    atol = ATOL[inp["kv_dtype"]]
+    worst, worst_ref = 0.0, 0.0
+    for b in requests:
+        ref = paged_oracle_request(inp, b)
+        got = got_all[b]
+        assert np.all(np.isfinite(got)), f"{label}: non-finite output in request {b}"
+        excess = (np.abs(got - ref) - out_ulp(ref, inp["q_dtype"])).max()
+        worst = max(worst, float(np.abs(got - ref).max()))
+        worst_ref = max(worst_ref, float(np.abs(ref).max()))
+        assert excess <= atol, f"{label}: request {b}: |err| - 1 ulp = {excess:.3e} > {atol}"
+    print(f"[parity] {label} max_abs_err={worst:.3e} max_abs_ref={worst_ref:.3e}", flush=True)
+    return worst

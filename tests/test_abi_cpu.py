@@ -264,3 +264,78 @@ def test_int8_chunk_sizing_counts_the_row_scales():
     d = desc(batch=4097, capacity=65536, kv=b.GQA_INT8_ROWSCALE, hq=16)
     p = b.gqa_plan(d)
     assert p["route"] == 1 and p["chunk_tokens"] == 64 * ((1 << 20) // (64 * 2 * 130))
+
+
+# ---------------------------------------------------------------- paged cache
+POOL, TABLE = 6 * 1024 * MiB, 7 * 1024 * MiB
+
+
+def pdesc(batch=2, T=1, hq=32, q=b.GQA_BF16, kv=b.GQA_BF16, P=16, num_pages=100, max_pages=8,
+          ks=1.0, vs=1.0, flags=0):
+    return b.GqaPagedDesc(batch=batch, q_tokens=T, num_q_heads=hq, num_kv_heads=8, head_dim=128,
+                          q_dtype=q, kv_dtype=kv, k_scale=ks, v_scale=vs, flags=flags, page_size=P,
+                          num_pages=num_pages, max_pages=max_pages)
+
+
+def vp(d, q=Q, pool=POOL, sc=None, table=TABLE, lens=LENS, qs=1.0, out=OUT, ns=0):
+    return b.gqa_validate_args_paged(d, q, pool, sc, table, lens, qs, out, ns)
+
+
+def test_paged_valid_arguments_pass():
+    assert vp(pdesc()) == OK
+    assert vp(pdesc(T=4)) == OK
+    assert vp(pdesc(T=8, hq=16)) == OK
+    assert vp(pdesc(kv=b.GQA_FP8_E4M3, ks=0.25, vs=0.5, P=64)) == OK
+    assert vp(pdesc(kv=b.GQA_INT8_ROWSCALE, hq=16, T=3), sc=5 * 1024 * MiB) == OK
+
+
+@pytest.mark.parametrize("P", [0, 8, 24, 48, 1000, (1 << 16) * 2])
+def test_paged_page_size_must_be_a_power_of_two_from_16(P):
+    assert vp(pdesc(P=P)) == INVALID
+    assert "page_size" in b.last_error()
+
+
+@pytest.mark.parametrize("hq,T", [(32, 5), (16, 9), (32, 0), (32, -1)])
+def test_paged_query_tokens_must_fit_one_mfma_tile(hq, T):
+    assert vp(pdesc(hq=hq, T=T)) == INVALID
+    assert "q_tokens" in b.last_error()
+
+
+def test_paged_other_descriptor_checks():
+    assert vp(pdesc(num_pages=0)) == INVALID
+    assert vp(pdesc(max_pages=0)) == INVALID
+    assert vp(pdesc(P=1 << 16, max_pages=65)) == INVALID          # > GQA_MAX_CAPACITY slots
+    assert vp(pdesc(flags=1)) == INVALID                            # no one-launch merge here
+    assert vp(pdesc(ks=0.5)) == INVALID                             # scale on a 16-bit pool
+    assert vp(pdesc(kv=b.GQA_INT8_ROWSCALE, hq=16)) == INVALID      # int8 needs its scales
+    assert vp(pdesc(), sc=5 * 1024 * MiB) == INVALID                # scales only for int8
+    assert vp(pdesc(), table=None) == INVALID
+    assert vp(pdesc(), table=TABLE + 2) == INVALID                  # 4-byte alignment
+    assert vp(pdesc(), qs=0.0) == INVALID
+
+
+def test_paged_aliasing_by_address_range():
+    d = pdesc(batch=2, T=3, num_pages=100, P=16, max_pages=8)
+    q_bytes = 2 * 3 * 32 * 128 * 2
+    pool_bytes = 100 * 2 * 8 * 16 * 128 * 2
+    assert vp(d, out=Q) == ALIAS
+    assert vp(d, out=POOL + pool_bytes - 16) == ALIAS
+    assert vp(d, out=POOL + pool_bytes) == OK
+    assert vp(d, out=TABLE - q_bytes + 16) == ALIAS                 # covers the block table
+    assert vp(d, out=LENS) == ALIAS
+
+
+def test_paged_plans_use_the_logical_capacity_and_query_rows():
+    # capacity = max_pages * page_size = 512 * 16; chunked workspace rows = B * T * Hq * S
+    d = pdesc(batch=3, T=2, P=16, max_pages=512)
+    p = b.gqa_plan_paged(d, 7)
+    assert p["route"] == 1 and p["num_splits"] == 7
+    assert p["workspace_bytes"] == 3 * 2 * 32 * 7 * 130 * 4 + 256
+    # balanced split: 16 partial rows per slot
+    p = b.gqa_plan_paged(pdesc(batch=8, T=3, P=16, max_pages=4096))
+    assert p["route"] == 2
+    assert p["workspace_bytes"] == 2 * 768 * 16 * 130 * 4 + ((4 * 9 + 255) // 256) * 256
+    # short route when the table addresses at most 64 slots
+    p = b.gqa_plan_paged(pdesc(batch=3, P=32, max_pages=2))
+    assert p["route"] == 0 and p["workspace_bytes"] == 0
+    assert vp(pdesc(batch=0), q=None, pool=None, table=None, lens=None, out=None) == OK
