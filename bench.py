@@ -50,6 +50,10 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle time budget for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--page-size", type=int, default=0,
+                    help="paged workloads: override the page size (slots per page)")
+    ap.add_argument("--q-tokens", type=int, default=0,
+                    help="paged workloads: override the query tokens per request")
     return ap.parse_args()
 
 
@@ -206,6 +210,15 @@ def main():
     torch.cuda.set_device(dev)
     arch = torch.cuda.get_device_properties(dev).gcnArchName
     w = WORKLOADS_BY_NAME[args.workload]
+    if args.page_size or args.q_tokens:
+        if not w.page_size:
+            print("--page-size / --q-tokens apply to paged workloads only", file=sys.stderr)
+            sys.exit(2)
+        import dataclasses
+        w = dataclasses.replace(w, page_size=args.page_size or w.page_size,
+                                q_tokens=args.q_tokens or w.q_tokens,
+                                name=f"{w.name}[P={args.page_size or w.page_size},"
+                                     f"T={args.q_tokens or w.q_tokens}]")
     print(f"[bench] device {arch}; workload {w.name}; generating inputs", file=sys.stderr, flush=True)
     paged = w.page_size > 0
     inp = make_paged_inputs(w, device=dev) if paged else make_inputs(w, device=dev)

@@ -39,6 +39,12 @@ namespace {
 
 constexpr int kRowsMax = kPagedSlotRows;   // MFMA rows that may hold queries
 
+// Build-time knob: minimum resident waves per SIMD the paged balanced kernel
+// is compiled for (the register budget: 2 -> 256 VGPRs, 3 -> 168).
+#ifndef GQA_PAGED_MIN_WAVES_PER_SIMD
+#define GQA_PAGED_MIN_WAVES_PER_SIMD 2
+#endif
+
 // LDS of one workgroup: the waves' K staging slices, merge buffers for one
 // group of 4 rows at a time, and the per-wave (m, l) of all 16 rows.
 struct PagedLds {
@@ -107,7 +113,9 @@ __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, in
   constexpr int Hq = kKvHeads * G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // Uniform per wave; saying so keeps each tile's descriptors (which depend on
+  // the wave's slot) in scalar registers instead of a waterfall loop per load.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15;
   const int grp = lane >> 4;
   const int T = a.q_tokens;
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_combine_kernel(StepArgs a)
 // written directly, first and last pieces go to slots 2w and 2w + 1 of
 // kRowsMax rows each.
 template <int QT, int KVT, int G>
-__global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void
+__global__ __launch_bounds__(kThreads, GQA_PAGED_MIN_WAVES_PER_SIMD) void
 gqa_paged_balanced_kernel(StepArgs a) {
   using E = Elem<QT>;
   __shared__ PagedLds lds;
