@@ -54,6 +54,8 @@ def parse_args():
                     help="paged workloads: override the page size (slots per page)")
     ap.add_argument("--q-tokens", type=int, default=0,
                     help="paged workloads: override the query tokens per request")
+    ap.add_argument("--shape", default="",
+                    help="override batch,capacity,len_lo,len_hi (e.g. 16,131072,65536,131072)")
     return ap.parse_args()
 
 
@@ -210,6 +212,11 @@ def main():
     torch.cuda.set_device(dev)
     arch = torch.cuda.get_device_properties(dev).gcnArchName
     w = WORKLOADS_BY_NAME[args.workload]
+    if args.shape:
+        import dataclasses
+        B, C, lo, hi = (int(x) for x in args.shape.split(","))
+        w = dataclasses.replace(w, batch=B, capacity=C, len_lo=lo, len_hi=hi,
+                                name=f"{w.name}[B={B},C={C},L={lo}..{hi}]")
     if args.page_size or args.q_tokens:
         if not w.page_size:
             print("--page-size / --q-tokens apply to paged workloads only", file=sys.stderr)

@@ -64,6 +64,7 @@ constexpr int64_t kFillWorkgroups = 768;
 constexpr int kNominalBalancedGrid = 768;
 constexpr int kMaxBalancedGrid = 4096;
 
+
 // Resident balanced-kernel workgroups per (device, dtype pair, query heads),
 // queried once.
 std::mutex g_grid_mu;
@@ -126,18 +127,23 @@ gqa_status_t check_desc(const gqa_desc_t* d) {
   return GQA_OK;
 }
 
-// Workspace: part_o [R,128] f32 | part_ml [R,2] f32 | aux int32 array, where R
-// is the number of partial rows: chunked split R = B*T*Hq*S (query-row-major;
-// T = 1 for the contiguous cache), aux = per-(request, KV head) counters
-// [B*8] (fused merge only); balanced split R = 2W*4 (two slots per
-// workgroup, 4 query rows each; 16 for the paged cache), aux = slab prefix [B+1].
+// Workspace: control words | part_o [R,128] f32 | part_ml [R,2] f32 | slab
+// prefix [B+1] int32 (balanced split only). The control words (the opt-in
+// fused merge's per-(request, KV head) counters [B*8]) come first, at an
+// offset no plan changes, and every launch leaves them at zero (the last
+// workgroup of each head resets its counter). R is the number of partial
+// rows: chunked split R = B*T*Hq*S (query-row-major; T = 1 for the contiguous
+// cache), balanced split R = 2W*4 (two slots per workgroup, 4 query rows
+// each; 16 for the paged cache).
 struct WorkspaceLayout {
-  uint64_t ml_offset, aux_offset, total;
+  uint64_t ctrl_bytes, o_offset, ml_offset, aux_offset, total;
 };
 
-WorkspaceLayout workspace_layout(uint64_t rows, uint64_t aux_ints) {
+WorkspaceLayout workspace_layout(uint64_t ctrl_bytes, uint64_t rows, uint64_t aux_ints) {
   WorkspaceLayout w;
-  w.ml_offset = rows * GQA_HEAD_DIM * sizeof(float);
+  w.ctrl_bytes = ctrl_bytes;
+  w.o_offset = ctrl_bytes;
+  w.ml_offset = w.o_offset + rows * GQA_HEAD_DIM * sizeof(float);
   w.aux_offset = w.ml_offset + rows * 2 * sizeof(float);
   w.total = w.aux_offset + ((aux_ints * sizeof(int32_t) + 255) & ~255ull);
   return w;
@@ -145,11 +151,15 @@ WorkspaceLayout workspace_layout(uint64_t rows, uint64_t aux_ints) {
 
 WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p, const Paging& pg) {
   if (p.route == 2)
-    return workspace_layout(2ull * (uint64_t)p.num_workgroups * (pg.on ? gqa::kPagedSlotRows : 4),
+    return workspace_layout(0, 2ull * (uint64_t)p.num_workgroups * (pg.on ? gqa::kPagedSlotRows : 4),
                             (uint64_t)d->batch + 1);
-  return workspace_layout((uint64_t)d->batch * (uint64_t)pg.q_tokens * (uint64_t)d->num_q_heads *
+  const bool fused = (d->flags & GQA_FLAG_FUSED_COMBINE) != 0;
+  const uint64_t ctrl =
+      fused ? (((uint64_t)d->batch * GQA_NUM_KV_HEADS * sizeof(uint32_t) + 255) & ~255ull) : 0;
+  return workspace_layout(ctrl,
+                          (uint64_t)d->batch * (uint64_t)pg.q_tokens * (uint64_t)d->num_q_heads *
                               (uint64_t)p.num_splits,
-                          (uint64_t)d->batch * GQA_NUM_KV_HEADS);
+                          0);
 }
 
 // grid_wgs: resident workgroups of the balanced kernel on the target device
@@ -292,9 +302,9 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.out = out;
   const WorkspaceLayout wl = plan_layout(d, p, pg);
   char* base = static_cast<char*>(ws);
-  a.part_o = ws ? reinterpret_cast<float*>(base) : nullptr;
+  a.part_o = ws ? reinterpret_cast<float*>(base + wl.o_offset) : nullptr;
   a.part_ml = ws ? reinterpret_cast<float*>(base + wl.ml_offset) : nullptr;
-  a.counters = (ws && p.route != 2) ? reinterpret_cast<uint32_t*>(base + wl.aux_offset) : nullptr;
+  a.counters = (ws && p.route != 2) ? reinterpret_cast<uint32_t*>(base) : nullptr;
   a.slab_prefix = (ws && p.route == 2) ? reinterpret_cast<int32_t*>(base + wl.aux_offset) : nullptr;
   a.fused_combine = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
   a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
@@ -327,6 +337,7 @@ gqa_status_t enqueue(const gqa::StepArgs& a, const gqa_desc_t* d, bool paged, hi
 struct CacheEntry {
   void* ptr = nullptr;
   size_t bytes = 0;
+  size_t zero_bytes = 0;   // leading bytes known to be zero (the control words of the last plan)
 };
 std::mutex g_cache_mu;
 std::map<std::pair<int, uintptr_t>, CacheEntry> g_cache;
@@ -453,7 +464,30 @@ gqa_status_t decode_checked(const gqa_desc_t* desc, const void* q, const void* k
         return fail(GQA_ERR_HIP, "hipMemsetAsync of the workspace failed: %s", hipGetErrorString(e));
       }
       ce.bytes = p.workspace_bytes;
+      ce.zero_bytes = p.workspace_bytes;
     }
+    // The control words must start at zero. A plan with more of them than the
+    // last one finds partials of the earlier plan there: clear those bytes
+    // (not during a capture, where that would record a memset).
+    const size_t ctrl = (size_t)plan_layout(desc, p, pg).ctrl_bytes;
+    if (ctrl > ce.zero_bytes) {
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      hipError_t e = hipStreamIsCapturing(stream, &cs);
+      if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(GQA_ERR_HIP, "hipStreamIsCapturing failed: %s", hipGetErrorString(e));
+      }
+      if (cs != hipStreamCaptureStatusNone)
+        return fail(GQA_ERR_CAPTURE,
+                    "the convenience call would clear %llu workspace bytes while the stream is "
+                    "capturing; use the prepare / launch_gqa_decode_prepared pair",
+                    (unsigned long long)(ctrl - ce.zero_bytes));
+      e = hipMemsetAsync(static_cast<char*>(ce.ptr) + ce.zero_bytes, 0, ctrl - ce.zero_bytes, stream);
+      if (e != hipSuccess)
+        return fail(GQA_ERR_HIP, "hipMemsetAsync of the workspace failed: %s", hipGetErrorString(e));
+    }
+    // Launches leave the control words at zero; everything after them is now dirty.
+    ce.zero_bytes = ctrl;
     ws = ce.ptr;
   }
   return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws, pg), desc, pg.on,

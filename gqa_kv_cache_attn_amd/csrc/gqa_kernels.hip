@@ -269,38 +269,19 @@ __global__ __launch_bounds__(kThreads) void gqa_combine_kernel(StepArgs a) {
 // ---------------------------------------------------------------------------
 // Partial rows of the balanced split: slot k holds kGroup rows (rows >= G
 // unused), so the slot stride does not depend on the geometry.
+//
+// The balanced-split range of workgroup u: slabs [s0, s1) (s0 < s1), in
+// pieces of one (request, KV head) each. Heads covered whole are written
+// directly; the first and last piece, when only part of a head, go to slots
+// 2u and 2u + 1.
 template <int QT, int KVT, int G>
-__global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa_balanced_attention_kernel(
-    StepArgs a) {
+__device__ __forceinline__ void balanced_unit(const StepArgs& a, const int* s_pref, int s0, int s1,
+                                              int u, WorkgroupLds& lds) {
   using E = Elem<QT>;
-  __shared__ WorkgroupLds lds;
-  __shared__ int s_pref[kMaxBalancedBatch + 1];
-  __shared__ int s_wave_tot[kWaves];
-
   const int tid = threadIdx.x;
   const int B = a.batch;
-  build_slab_prefix(a, s_pref, s_wave_tot);
-  // Values read from LDS are the same in every lane; saying so keeps the
-  // loop control in scalar registers.
-  const int64_t N = __builtin_amdgcn_readfirstlane(s_pref[B]);
-  const int W = (int)gridDim.x;
-  const int w = (int)blockIdx.x;
-  if (w == 0)   // the combine kernel reads the same prefix
-    for (int i = tid; i <= B; i += kThreads) a.slab_prefix[i] = s_pref[i];
-
   const int er = tid >> 6;
   const int ed = (tid & 63) * 2;
-  // Slab counts fit in int32 (checked when the plan is made).
-  const int s0 = (int)((int64_t)w * N / W);
-  const int s1 = (int)((int64_t)(w + 1) * N / W);
-  if (s0 == s1) {
-    // Fewer slabs than workgroups: mark slot 2w empty for the combine, which
-    // may look at it when this workgroup falls inside a head's range of workgroups.
-    if ((tid & 63) == 0)
-      *reinterpret_cast<float2*>(a.part_ml + ((size_t)2 * w * kGroup + er) * 2) =
-          make_float2(-INFINITY, 0.f);
-    return;
-  }
 #pragma nounroll
   for (int s = s0; s < s1;) {
     // request b with pref[b] <= s < pref[b + 1]
@@ -327,13 +308,46 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
       if (er < G)
         E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
     } else {
-      const size_t slot = 2 * (size_t)w + (s == s0 ? 0 : 1);
+      const size_t slot = 2 * (size_t)u + (s == s0 ? 0 : 1);
       const size_t row = slot * kGroup + er;
       *reinterpret_cast<float2*>(a.part_o + row * kHeadDim + ed) = make_float2(o0, o1);
       if ((tid & 63) == 0) *reinterpret_cast<float2*>(a.part_ml + row * 2) = make_float2(M, lsum);
     }
     s = pe;
   }
+}
+
+template <int QT, int KVT, int G>
+__global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa_balanced_attention_kernel(
+    StepArgs a) {
+  __shared__ WorkgroupLds lds;
+  __shared__ int s_pref[kMaxBalancedBatch + 1];
+  __shared__ int s_wave_tot[kWaves];
+
+  const int tid = threadIdx.x;
+  const int B = a.batch;
+  build_slab_prefix(a, s_pref, s_wave_tot);
+  // Values read from LDS are the same in every lane; saying so keeps the
+  // loop control in scalar registers. Slab counts fit in int32 (checked when
+  // the plan is made).
+  const int N = __builtin_amdgcn_readfirstlane(s_pref[B]);
+  const int W = (int)gridDim.x;
+  const int w = (int)blockIdx.x;
+  if (w == 0)   // the combine kernel reads the same prefix
+    for (int i = tid; i <= B; i += kThreads) a.slab_prefix[i] = s_pref[i];
+
+  const int s0 = (int)((int64_t)w * N / W);
+  const int s1 = (int)((int64_t)(w + 1) * N / W);
+  if (s0 == s1) {
+    // Fewer slabs than workgroups: mark slot 2w empty for the combine, which
+    // may look at it when this workgroup falls inside a head's range of workgroups.
+    const int er = tid >> 6;
+    if ((tid & 63) == 0)
+      *reinterpret_cast<float2*>(a.part_ml + ((size_t)2 * w * kGroup + er) * 2) =
+          make_float2(-INFINITY, 0.f);
+    return;
+  }
+  balanced_unit<QT, KVT, G>(a, s_pref, s0, s1, w, lds);
 }
 
 // Merge of the balanced split, one workgroup per (request, KV head); wave

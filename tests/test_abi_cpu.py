@@ -135,9 +135,9 @@ def test_plan_routes_on_capacity():
         assert b.gqa_plan(desc(capacity=C), 2)["route"] == 1   # explicit split count: chunked
 
 
-def balanced_ws(B, G=768):
-    # partials: 2 slots per workgroup x 4 rows x (128 + 2) floats; slab prefix [B + 1] ints
-    return 2 * G * 4 * 130 * 4 + ((4 * (B + 1) + 255) // 256) * 256
+def balanced_ws(B, G=768, rows_per_slot=4):
+    # partials: 2 slots per workgroup x rows x (128 + 2) floats | slab prefix [B + 1]
+    return 2 * G * rows_per_slot * 130 * 4 + ((4 * (B + 1) + 255) // 256) * 256
 
 
 @pytest.mark.parametrize("C", [65, 100, 1000, 1024, 8192, 65536, 131072])
@@ -164,8 +164,11 @@ def test_chunked_auto_plan_is_consistent(B, C):
     assert T % 16 == 0 and T % 64 == 0
     assert S == -(-C // T)
     assert p["num_workgroups"] == B * 8 * S
-    # FP32 partials (O, then max/sum) and one uint32 counter per (request, KV head)
-    want_ws = B * 32 * S * 130 * 4 + ((B * 8 * 4 + 255) // 256) * 256 if S > 1 else 0
+    # control words (fused merge: one uint32 counter per (request, KV head)),
+    # then FP32 partials (O, then max/sum)
+    fused = B <= 4096
+    ctrl = ((B * 8 * 4 + 255) // 256) * 256 if fused else 0
+    want_ws = ctrl + B * 32 * S * 130 * 4 if S > 1 else 0
     assert p["workspace_bytes"] == want_ws
 
 
@@ -253,7 +256,7 @@ def test_chunked_workspace_scales_with_query_heads(hq, kv):
     d = desc(batch=3, capacity=5000, kv=kv, hq=hq)
     p = b.gqa_plan(d, 7)
     assert p["route"] == 1 and p["num_splits"] == 7
-    assert p["workspace_bytes"] == 3 * hq * 7 * 130 * 4 + 256
+    assert p["workspace_bytes"] == 3 * hq * 7 * 130 * 4
     # the balanced split's partial slots do not depend on the geometry
     assert b.gqa_plan(desc(batch=8, capacity=65536, kv=kv, hq=hq))["workspace_bytes"] == balanced_ws(8)
 
@@ -330,11 +333,11 @@ def test_paged_plans_use_the_logical_capacity_and_query_rows():
     d = pdesc(batch=3, T=2, P=16, max_pages=512)
     p = b.gqa_plan_paged(d, 7)
     assert p["route"] == 1 and p["num_splits"] == 7
-    assert p["workspace_bytes"] == 3 * 2 * 32 * 7 * 130 * 4 + 256
+    assert p["workspace_bytes"] == 3 * 2 * 32 * 7 * 130 * 4
     # balanced split: 16 partial rows per slot
     p = b.gqa_plan_paged(pdesc(batch=8, T=3, P=16, max_pages=4096))
     assert p["route"] == 2
-    assert p["workspace_bytes"] == 2 * 768 * 16 * 130 * 4 + ((4 * 9 + 255) // 256) * 256
+    assert p["workspace_bytes"] == balanced_ws(8, rows_per_slot=16)
     # short route when the table addresses at most 64 slots
     p = b.gqa_plan_paged(pdesc(batch=3, P=32, max_pages=2))
     assert p["route"] == 0 and p["workspace_bytes"] == 0

@@ -159,3 +159,21 @@ def test_int8_entry_points_reject_mismatches_and_aliases():
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
     assert torch.equal(alias.view(torch.int16), before.view(torch.int16))
+
+
+def test_convenience_calls_with_different_plans_share_the_workspace_safely():
+    """Back-to-back convenience calls on one stream whose plans lay the cached
+    workspace out differently (batch, capacity, route): each result matches the
+    oracle, so no plan starts from control words another plan left dirty."""
+    from gpu_util import run_decode
+    cases = [(32, 4096, "bf16"), (4, 8192, "bf16"), (32, 4096, "bf16"), (3, 1000, "f16"),
+             (8, 2048, "fp8_e4m3")]
+    for i, (B, C, kd) in enumerate(cases):
+        qd = "f16" if kd == "f16" else "bf16"
+        fp8 = kd == "fp8_e4m3"
+        w = Workload(f"reuse{i}", B, C, 1, C, qd, kd, q_scale=0.8,
+                     k_scale=1 / 64 if fp8 else 1.0, v_scale=1 / 64 if fp8 else 1.0, seed=60 + i)
+        inp = make_inputs(w, device="cuda")
+        out, _ = run_decode(inp, "convenience")
+        pairs = all_pairs(B) if B <= 8 else [(b, (3 * b) % 8) for b in range(B)]
+        compare(out, oracle_pairs(inp, pairs), inp, f"workspace reuse {i} (B={B}, C={C}, {kd})")
