@@ -81,6 +81,56 @@ int device_balanced_grid(int dev, const gqa_desc_t* d, bool paged) {
   return W;
 }
 
+// Compute units of a device (the size of one tier of balanced-split shares), queried once.
+std::map<int, int> g_cus;
+
+int device_cus(int dev) {
+  std::lock_guard<std::mutex> lk(g_grid_mu);
+  auto it = g_cus.find(dev);
+  if (it != g_cus.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    cus = 0;
+  }
+  g_cus.emplace(dev, cus);
+  return cus;
+}
+
+// Relative shares (per mille) of the balanced split's workgroups by tier (the
+// k-th workgroup resident on a CU: workgroups tier * CUs .. (tier + 1) * CUs - 1)
+// and by parity (odd workgroups run on odd-numbered XCDs). Measured on MI355X
+// with equal shares (per-workgroup timestamps, 64k bf16 and 128k fp8
+// workloads): the second and third workgroup of each CU took 1.1-1.2x and
+// 1.25-1.45x as long as the first, and workgroups on odd XCDs 1.07-1.1x as
+// long as on even ones, reproducibly from launch to launch and whatever
+// slabs they read. These defaults (a sweep of five sets) lift the long-context
+// kernels by 1-3 points of HBM peak. Build-time knobs; shares only move
+// range boundaries, never the result's correctness.
+#ifndef GQA_SHARE_TIER1
+#define GQA_SHARE_TIER1 840
+#endif
+#ifndef GQA_SHARE_TIER2
+#define GQA_SHARE_TIER2 670
+#endif
+#ifndef GQA_SHARE_TIER3
+#define GQA_SHARE_TIER3 670
+#endif
+#ifndef GQA_SHARE_ODD
+#define GQA_SHARE_ODD 920
+#endif
+
+void set_shares(gqa::StepArgs& a, int tier_size) {
+  static const int kTier[gqa::kShareTiers] = {1000, GQA_SHARE_TIER1, GQA_SHARE_TIER2,
+                                             GQA_SHARE_TIER3};
+  // tier_size 0 (unknown) or a grid of one tier: plain equal shares
+  a.tier_size = tier_size > 0 ? tier_size : (1 << 28);
+  for (int t = 0; t < gqa::kShareTiers; ++t) {
+    a.share[2 * t] = kTier[t];
+    a.share[2 * t + 1] = kTier[t] * GQA_SHARE_ODD / 1000;
+  }
+}
+
 int elem_bytes(int dt) { return (dt == GQA_FP8_E4M3 || dt == GQA_INT8_ROWSCALE) ? 1 : 2; }
 
 // K+V bytes one cache slot of one KV head occupies (row scales included).
@@ -292,7 +342,7 @@ gqa_status_t check_device(int* dev_out) {
 
 gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, const void* scales,
                         const int32_t* lens, float q_scale, void* out, const gqa_plan_t& p,
-                        void* ws, const Paging& pg) {
+                        void* ws, const Paging& pg, int tier_size) {
   gqa::StepArgs a;
   a.q = q;
   a.kv = kv;
@@ -308,6 +358,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.slab_prefix = (ws && p.route == 2) ? reinterpret_cast<int32_t*>(base + wl.aux_offset) : nullptr;
   a.fused_combine = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
   a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
+  set_shares(a, tier_size);
   a.batch = d->batch;
   a.capacity = d->capacity;
   a.num_splits = p.num_splits;
@@ -355,6 +406,7 @@ struct gqa_prepared {
   float q_scale;
   void* workspace;
   int device;
+  int tier_size;           // the device's CU count (balanced-split shares)
   Paging pg;               // paged cache / several query tokens
 };
 
@@ -405,6 +457,7 @@ gqa_status_t prepare_checked(const gqa_desc_t* desc, const void* q, const void* 
   h->q_scale = q_scale;
   h->workspace = ws;
   h->device = dev;
+  h->tier_size = device_cus(dev);
   h->pg = pg;
   *handle = h;
   return ok();
@@ -490,8 +543,8 @@ gqa_status_t decode_checked(const gqa_desc_t* desc, const void* q, const void* k
     ce.zero_bytes = ctrl;
     ws = ce.ptr;
   }
-  return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws, pg), desc, pg.on,
-                 stream);
+  return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws, pg, device_cus(dev)),
+                 desc, pg.on, stream);
 }
 
 gqa_status_t validate_impl(const gqa_desc_t* desc, const void* q, const void* kv,
@@ -656,7 +709,7 @@ GQA_API gqa_status_t launch_gqa_decode_prepared_timed(gqa_prepared_t* h, hipStre
     st = fail(GQA_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
   if (st == GQA_OK) {
     const gqa::StepArgs a = step_args(&h->desc, h->q, h->kv, h->kv_scales, h->seq_lens, h->q_scale,
-                                      h->out, h->plan, h->workspace, h->pg);
+                                      h->out, h->plan, h->workspace, h->pg, h->tier_size);
     st = enqueue(a, &h->desc, h->pg.on, stream, ev_mid);
   }
   if (st == GQA_OK && ev_end != nullptr && (e = hipEventRecord(ev_end, stream)) != hipSuccess)

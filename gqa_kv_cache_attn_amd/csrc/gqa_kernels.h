@@ -12,6 +12,8 @@ enum DType : int { kF16 = 0, kBF16 = 1, kFP8 = 2, kI8 = 3 };
 
 // The balanced split keeps the per-request slab prefix in LDS.
 constexpr int kMaxBalancedBatch = 4096;
+// Tiers of workgroup shares in the balanced split (StepArgs::share).
+constexpr int kShareTiers = 4;
 
 // Arguments of one decode step, passed to the kernels by value.
 struct StepArgs {
@@ -33,6 +35,10 @@ struct StepArgs {
   float v_scale;
   int32_t fused_combine;     // 1: last workgroup of a head combines; 0: separate combine kernel
   int32_t grid_wgs;          // > 0: balanced split with this many persistent workgroups
+  // Balanced split shares: workgroup w takes a share of the slabs proportional
+  // to share[2 * min(w / tier_size, kShareTiers - 1) + (w & 1)].
+  int32_t tier_size;         // workgroups per tier (the device's CU count)
+  int32_t share[2 * 4];
   // Paged cache (gqa_paged.hip only; kv then is the page pool
   // [num_pages, 2, 8, page_size, 128] and kv_scales [num_pages, 2, 8, page_size]).
   const int32_t* block_table;  // [batch, max_pages]: page of each request's page-sized run of slots

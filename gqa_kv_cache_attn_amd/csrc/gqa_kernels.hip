@@ -336,8 +336,9 @@ __global__ __launch_bounds__(kThreads, GQA_BALANCED_MIN_WAVES_PER_SIMD) void gqa
   if (w == 0)   // the combine kernel reads the same prefix
     for (int i = tid; i <= B; i += kThreads) a.slab_prefix[i] = s_pref[i];
 
-  const int s0 = (int)((int64_t)w * N / W);
-  const int s1 = (int)((int64_t)(w + 1) * N / W);
+  const int64_t total = share_prefix(a, W);
+  const int s0 = balanced_bound(a, w, N, total);
+  const int s1 = balanced_bound(a, w + 1, N, total);
   if (s0 == s1) {
     // Fewer slabs than workgroups: mark slot 2w empty for the combine, which
     // may look at it when this workgroup falls inside a head's range of workgroups.
@@ -370,15 +371,15 @@ __global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs
     E::store2(outp, 0.f, 0.f);
     return;
   }
-  const int64_t W = a.grid_wgs;
+  const int W = a.grid_wgs;
+  const int64_t total = share_prefix(a, W);
   const int64_t seg_start = a.slab_prefix[b] + (int64_t)g * nsb;
   const int64_t seg_end = seg_start + nsb;
-  // workgroup whose range holds slab t: the largest w with w N / W <= t
-  const int wf = (int)(((seg_start + 1) * W - 1) / N);
-  const int wl = (int)((seg_end * W - 1) / N);
+  const int wf = balanced_owner(a, seg_start, N, W, total);
+  const int wl = balanced_owner(a, seg_end - 1, N, W, total);
   if (wf == wl) return;
   // wf's range may begin in an earlier head: then this head is its last piece
-  const int first_slot_bump = ((int64_t)wf * N / W < seg_start) ? 1 : 0;
+  const int first_slot_bump = balanced_bound(a, wf, N, total) < seg_start ? 1 : 0;
   merge_rows<QT>(a, wl - wf + 1,
                  [&](int k) -> size_t {
                    return (2 * (size_t)(wf + k) + (k == 0 ? first_slot_bump : 0)) * kGroup + r;

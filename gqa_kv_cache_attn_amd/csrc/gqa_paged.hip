@@ -345,8 +345,9 @@ gqa_paged_balanced_kernel(StepArgs a) {
     for (int i = tid; i <= B; i += kThreads) a.slab_prefix[i] = s_pref[i];
 
   const int ed = lane * 2;
-  const int s0 = (int)((int64_t)w * N / W);
-  const int s1 = (int)((int64_t)(w + 1) * N / W);
+  const int64_t total = share_prefix(a, W);
+  const int s0 = balanced_bound(a, w, N, total);
+  const int s1 = balanced_bound(a, w + 1, N, total);
   if (s0 == s1) {   // no slab: mark slot 2w empty for the combine
     if (tid < kRowsMax)
       *reinterpret_cast<float2*>(a.part_ml + ((size_t)2 * w * kRowsMax + tid) * 2) =
@@ -406,13 +407,14 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_balanced_combine_kernel(St
     zero_rows<QT, G>(a, b, g);
     return;
   }
-  const int64_t W = a.grid_wgs;
+  const int W = a.grid_wgs;
+  const int64_t total = share_prefix(a, W);
   const int64_t seg_start = a.slab_prefix[b] + (int64_t)g * nsb;
   const int64_t seg_end = seg_start + nsb;
-  const int wf = (int)(((seg_start + 1) * W - 1) / N);
-  const int wl = (int)((seg_end * W - 1) / N);
+  const int wf = balanced_owner(a, seg_start, N, W, total);
+  const int wl = balanced_owner(a, seg_end - 1, N, W, total);
   if (wf == wl) return;   // one workgroup covered the head and wrote it
-  const int first_slot_bump = ((int64_t)wf * N / W < seg_start) ? 1 : 0;
+  const int first_slot_bump = balanced_bound(a, wf, N, total) < seg_start ? 1 : 0;
   for (int row = threadIdx.x >> 6; row < T * G; row += kWaves) {
     char* outp = static_cast<char*>(a.out) + (query_row<G>(b, g, row, T) * kHeadDim + 2 * lane) * 2;
     if (row_limit<G>(L, T, row) <= 0) {   // sees no slot: every piece is empty
