@@ -178,7 +178,7 @@ gqa_status_t check_desc(const gqa_desc_t* d) {
 }
 
 // Workspace: control words | part_o [R,128] f32 | part_ml [R,2] f32 | slab
-// prefix [B+1] int32 (balanced split only). The control words (the opt-in
+// prefix [B+1] and head pieces [2, B*8] int32 (balanced split only). The control words (the opt-in
 // fused merge's per-(request, KV head) counters [B*8]) come first, at an
 // offset no plan changes, and every launch leaves them at zero (the last
 // workgroup of each head resets its counter). R is the number of partial
@@ -200,9 +200,9 @@ WorkspaceLayout workspace_layout(uint64_t ctrl_bytes, uint64_t rows, uint64_t au
 }
 
 WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p, const Paging& pg) {
-  if (p.route == 2)
+  if (p.route == 2)   // aux: slab prefix [B+1] | head pieces [2, B*8]
     return workspace_layout(0, 2ull * (uint64_t)p.num_workgroups * (pg.on ? gqa::kPagedSlotRows : 4),
-                            (uint64_t)d->batch + 1);
+                            (uint64_t)d->batch + 1 + 2ull * (uint64_t)d->batch * GQA_NUM_KV_HEADS);
   const bool fused = (d->flags & GQA_FLAG_FUSED_COMBINE) != 0;
   const uint64_t ctrl =
       fused ? (((uint64_t)d->batch * GQA_NUM_KV_HEADS * sizeof(uint32_t) + 255) & ~255ull) : 0;
@@ -356,6 +356,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.part_ml = ws ? reinterpret_cast<float*>(base + wl.ml_offset) : nullptr;
   a.counters = (ws && p.route != 2) ? reinterpret_cast<uint32_t*>(base) : nullptr;
   a.slab_prefix = (ws && p.route == 2) ? reinterpret_cast<int32_t*>(base + wl.aux_offset) : nullptr;
+  a.head_pieces = a.slab_prefix ? a.slab_prefix + d->batch + 1 : nullptr;
   a.fused_combine = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
   a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
   set_shares(a, tier_size);

@@ -496,7 +496,7 @@ struct WorkgroupLds {
 
 // Balanced split: workgroup w's range is [bound(w), bound(w + 1)), with
 // bound(w) = N * S(w) / S(W) and S(w) the sum of the shares of workgroups
-// 0 .. w-1 (integer arithmetic, so every kernel computes the same ranges).
+// 0 .. w-1 (integer arithmetic).
 // The shares follow how the hardware serves co-resident workgroups: on each
 // CU the workgroup dispatched first streams fastest, and workgroups of
 // odd-numbered XCDs (w odd: XCDs take workgroups round-robin) stream slower.
@@ -518,16 +518,20 @@ __device__ __forceinline__ int balanced_bound(const StepArgs& a, int w, int64_t 
   return (int)(N * share_prefix(a, w) / total);
 }
 
-// The workgroup whose range holds slab t (0 <= t < N): the largest w with
-// bound(w) <= t.
-__device__ __forceinline__ int balanced_owner(const StepArgs& a, int64_t t, int64_t N, int W,
-                                              int64_t total) {
-  int lo = 0, hi = W;   // bound(lo) <= t < bound(hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (balanced_bound(a, mid, N, total) <= t) lo = mid; else hi = mid;
+// Balanced split bookkeeping for the combine: the slot of the head's first
+// piece (-1 when one workgroup wrote the head whole) and the workgroup that
+// holds its last piece. Every head with a slab gets its first entry written
+// by every launch, so nothing of an earlier launch is read.
+__device__ __forceinline__ void record_piece(const StepArgs& a, int head, bool whole, bool first,
+                                             bool last, size_t slot, int w) {
+  if (threadIdx.x != 0) return;
+  const int heads = a.batch * kKvHeads;
+  if (whole) {
+    a.head_pieces[head] = -1;
+    return;
   }
-  return lo;
+  if (first) a.head_pieces[head] = (int)slot;
+  if (last) a.head_pieces[heads + head] = w;
 }
 
 // Balanced split: slabs of 64 slots per (request, KV head).

@@ -26,6 +26,9 @@ struct StepArgs {
   float* part_ml;            // [batch, Hq, num_splits, 2] chunk (max, sum), log2 domain
   uint32_t* counters;        // [batch, 8] finished chunks per (request, KV head); 0 between launches
   int32_t* slab_prefix;      // [batch + 1] balanced split: 8 * slabs before each request
+  int32_t* head_pieces;      // [2, batch * 8] balanced split, per (request, KV head): the slot
+                             // of its first piece (-1: written whole), then the workgroup
+                             // holding its last piece
   int32_t batch;
   int32_t num_q_heads;       // Hq: 32 (4 per KV head) or 16 (2 per KV head)
   int32_t capacity;

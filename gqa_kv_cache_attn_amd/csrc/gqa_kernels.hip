@@ -303,12 +303,14 @@ __device__ __forceinline__ void balanced_unit(const StepArgs& a, const int* s_pr
     float M, lsum, o0, o1;
     attend_range<QT, KVT, G>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
     const size_t head = ((size_t)b * kKvHeads + g) * G + er;
-    if (s == seg_start && pe == seg_end) {
+    const bool whole = s == seg_start && pe == seg_end;
+    const size_t slot = 2 * (size_t)u + (s == s0 ? 0 : 1);
+    record_piece(a, b * kKvHeads + g, whole, s == seg_start, pe == seg_end, slot, u);
+    if (whole) {
       const float inv = a.v_scale / lsum;
       if (er < G)
         E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
     } else {
-      const size_t slot = 2 * (size_t)u + (s == s0 ? 0 : 1);
       const size_t row = slot * kGroup + er;
       *reinterpret_cast<float2*>(a.part_o + row * kHeadDim + ed) = make_float2(o0, o1);
       if ((tid & 63) == 0) *reinterpret_cast<float2*>(a.part_ml + row * 2) = make_float2(M, lsum);
@@ -365,24 +367,21 @@ __global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs
   if (r >= G) return;
   const size_t head = ((size_t)b * kKvHeads + g) * G + r;
   char* outp = static_cast<char*>(a.out) + (head * kHeadDim + 2 * lane) * 2;
-  const int64_t N = a.slab_prefix[a.batch];
   const int nsb = (a.slab_prefix[b + 1] - a.slab_prefix[b]) / kKvHeads;
   if (nsb == 0) {
     E::store2(outp, 0.f, 0.f);
     return;
   }
-  const int W = a.grid_wgs;
-  const int64_t total = share_prefix(a, W);
-  const int64_t seg_start = a.slab_prefix[b] + (int64_t)g * nsb;
-  const int64_t seg_end = seg_start + nsb;
-  const int wf = balanced_owner(a, seg_start, N, W, total);
-  const int wl = balanced_owner(a, seg_end - 1, N, W, total);
-  if (wf == wl) return;
-  // wf's range may begin in an earlier head: then this head is its last piece
-  const int first_slot_bump = balanced_bound(a, wf, N, total) < seg_start ? 1 : 0;
+  // Where the attention kernel put the head's pieces: the first piece's slot
+  // (-1: written whole) and the workgroup of the last piece. The workgroups
+  // in between hold the head in their first slot (or, with no slab, mark it empty).
+  const int first_slot = a.head_pieces[bg];
+  if (first_slot < 0) return;
+  const int wf = first_slot >> 1;
+  const int wl = a.head_pieces[a.batch * kKvHeads + bg];
   merge_rows<QT>(a, wl - wf + 1,
                  [&](int k) -> size_t {
-                   return (2 * (size_t)(wf + k) + (k == 0 ? first_slot_bump : 0)) * kGroup + r;
+                   return (k == 0 ? (size_t)first_slot : 2 * (size_t)(wf + k)) * kGroup + r;
                  },
                  outp);
 }

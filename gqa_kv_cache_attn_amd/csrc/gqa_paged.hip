@@ -373,6 +373,7 @@ gqa_paged_balanced_kernel(StepArgs a) {
     const int c1 = min((pe - seg_start) * kSlab, L);
     const bool whole = s == seg_start && pe == seg_end;
     const size_t slot = 2 * (size_t)w + (s == s0 ? 0 : 1);
+    record_piece(a, b * kKvHeads + g, whole, s == seg_start, pe == seg_end, slot, w);
     attend_paged<QT, KVT, G>(a, b, g, c0, c1, L, lds,
                              [&](int row, float M, float lsum, float o0, float o1) {
       if (row >= R) return;
@@ -401,20 +402,17 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_balanced_combine_kernel(St
   const int lane = threadIdx.x & 63;
   const int T = a.q_tokens;
   const int L = min(max(a.seq_lens[b], 0), a.capacity);
-  const int64_t N = a.slab_prefix[a.batch];
   const int nsb = (a.slab_prefix[b + 1] - a.slab_prefix[b]) / kKvHeads;
   if (nsb == 0) {
     zero_rows<QT, G>(a, b, g);
     return;
   }
-  const int W = a.grid_wgs;
-  const int64_t total = share_prefix(a, W);
-  const int64_t seg_start = a.slab_prefix[b] + (int64_t)g * nsb;
-  const int64_t seg_end = seg_start + nsb;
-  const int wf = balanced_owner(a, seg_start, N, W, total);
-  const int wl = balanced_owner(a, seg_end - 1, N, W, total);
-  if (wf == wl) return;   // one workgroup covered the head and wrote it
-  const int first_slot_bump = balanced_bound(a, wf, N, total) < seg_start ? 1 : 0;
+  // The head's first-piece slot (-1: written whole) and last workgroup, as
+  // the attention kernel recorded them.
+  const int first_slot = a.head_pieces[bg];
+  if (first_slot < 0) return;
+  const int wf = first_slot >> 1;
+  const int wl = a.head_pieces[a.batch * kKvHeads + bg];
   for (int row = threadIdx.x >> 6; row < T * G; row += kWaves) {
     char* outp = static_cast<char*>(a.out) + (query_row<G>(b, g, row, T) * kHeadDim + 2 * lane) * 2;
     if (row_limit<G>(L, T, row) <= 0) {   // sees no slot: every piece is empty
@@ -423,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_balanced_combine_kernel(St
     }
     merge_rows<QT>(a, wl - wf + 1,
                    [&](int k) -> size_t {
-                     return (2 * (size_t)(wf + k) + (k == 0 ? first_slot_bump : 0)) * kRowsMax + row;
+                     return (k == 0 ? (size_t)first_slot : 2 * (size_t)(wf + k)) * kRowsMax + row;
                    },
                    outp);
   }

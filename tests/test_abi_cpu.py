@@ -137,7 +137,8 @@ def test_plan_routes_on_capacity():
 
 def balanced_ws(B, G=768, rows_per_slot=4):
     # partials: 2 slots per workgroup x rows x (128 + 2) floats | slab prefix [B + 1]
-    return 2 * G * rows_per_slot * 130 * 4 + ((4 * (B + 1) + 255) // 256) * 256
+    # and, per (request, KV head), its first-piece slot and last workgroup
+    return 2 * G * rows_per_slot * 130 * 4 + ((4 * (B + 1 + 2 * 8 * B) + 255) // 256) * 256
 
 
 @pytest.mark.parametrize("C", [65, 100, 1000, 1024, 8192, 65536, 131072])
