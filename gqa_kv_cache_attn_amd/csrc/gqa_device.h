@@ -2,8 +2,27 @@
 // contiguous cache; gqa_paged.hip: the paged cache with several query tokens
 // per request): element traits of the MFMA operand types, whole-row tile
 // loads through buffer descriptors, the per-tile step of the online softmax
-// (QK^T and PV on the matrix cores), and the log-sum-exp merge of partial
-// rows. Included by the .hip sources only.
+// (QK^T and PV on the matrix cores), the log-sum-exp merge of partial rows,
+// and the balanced split's bookkeeping. Included by the .hip sources only.
+//
+// Tile step. A wave takes 16 cache slots at a time. The query rows of one
+// (request, KV head) -- G = 4 (or 2) grouped heads, times the query tokens of
+// a paged call -- form the 16-column B operand (unused columns zero; the
+// matrix cores have far more throughput than this stream needs):
+//   scores^T[16 tok, 16 rows] = K_tile[16 tok, 128] x Q^T[128, 16]
+//       4 x v_mfma_f32_16x16x32_{bf16,f16}; the coalesced loads deliver K
+//       one row per 16 (or 8) lanes, so each wave passes its K tile through a
+//       private, XOR-swizzled LDS slice to get one token per lane;
+//   O[16 rows, 128]           += P[16 rows, 16 tok] x V_tile[16 tok, 128]
+//       8 x v_mfma_f32_16x16x16_{bf16,f16} (16 with the bf16 hi + lo weight
+//       split); the score accumulator already is the P operand layout, and
+//       byte permutes turn the V load layout into the B operand.
+// fp8 e4m3 and int8 bytes are widened exactly in registers (fp8 with the
+// gfx950 packed converts), so the cache is read once, at 1 byte per element.
+// The online softmax runs in fp32 in the log2 domain. Loads are raw buffer
+// loads whose range ends at the range's last valid slot: slots past a length
+// read as 0 without touching memory, which also makes the one-tile-ahead
+// prefetch free at the end of a range.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -11,35 +11,20 @@
 // cache"): the K row scale multiplies that token's score, the V row scale
 // its weight in the PV product.
 //
-// Work split. A workgroup (4 waves of 64 lanes) owns one chunk of one
-// (request, KV head): `chunk_tokens` consecutive cache slots. Within the
-// chunk the waves take 16-token tiles round-robin. Every chunk keeps an fp32
-// online softmax (running max m, running sum l, unnormalised output O) in the
-// log2 domain; the 4 waves merge through LDS at the end. With one chunk per
-// head the workgroup normalises and writes the output; otherwise it writes
-// (m, l, O) as FP32 partials — the split-KV scheme of the article's
-// "default routes and num_splits" section — and a log-sum-exp combine kernel
-// merges the chunks of each query head.
-//
-// Tile math on the matrix cores. The 4 grouped query rows form a 16-row MFMA
-// operand (rows 4..15 zero; the cores have ~10x the throughput this stream
-// needs, so the padding costs nothing measurable):
-//   scores^T[16 tok, 16 rows] = K_tile[16 tok, 128] x Q^T[128, 16]
-//       4 x v_mfma_f32_16x16x32_{bf16,f16}; K arrives straight from HBM in
-//       the A-operand layout (lane = token, 8 consecutive dims per lane).
-//   O[16 rows, 128]           += P[16 rows, 16 tok] x V_tile[16 tok, 128]
-//       8 x v_mfma_f32_16x16x16_{bf16,f16}; the score accumulator already is
-//       the P A-operand layout, and each lane loads 16 contiguous bytes of a
-//       V row (a wave covers 4 whole rows per load), which a byte permute
-//       turns into the B-operand layout (4 tokens of one dim per lane).
-// fp8 e4m3 K/V bytes are widened to bf16/f16 in registers with the gfx950
-// packed converts (exact: every e4m3 value is representable), so the cache
-// is read once, at 1 byte per element.
-//
-// Loads are raw buffer loads whose range ends at the chunk's last valid
-// slot: slots past the request's length are never fetched (they read as 0
-// without touching memory), which also makes the one-tile-ahead prefetch
-// free at the end of a chunk.
+// Routes (the tile step, loads and merges they share are in gqa_device.h):
+//   * chunked split (gqa_attention_kernel): a workgroup of 4 waves owns one
+//     chunk of `chunk_tokens` slots of one (request, KV head); one chunk per
+//     head normalises and writes the output in place (the short route is the
+//     one-chunk case), several write FP32 (m, l, O) partials -- the split-KV
+//     scheme of the article's "default routes and num_splits" section -- that
+//     gqa_combine_kernel merges per query head (or, opt-in, the head's last
+//     workgroup merges them inside the attention kernel);
+//   * balanced split (gqa_balanced_attention_kernel): a persistent grid
+//     shares the step's 64-slot slabs across workgroups from the actual
+//     lengths, weighted by how fast the hardware serves each workgroup;
+//     heads a workgroup covers whole are written directly and the pieces of
+//     the others merged by gqa_balanced_combine_kernel;
+//   * KV append (gqa_kv_append_kernel): the cache write before a step.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
