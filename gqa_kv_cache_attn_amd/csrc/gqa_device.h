@@ -201,14 +201,19 @@ struct Planes {
 // slots at or past c1 read 0. A quad that straddles c1, or any quad of a
 // plane that is not 8-byte aligned, is read one scale at a time, so no load
 // reaches past the range's end whatever the hardware's range-check
-// granularity, and none is misaligned.
+// granularity, and none is misaligned. The scales stream like the rows they
+// belong to (read once per step) and take the same non-temporal policy: with
+// the default one they stay cached between back-to-back steps, which a model
+// that runs other layers in between never sees, and a step that starts on
+// caches full of other data ran 20% slower than with the streaming policy.
 __device__ __forceinline__ u32x2 load_scale_quad(__amdgpu_buffer_rsrc_t r, int tok, int c1,
                                                  bool quads) {
   if (quads && (tok + 4 <= c1 || tok >= c1))
-    return __builtin_amdgcn_raw_buffer_load_b64(r, tok * 2, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, tok * 2, 0, kLoadAux);
   u32 h[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) h[i] = __builtin_amdgcn_raw_buffer_load_b16(r, (tok + i) * 2, 0, 0);
+  for (int i = 0; i < 4; ++i)
+    h[i] = __builtin_amdgcn_raw_buffer_load_b16(r, (tok + i) * 2, 0, kLoadAux);
   return (u32x2){h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
