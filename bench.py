@@ -45,7 +45,7 @@ def parse_args():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = automatic")
     ap.add_argument("--fused-combine", action="store_true",
                     help="merge chunks in the last workgroup instead of a second kernel")
-    ap.add_argument("--cold-calls", type=int, default=30,
+    ap.add_argument("--cold-calls", type=int, default=50,
                     help="calls timed one by one after a 512 MiB cache-flush write")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle time budget for the cpu_baseline sample")
