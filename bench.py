@@ -337,21 +337,31 @@ def main():
     torch.cuda.synchronize()
     convenience_us = c_begin.elapsed_time(c_end) / K * 1e3
 
-    # KV append (the cache write before each step): one token per request at
-    # slot L_b, past the valid prefix, so the decode inputs are unchanged. An
-    # INT8 cache's rows and scales are written by the caller: not timed here.
+    # KV append (the cache write before each step): the step's new tokens (one
+    # per request, T for a paged verify pass) at slots L_b .. L_b + T - 1, past
+    # the valid prefix, so the decode inputs are unchanged (slots past the
+    # cache write nothing). An INT8 cache's rows and scales are written by the
+    # caller: not timed here.
     append_us = None
-    if w.kv_dtype != "int8" and not paged:
-        k_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
-        v_new = torch.randn(w.batch, 8, 128, device=dev).to(inp["q"].dtype)
-        slots = inp["seq_lens"].clamp(max=w.capacity - 1)
+    if w.kv_dtype != "int8":
+        shape = (w.batch, w.q_tokens, 8, 128) if paged else (w.batch, 8, 128)
+        k_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
+        v_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
+        slots = inp["seq_lens"].clone()
+        if paged:
+            def append():
+                b.gqa_kv_append_paged(inp["kv_pages"], inp["block_table"], k_new, v_new, slots,
+                                      inp["k_scale"], inp["v_scale"], num_q_heads=w.num_q_heads)
+        else:
+            def append():
+                b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
         for _ in range(3):
-            b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
+            append()
         a_begin, a_end = new_event(), new_event()
         torch.cuda.synchronize()
         a_begin.record(stream)
         for _ in range(K):
-            b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
+            append()
         a_end.record(stream)
         torch.cuda.synchronize()
         append_us = round(a_begin.elapsed_time(a_end) / K * 1e3, 2)

@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -63,6 +64,9 @@ constexpr int64_t kFillWorkgroups = 768;
 // prepare and the convenience call use the device's own figure (capped).
 constexpr int kNominalBalancedGrid = 768;
 constexpr int kMaxBalancedGrid = 4096;
+// A dispatch counts its work-items in 32 bits: at most this many 256-thread
+// workgroups per launch (decode and append kernels alike).
+constexpr int64_t kMaxLaunchWorkgroups = (int64_t)UINT32_MAX / 256;
 
 
 // Resident balanced-kernel workgroups per (device, dtype pair, query heads),
@@ -267,7 +271,9 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, i
   const int64_t chunk = chunk_granules * GQA_CHUNK_GRANULE;
   const int64_t S = (C + chunk - 1) / chunk;
   const int64_t wgs = (int64_t)d->batch * GQA_NUM_KV_HEADS * S;
-  if (wgs > INT32_MAX) return fail(GQA_ERR_INVALID_ARG, "problem too large for one launch");
+  if (wgs > kMaxLaunchWorkgroups)
+    return fail(GQA_ERR_INVALID_ARG, "problem too large for one launch (%lld workgroups)",
+                (long long)wgs);
   p->route = C <= GQA_SHORT_CAPACITY_MAX ? 0 : 1;
   p->num_splits = (int32_t)S;
   p->chunk_tokens = (int32_t)chunk;
@@ -578,12 +584,10 @@ gqa_status_t decode_impl(const gqa_desc_t* desc, const void* q, const void* kv,
 }
 
 // --- paged cache ---------------------------------------------------------------
-// Checks a paged descriptor and its buffers; on success fills the equivalent
-// contiguous descriptor (capacity = max_pages * page_size, the longest length
-// a block-table row can address) and the paging record.
-gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const void* pool,
-                              const void* scales, const int32_t* table, const int32_t* lens,
-                              float q_scale, const void* out, gqa_desc_t* d, Paging* pg) {
+// Checks a paged descriptor; on success fills the equivalent contiguous
+// descriptor (capacity = max_pages * page_size, the longest length a
+// block-table row can address) and the paging record (without a table).
+gqa_status_t check_paged_desc(const gqa_paged_desc_t* pd, gqa_desc_t* d, Paging* pg) {
   if (pd == nullptr) return fail(GQA_ERR_INVALID_ARG, "desc is NULL");
   const int P = pd->page_size;
   if (P < 16 || P > GQA_MAX_PAGE_SIZE || (P & (P - 1)) != 0)
@@ -617,14 +621,31 @@ gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const v
                 "q_tokens must be in [1, %d] for %d query heads (q_tokens x query heads per KV "
                 "head <= %d; got %d)",
                 GQA_PAGED_MAX_ROWS / group, pd->num_q_heads, GQA_PAGED_MAX_ROWS, pd->q_tokens);
-  if (!scale_ok(q_scale))
-    return fail(GQA_ERR_INVALID_ARG, "q_scale must be finite and > 0 (got %g)", (double)q_scale);
-  const bool int8 = pd->kv_dtype == GQA_INT8_ROWSCALE;
   pg->on = true;
   pg->q_tokens = pd->q_tokens;
   pg->page_shift = __builtin_ctz((unsigned)P);
   pg->num_pages = pd->num_pages;
   pg->max_pages = pd->max_pages;
+  pg->block_table = nullptr;
+  return GQA_OK;
+}
+
+// Bytes of the pool's K/V rows.
+size_t pool_bytes_of(const gqa_paged_desc_t* pd) {
+  return (size_t)pd->num_pages * 2 * GQA_NUM_KV_HEADS * (size_t)pd->page_size * GQA_HEAD_DIM *
+         elem_bytes(pd->kv_dtype);
+}
+
+// Checks a paged descriptor and a decode call's buffers (see check_paged_desc).
+gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const void* pool,
+                              const void* scales, const int32_t* table, const int32_t* lens,
+                              float q_scale, const void* out, gqa_desc_t* d, Paging* pg) {
+  gqa_status_t st = check_paged_desc(pd, d, pg);
+  if (st != GQA_OK) return st;
+  if (!scale_ok(q_scale))
+    return fail(GQA_ERR_INVALID_ARG, "q_scale must be finite and > 0 (got %g)", (double)q_scale);
+  const bool int8 = pd->kv_dtype == GQA_INT8_ROWSCALE;
+  const int P = pd->page_size;
   pg->block_table = table;
   if (pd->batch == 0) return GQA_OK;
   if (!q || !pool || !table || !lens || !out || (int8 && !scales))
@@ -643,7 +664,7 @@ gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const v
   const size_t q_bytes =
       B * (size_t)pd->q_tokens * (size_t)pd->num_q_heads * GQA_HEAD_DIM * elem_bytes(pd->q_dtype);
   const size_t rows = (size_t)pd->num_pages * 2 * GQA_NUM_KV_HEADS * (size_t)P;
-  const size_t pool_bytes = rows * GQA_HEAD_DIM * elem_bytes(pd->kv_dtype);
+  const size_t pool_bytes = pool_bytes_of(pd);
   const size_t sc_bytes = int8 ? rows * 2 : 0;
   const size_t table_bytes = B * (size_t)pd->max_pages * sizeof(int32_t);
   if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, pool, pool_bytes) ||
@@ -824,6 +845,8 @@ GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, co
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv, 16) || !aligned(positions, 4))
     return fail(GQA_ERR_INVALID_ARG,
                 "k_new, v_new and kv must be 16-byte aligned and positions 4-byte aligned");
+  if (desc->batch > kMaxLaunchWorkgroups)   // one workgroup per request
+    return fail(GQA_ERR_INVALID_ARG, "batch too large for one append launch (%d)", desc->batch);
   const size_t B = (size_t)desc->batch;
   const size_t row_bytes = B * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * elem_bytes(desc->q_dtype);
   const size_t kv_bytes =
@@ -843,6 +866,58 @@ GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, co
   a.capacity = desc->capacity;
   a.k_scale = desc->k_scale;
   a.v_scale = desc->v_scale;
+  hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+GQA_API gqa_status_t gqa_kv_append_paged(const gqa_paged_desc_t* desc, const void* k_new,
+                                         const void* v_new, const int32_t* positions,
+                                         const int32_t* block_table, void* kv_pages,
+                                         hipStream_t stream) {
+  gqa_desc_t d;
+  Paging pg;
+  gqa_status_t st = check_paged_desc(desc, &d, &pg);
+  if (st != GQA_OK) return st;
+  if (desc->kv_dtype == GQA_INT8_ROWSCALE)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_kv_append_paged does not write an INT8_ROWSCALE pool");
+  if (desc->batch == 0) return ok();
+  if (!k_new || !v_new || !positions || !block_table || !kv_pages)
+    return fail(GQA_ERR_INVALID_ARG,
+                "k_new, v_new, positions, block_table and kv_pages must be non-NULL");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv_pages, 16) ||
+      !aligned(positions, 4) || !aligned(block_table, 4))
+    return fail(GQA_ERR_INVALID_ARG,
+                "k_new, v_new and kv_pages must be 16-byte aligned, positions and block_table "
+                "4-byte aligned");
+  if ((int64_t)desc->batch * desc->q_tokens > kMaxLaunchWorkgroups)   // one workgroup per token
+    return fail(GQA_ERR_INVALID_ARG, "batch x q_tokens too large for one append launch");
+  const size_t B = (size_t)desc->batch;
+  const size_t row_bytes =
+      B * (size_t)desc->q_tokens * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * elem_bytes(desc->q_dtype);
+  const size_t pool_bytes = pool_bytes_of(desc);
+  if (ranges_overlap(kv_pages, pool_bytes, k_new, row_bytes) ||
+      ranges_overlap(kv_pages, pool_bytes, v_new, row_bytes) ||
+      ranges_overlap(kv_pages, pool_bytes, positions, B * sizeof(int32_t)) ||
+      ranges_overlap(kv_pages, pool_bytes, block_table, B * (size_t)desc->max_pages * sizeof(int32_t)))
+    return fail(GQA_ERR_ALIAS, "kv_pages must not overlap k_new, v_new, positions or block_table");
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != GQA_OK) return st;
+  gqa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.positions = positions;
+  a.kv = kv_pages;
+  a.batch = desc->batch;
+  a.tokens = desc->q_tokens;
+  a.capacity = d.capacity;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
+  a.block_table = block_table;
+  a.max_pages = desc->max_pages;
+  a.page_shift = pg.page_shift;
+  a.num_pages = desc->num_pages;
   hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

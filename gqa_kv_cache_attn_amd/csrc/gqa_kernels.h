@@ -53,14 +53,24 @@ struct StepArgs {
 
 // Arguments of one KV append (one new token per request).
 struct AppendArgs {
-  const void* k_new;         // [batch, 8, 128] 16-bit
-  const void* v_new;         // [batch, 8, 128] 16-bit
-  const int32_t* positions;  // [batch] slot to write; outside [0, capacity) -> skipped
-  void* kv;                  // [batch, 2, 8, capacity, 128] kv dtype
+  const void* k_new;         // [batch, tokens, 8, 128] 16-bit
+  const void* v_new;         // [batch, tokens, 8, 128] 16-bit
+  const int32_t* positions;  // [batch] slot of the first new token; slots outside
+                             // [0, capacity) are skipped
+  void* kv;                  // contiguous [batch, 2, 8, capacity, 128] or page pool
+                             // [num_pages, 2, 8, 1 << page_shift, 128], kv dtype
   int32_t batch;
-  int32_t capacity;
+  int32_t tokens = 1;        // new tokens per request
+  int32_t capacity;          // slots a request can address (paged: max_pages << page_shift)
   float k_scale;             // fp8 cache: stored code = e4m3(k / k_scale)
   float v_scale;
+  // Page pool (block_table != nullptr): slot j of request b is row j % page
+  // size of page block_table[b * max_pages + j / page size]; entries outside
+  // [0, num_pages) are skipped.
+  const int32_t* block_table = nullptr;
+  int32_t max_pages = 0;
+  int32_t page_shift = 0;
+  int32_t num_pages = 0;
 };
 
 hipError_t enqueue_kv_append(const AppendArgs& args, int src_dtype, int kv_dtype, hipStream_t stream);

@@ -24,7 +24,8 @@
 //     lengths, weighted by how fast the hardware serves each workgroup;
 //     heads a workgroup covers whole are written directly and the pieces of
 //     the others merged by gqa_balanced_combine_kernel;
-//   * KV append (gqa_kv_append_kernel): the cache write before a step.
+//   * KV append (gqa_kv_append_kernel): the cache write before a step, into
+//     the contiguous cache or a page pool.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -404,8 +405,10 @@ hipError_t enqueue_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mi
 }
 
 // ---------------------------------------------------------------------------
-// KV append: write one new token's K and V rows of every KV head at slot
-// positions[b] (the cache write that precedes each decode step). An fp8
+// KV append: write the K and V rows of every KV head of T new tokens per
+// request at slots positions[b] + t (the cache write that precedes each
+// decode step; T > 1 for the draft tokens a verify pass attends), into the
+// contiguous cache or through the block table into a page pool. An fp8
 // cache stores e4m3(x / scale), per-tensor scales as in the Thor FP8-KV
 // notes; the division is an IEEE fp32 division and the code the nearest
 // E4M3FN value (ties to even), saturating at +-448.
@@ -434,20 +437,33 @@ __device__ __forceinline__ u32 f32_to_e4m3fn_sat(float x) {
 template <int QT, int KVT>
 __global__ __launch_bounds__(256) void gqa_kv_append_kernel(AppendArgs a) {
   using E = Elem<QT>;
-  // one thread per 8 dims of one (request, plane, KV head) row
-  const int t = (int)(blockIdx.x * 256 + threadIdx.x);
-  if (t >= a.batch * 2 * kKvHeads * (kHeadDim / 8)) return;
-  const int chunk = t % (kHeadDim / 8);
-  const int row = t / (kHeadDim / 8);
-  const int g = row % kKvHeads;
-  const int plane = (row / kKvHeads) % 2;
-  const int b = row / (2 * kKvHeads);
-  const int pos = a.positions[b];
+  // One thread per 8 dims of one (request, new token, plane, KV head) row:
+  // the 256 threads of a workgroup write the 16 rows of one new token.
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int T = a.tokens;
+  if (t >= (int64_t)a.batch * T * 2 * kKvHeads * (kHeadDim / 8)) return;
+  const int chunk = (int)(t % (kHeadDim / 8));
+  const int64_t row = t / (kHeadDim / 8);
+  const int g = (int)(row % kKvHeads);
+  const int plane = (int)((row / kKvHeads) % 2);
+  const int64_t bt = row / (2 * kKvHeads);   // request * T + token
+  const int token = (int)(bt % T);
+  const int b = (int)(bt / T);
+  const int64_t pos = (int64_t)a.positions[b] + token;
   if (pos < 0 || pos >= a.capacity) return;
+  size_t dst_row;   // destination row, in rows of 128 values
+  if (a.block_table == nullptr) {
+    dst_row = ((size_t)(b * 2 + plane) * kKvHeads + g) * (size_t)a.capacity + (size_t)pos;
+  } else {
+    const int page = a.block_table[(size_t)b * a.max_pages + (size_t)(pos >> a.page_shift)];
+    if (page < 0 || page >= a.num_pages) return;
+    dst_row = ((((size_t)page * 2 + plane) * kKvHeads + g) << a.page_shift) +
+              (size_t)(pos & ((1 << a.page_shift) - 1));
+  }
   const char* src = static_cast<const char*>(plane ? a.v_new : a.k_new) +
-                    (((size_t)b * kKvHeads + g) * kHeadDim + chunk * 8) * 2;
+                    ((bt * kKvHeads + g) * kHeadDim + chunk * 8) * 2;
   const u32x4 in = *reinterpret_cast<const u32x4*>(src);
-  const size_t dst = ((((size_t)b * 2 + plane) * kKvHeads + g) * a.capacity + pos) * kHeadDim + chunk * 8;
+  const size_t dst = dst_row * kHeadDim + chunk * 8;
   if constexpr (KVT == kFP8) {
     const float scale = plane ? a.v_scale : a.k_scale;
     u32 w[2] = {0u, 0u};
@@ -464,9 +480,9 @@ __global__ __launch_bounds__(256) void gqa_kv_append_kernel(AppendArgs a) {
 
 template <int QT, int KVT>
 hipError_t enqueue_append_typed(const AppendArgs& a, hipStream_t stream) {
-  const int threads = a.batch * 2 * kKvHeads * (kHeadDim / 8);
-  hipLaunchKernelGGL((gqa_kv_append_kernel<QT, KVT>), dim3((threads + 255) / 256), dim3(256), 0,
-                     stream, a);
+  // 256 threads per new token (2 planes x 8 heads x 16 chunks): one workgroup each
+  const unsigned blocks = (unsigned)((int64_t)a.batch * a.tokens);
+  hipLaunchKernelGGL((gqa_kv_append_kernel<QT, KVT>), dim3(blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -303,6 +303,31 @@ GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* handle, gqa_plan_t*
 GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,
                                    const int32_t* positions, void* kv, hipStream_t stream);
 
+/* Append desc->q_tokens new tokens per request to a page pool: token t of
+ * request b lands at slot s = positions[b] + t, i.e. row s % page_size of
+ * page block_table[b][s / page_size], with the K row k_new[b, t, g, :] and
+ * the V row v_new[b, t, g, :] of every KV head g. It is the cache write
+ * before a step over a paged cache (FreeToken Turing notes, change 2, name a
+ * paged-KV decode backend; Thor Qwen3-VL doc, "Runtime architecture", for
+ * the write), several tokens at once for a verify pass over draft tokens
+ * (Thor vLLM notes on MTP); with positions[b] = L_b - q_tokens the tokens
+ * are the ones gqa_decode_paged then attends with the same descriptor.
+ * Layouts: k_new, v_new [batch, q_tokens, 8, 128] in desc->q_dtype (F16 or
+ * BF16), 16-byte aligned; positions int32 [batch] and block_table
+ * [batch, max_pages] int32, both read on the device only, 4-byte aligned;
+ * kv_pages as for gqa_decode_paged, written in place. Encoding as for
+ * gqa_kv_append (16-bit: stored as is; FP8_E4M3: e4m3 of x / k_scale or
+ * x / v_scale, saturating). Slots outside [0, max_pages * page_size) and
+ * block-table entries outside [0, num_pages) write nothing. Two new tokens
+ * must not land on the same page row (which one is stored is then
+ * unspecified). kv_pages must not overlap k_new, v_new, positions or
+ * block_table (GQA_ERR_ALIAS). Asynchronous on `stream`; allocates nothing.
+ * An INT8 pool is rejected (GQA_ERR_INVALID_ARG). */
+GQA_API gqa_status_t gqa_kv_append_paged(const gqa_paged_desc_t* desc, const void* k_new,
+                                         const void* v_new, const int32_t* positions,
+                                         const int32_t* block_table, void* kv_pages,
+                                         hipStream_t stream);
+
 /* Host-only validation of a call's arguments (never touches a device, so it
  * runs without a GPU). Same checks and status codes as prepare_gqa_decode,
  * except the device check; the _int8 form as prepare_gqa_decode_int8. */

@@ -11,7 +11,8 @@ Modules:
   brute       pure-Python loops (math.fsum / math.exp) for tiny inputs.
   kv_append   the cache write before a decode step (fp8 quantise-on-write).
   paged       decode over a paged cache (page pool + block table) with T
-              query tokens per request, causal among themselves.
+              query tokens per request, causal among themselves, and the
+              append of T new tokens per request into the pool.
 
 Every function is pinned by ``tests/test_oracle_pins.py`` (and
 ``tests/test_oracle_pins_paged.py`` for ``paged``) against facts fixed

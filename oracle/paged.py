@@ -27,6 +27,15 @@ What is computed.
 
 Everything else (head grouping h // (Hq / 8), the scales, the softmax) is the
 single-token definition applied to each (request, token, KV head).
+
+* Appending to a pool. The write before a step (the Thor Qwen3-VL doc,
+  "Runtime architecture": decode writes each new token's K and V rows into
+  the cache) lands, for new token t of request b, at slot
+  ``positions[b] + t`` of the request, i.e. through the block table as above;
+  the stored value is the one the contiguous append stores (16-bit: as is;
+  fp8: ``kv_append.quantise_fp8``). Readings taken, as for the contiguous
+  append: slots outside ``[0, max_pages * page_size)`` and table entries
+  outside ``[0, num_pages)`` write nothing.
 """
 
 from __future__ import annotations
@@ -34,6 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 from .gqa_oracle import HEAD_DIM, NUM_KV_HEADS, gqa_decode_head
+from .kv_append import quantise_fp8
 
 
 def gather_pages(kv_pages: np.ndarray, table_row, length: int, page_size: int) -> np.ndarray:
@@ -101,3 +111,37 @@ def gqa_decode_paged_reference(q: np.ndarray, kv_pages: np.ndarray, block_table,
         raise ValueError("a length exceeds max_pages * page_size")
     rows = [gather_pages(kv_pages, table[b], int(lens[b]), page_size) for b in range(len(lens))]
     return gqa_decode_multi(q, rows, lens, q_scale, k_scale, v_scale)
+
+
+def kv_append_paged_reference(pool_bits: np.ndarray, block_table, positions, k_new_f32,
+                              v_new_f32, kv_dtype: str, k_scale: float = 1.0,
+                              v_scale: float = 1.0, new_bits=None) -> np.ndarray:
+    """Return a copy of the stored pool ``pool_bits`` [num_pages, 2, 8, P, 128]
+    after appending T tokens per request.
+
+    k_new_f32 / v_new_f32: [B, T, 8, 128] decoded new rows (fp32-exact values);
+    for a 16-bit pool ``new_bits`` = (k_bits, v_bits) [B, T, 8, 128] are the
+    stored patterns to copy verbatim. Tokens are written in (b, t) order.
+    """
+    out = np.array(pool_bits, copy=True)
+    num_pages, _, H, P, D = out.shape
+    assert H == NUM_KV_HEADS and D == HEAD_DIM
+    table = np.asarray(block_table)
+    B, max_pages = table.shape
+    T = np.asarray(k_new_f32).shape[1]
+    for b in range(B):
+        for t in range(T):
+            s = int(positions[b]) + t
+            if s < 0 or s >= max_pages * P:
+                continue
+            page = int(table[b, s // P])
+            if not 0 <= page < num_pages:
+                continue
+            row = s % P
+            if kv_dtype == "fp8_e4m3":
+                out[page, 0, :, row, :] = quantise_fp8(k_new_f32[b][t], k_scale)
+                out[page, 1, :, row, :] = quantise_fp8(v_new_f32[b][t], v_scale)
+            else:
+                out[page, 0, :, row, :] = new_bits[0][b][t]
+                out[page, 1, :, row, :] = new_bits[1][b][t]
+    return out

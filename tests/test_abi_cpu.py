@@ -344,3 +344,26 @@ def test_paged_plans_use_the_logical_capacity_and_query_rows():
     p = b.gqa_plan_paged(pdesc(batch=3, P=32, max_pages=2))
     assert p["route"] == 0 and p["workspace_bytes"] == 0
     assert vp(pdesc(batch=0), q=None, pool=None, table=None, lens=None, out=None) == OK
+
+
+def test_paged_append_rejects_bad_arguments_without_touching_a_device():
+    d = pdesc(batch=2, T=3, P=16, num_pages=100, max_pages=8)
+    K, V, POS = 1 << 30, 5 << 30, 3 << 30
+    pool_bytes = 100 * 2 * 8 * 16 * 128 * 2
+    app = b._append_paged
+
+    def call(desc_, k=K, v_=V, pos=POS, table=TABLE, pool=POOL):
+        return app(ctypes.byref(desc_), k, v_, pos, table, pool, None)
+
+    assert call(d, k=None) == INVALID
+    assert call(d, table=None) == INVALID
+    assert call(d, k=K + 4) == INVALID                          # 16-byte alignment
+    assert call(d, table=TABLE + 2) == INVALID                  # 4-byte alignment
+    assert call(d, k=POOL + pool_bytes - 16) == ALIAS           # k_new inside the pool
+    assert call(d, table=POOL + 64) == ALIAS                    # block table inside the pool
+    # adjacent to the pool is fine: validation passes and only the device check is left
+    assert call(d, pos=POOL + pool_bytes) not in (INVALID, ALIAS)
+    assert call(pdesc(P=24)) == INVALID and "page_size" in b.last_error()
+    assert call(pdesc(T=5)) == INVALID                           # 5 tokens x 4 heads > 16 rows
+    assert call(pdesc(kv=b.GQA_INT8_ROWSCALE, hq=16)) == INVALID and "INT8" in b.last_error()
+    assert call(pdesc(batch=0), None, None, None, None, None) == OK

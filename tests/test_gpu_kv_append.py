@@ -1,14 +1,17 @@
 """GPU parity of the KV append (cache write before each decode step): the cache
-after gqa_kv_append equals the oracle's, byte for byte."""
+after gqa_kv_append (or the page pool after gqa_kv_append_paged) equals the
+oracle's, byte for byte."""
 
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import Workload, all_pairs, binding, compare, make_inputs, oracle_pairs, require_gpu
-from gqa_kv_cache_attn_amd.inputs import storage_bits
+from gpu_util import (Workload, all_pairs, binding, compare, compare_paged, make_inputs,
+                      oracle_pairs, require_gpu)
+from gqa_kv_cache_attn_amd.inputs import make_paged_inputs, storage_bits
 from oracle import decode_storage
 from oracle.kv_append import kv_append_reference
+from oracle.paged import kv_append_paged_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -104,3 +107,103 @@ def test_append_argument_errors():
     flat = kv.view(-1)
     with pytest.raises(ValueError):           # k_new inside the cache
         b.gqa_kv_append(kv, flat[:2 * 8 * 128].view(2, 8, 128), k, pos)
+
+
+# ---------------------------------------------------------------- page pool
+def _expected_paged(pool, table, k_new, v_new, positions, src, kd, ks, vs):
+    k_bits, v_bits = storage_bits(k_new), storage_bits(v_new)
+    with np.errstate(invalid="ignore"):
+        k32 = decode_storage(k_bits, src).astype(np.float32)
+        v32 = decode_storage(v_bits, src).astype(np.float32)
+    return kv_append_paged_reference(storage_bits(pool), table.cpu().numpy(),
+                                     positions.cpu().numpy(), k32, v32, kd, ks, vs,
+                                     new_bits=(k_bits, v_bits))
+
+
+def _new_rows(B, T, src, seed):
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    k_new = (torch.randn(B, T, 8, 128, generator=gen, device="cuda") * 40).to(TORCH[src])
+    v_new = (torch.randn(B, T, 8, 128, generator=gen, device="cuda") * 3).to(TORCH[src])
+    return k_new, v_new
+
+
+@pytest.mark.parametrize("src,kd,ks,vs", [("f16", "f16", 1.0, 1.0), ("bf16", "bf16", 1.0, 1.0),
+                                          ("bf16", "fp8_e4m3", 1 / 64, 1 / 64),
+                                          ("f16", "fp8_e4m3", 0.0137, 0.75)])
+@pytest.mark.parametrize("P", [16, 64])
+@pytest.mark.parametrize("T", [1, 3])
+def test_paged_append_is_byte_exact(src, kd, ks, vs, P, T):
+    """Slots across page boundaries, before slot 0, past the last page, and in
+    table entries outside the pool (those write nothing)."""
+    B, C = 6, 256
+    w = Workload("append_paged", B, C, 1, C, src, kd, k_scale=ks, v_scale=vs, seed=61,
+                 page_size=P, q_tokens=T)
+    inp = make_paged_inputs(w, device="cuda")
+    pool, table = inp["kv_pages"], inp["block_table"]
+    max_pages, num_pages = table.shape[1], pool.shape[0]
+    table[4, 0] = -1                      # request 4 writes into entry 0 only: skipped
+    table[5, 1] = num_pages + 7           # request 5 crosses into entry 1: skipped there
+    k_new, v_new = _new_rows(B, T, src, 62)
+    k_new[0, 0, 0, :6] = torch.tensor([float("nan"), float("inf"), -float("inf"), 0.0, -0.0, 1e-7])
+    # request 1 (T > 1) crosses a page boundary; request 2's later tokens fall
+    # past the last page; request 3 starts before slot 0; request 5 starts in
+    # its first page and crosses into the bad entry
+    positions = torch.tensor([0, P - 1, max_pages * P - 1, -1, 0, P - 1], dtype=torch.int32,
+                             device="cuda")
+    print(f"[case] paged append {src}->{kd} P={P} T={T}", flush=True)
+    want = _expected_paged(pool, table, k_new, v_new, positions, src, kd, ks, vs)
+    binding().gqa_kv_append_paged(pool, table, k_new, v_new, positions, ks, vs)
+    torch.cuda.synchronize()
+    got = storage_bits(pool)
+    bad = np.flatnonzero(got.ravel() != want.ravel())
+    assert bad.size == 0, f"{bad.size} mismatching bytes, first at {bad[:5]}"
+
+
+@pytest.mark.parametrize("src,kd", [("bf16", "bf16"), ("bf16", "fp8_e4m3"), ("f16", "f16")])
+@pytest.mark.parametrize("hq,T", [(32, 4), (16, 3)])
+def test_paged_append_then_verify_pass(src, kd, hq, T):
+    """The verify step of speculative decoding: T draft tokens appended at
+    slots L .. L + T - 1, then decoded with lengths L + T; the pool must equal
+    the oracle's and the output the oracle's decode of that pool."""
+    B, C, P = 4, 1024, 16
+    fp8 = kd == "fp8_e4m3"
+    w = Workload("append_verify", B, C, 1, C - T, src, kd, q_scale=0.8,
+                 k_scale=1 / 64 if fp8 else 1.0, v_scale=1 / 64 if fp8 else 1.0, seed=63,
+                 num_q_heads=hq, page_size=P, q_tokens=T)
+    inp = make_paged_inputs(w, device="cuda")
+    lens = inp["seq_lens"]
+    k_new, v_new = _new_rows(B, T, src, 64)
+    want = _expected_paged(inp["kv_pages"], inp["block_table"], k_new, v_new, lens, src, kd,
+                           inp["k_scale"], inp["v_scale"])
+    b = binding()
+    b.gqa_kv_append_paged(inp["kv_pages"], inp["block_table"], k_new, v_new, lens,
+                          inp["k_scale"], inp["v_scale"], num_q_heads=hq)
+    lens += T
+    out = torch.empty_like(inp["q"])
+    b.gqa_decode_paged(inp["q"], inp["kv_pages"], inp["block_table"], lens, inp["q_scale"], out,
+                       k_scale=inp["k_scale"], v_scale=inp["v_scale"])
+    torch.cuda.synchronize()
+    assert np.array_equal(storage_bits(inp["kv_pages"]), want)
+    compare_paged(out, inp, range(B), f"paged append+verify {src}/{kd}/{hq}q/T={T}")
+
+
+def test_paged_append_argument_errors():
+    b = binding()
+    pool = torch.zeros(4, 2, 8, 16, 128, dtype=torch.bfloat16, device="cuda")
+    table = torch.zeros(2, 2, dtype=torch.int32, device="cuda")
+    k = torch.zeros(2, 2, 8, 128, dtype=torch.bfloat16, device="cuda")
+    pos = torch.zeros(2, dtype=torch.int32, device="cuda")
+    before = pool.clone()
+    with pytest.raises(ValueError):           # a scale on a 16-bit pool
+        b.gqa_kv_append_paged(pool, table, k, k, pos, 0.5, 1.0)
+    with pytest.raises(ValueError):           # f16 rows into a bf16 pool
+        b.gqa_kv_append_paged(pool, table, k.half(), k.half(), pos)
+    with pytest.raises(ValueError):           # 5 tokens x 4 query heads per KV head > 16 rows
+        k5 = torch.zeros(2, 5, 8, 128, dtype=torch.bfloat16, device="cuda")
+        b.gqa_kv_append_paged(pool, table, k5, k5, pos)
+    flat = pool.view(-1)
+    with pytest.raises(ValueError):           # k_new inside the pool
+        b.gqa_kv_append_paged(pool, table, flat[:2 * 2 * 8 * 128].view(2, 2, 8, 128), k, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, before)

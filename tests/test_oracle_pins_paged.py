@@ -11,7 +11,9 @@ import torch
 
 from oracle import HEAD_DIM, NUM_KV_HEADS, decode_int8_rows, gqa_decode_reference
 from oracle.brute import brute_decode
-from oracle.paged import gather_pages, gqa_decode_multi, gqa_decode_paged_reference
+from oracle.kv_append import kv_append_reference, quantise_fp8
+from oracle.paged import (gather_pages, gqa_decode_multi, gqa_decode_paged_reference,
+                          kv_append_paged_reference)
 
 
 def _scatter_case(rng, B, P, max_pages, lens, spare=3, dtype=np.float64):
@@ -152,3 +154,72 @@ def test_rejects_impossible_inputs():
         gqa_decode_paged_reference(q, pool, np.array([[0, pool.shape[0]]]), [20], 16)
     with pytest.raises(ValueError):          # length beyond max_pages * page_size
         gqa_decode_paged_reference(q, pool, table, [33], 16)
+
+
+# ---------------------------------------------------------------- appending to a pool
+def _bits_case(rng, num_pages, P, B, T):
+    pool = rng.integers(0, 256, size=(num_pages, 2, NUM_KV_HEADS, P, HEAD_DIM), dtype=np.uint8)
+    k = rng.standard_normal((B, T, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    v = rng.standard_normal((B, T, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    return pool, k, v
+
+
+def test_append_on_an_identity_table_is_the_contiguous_append():
+    """page_size = capacity and block_table[b] = [b]: the pool is the contiguous
+    cache, so one token per request must land exactly where the contiguous
+    append puts it (fp8 codes and 16-bit copies alike)."""
+    rng = np.random.default_rng(51)
+    B, C = 3, 16
+    pool, k, v = _bits_case(rng, B, C, B, 1)
+    pos = [0, 15, 9]
+    table = np.arange(B).reshape(B, 1)
+    got = kv_append_paged_reference(pool, table, pos, k, v, "fp8_e4m3", 0.5, 0.125)
+    want = kv_append_reference(pool, k[:, 0], v[:, 0], pos, "fp8_e4m3", 0.5, 0.125)
+    assert np.array_equal(got, want)
+    kb = rng.integers(0, 1 << 16, size=k.shape, dtype=np.uint16)
+    vb = rng.integers(0, 1 << 16, size=k.shape, dtype=np.uint16)
+    pool16 = rng.integers(0, 1 << 16, size=(B, 2, NUM_KV_HEADS, C, HEAD_DIM), dtype=np.uint16)
+    got = kv_append_paged_reference(pool16, table, pos, k, v, "bf16", new_bits=(kb, vb))
+    want = kv_append_reference(pool16, k[:, 0], v[:, 0], pos, "bf16", new_bits=(kb[:, 0], vb[:, 0]))
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("P", [16, 32])
+def test_appended_tokens_are_read_back_at_their_slots_and_nothing_else_changes(P):
+    """Through the separately pinned gather: slot positions[b] + t of request b
+    holds token t's encoded rows (also across a page boundary); every other
+    row of the pool keeps its bytes."""
+    rng = np.random.default_rng(52)
+    B, T, max_pages, num_pages = 3, 3, 4, 15
+    pool, k, v = _bits_case(rng, num_pages, P, B, T)
+    table = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages)
+    pos = [P - 1, 0, 2 * P + 5]          # request 0 crosses into its second page
+    got = kv_append_paged_reference(pool, table, pos, k, v, "fp8_e4m3", 0.25, 2.0)
+    touched = np.zeros((num_pages, P), dtype=bool)
+    for b in range(B):
+        rows = gather_pages(got, table[b], pos[b] + T, P)        # [2, 8, L, 128]
+        for t in range(T):
+            s = pos[b] + t
+            assert np.array_equal(rows[0, :, s], quantise_fp8(k[b, t], 0.25))
+            assert np.array_equal(rows[1, :, s], quantise_fp8(v[b, t], 2.0))
+            touched[table[b, s // P], s % P] = True
+    assert touched.sum() == B * T
+    assert np.array_equal(got.transpose(0, 3, 1, 2, 4)[~touched], pool.transpose(0, 3, 1, 2, 4)[~touched])
+
+
+def test_append_skips_slots_and_pages_out_of_range():
+    rng = np.random.default_rng(53)
+    P, B, T, max_pages, num_pages = 16, 4, 2, 2, 6
+    pool, k, v = _bits_case(rng, num_pages, P, B, T)
+    table = np.array([[0, 1], [2, -1], [3, num_pages], [4, 5]])
+    # request 0: slots -2, -1 (before the start); request 1: slots 15, 16 (16 is in
+    # page entry -1); request 2: slots 16, 17 in entry num_pages; request 3:
+    # slots 31, 32 (32 beyond max_pages * P)
+    pos = [-2, 15, 16, 31]
+    got = kv_append_paged_reference(pool, table, pos, k, v, "fp8_e4m3", 1.0, 1.0)
+    want = pool.copy()
+    want[2, 0, :, 15] = quantise_fp8(k[1, 0], 1.0)
+    want[2, 1, :, 15] = quantise_fp8(v[1, 0], 1.0)
+    want[5, 0, :, 15] = quantise_fp8(k[3, 0], 1.0)
+    want[5, 1, :, 15] = quantise_fp8(v[3, 0], 1.0)
+    assert np.array_equal(got, want)
