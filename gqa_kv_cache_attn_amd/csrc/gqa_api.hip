@@ -109,10 +109,15 @@ int device_cus(int dev) {
 // 1.25-1.45x as long as the first, and workgroups on odd XCDs 1.07-1.1x as
 // long as on even ones, reproducibly from launch to launch and whatever
 // slabs they read. These defaults (a sweep of five sets) lift the long-context
-// kernels by 1-3 points of HBM peak. Build-time knobs; shares only move
+// kernels by 1-3 points of HBM peak. With two workgroups per CU the second
+// is barely slower: a sweep of its share (780-960) was fastest at 960 on
+// both workloads (0.4-0.7% over 840). Build-time knobs; shares only move
 // range boundaries, never the result's correctness.
 #ifndef GQA_SHARE_TIER1
 #define GQA_SHARE_TIER1 840
+#endif
+#ifndef GQA_SHARE_TIER1_OF_TWO
+#define GQA_SHARE_TIER1_OF_TWO 960   // second workgroup when two share each CU
 #endif
 #ifndef GQA_SHARE_TIER2
 #define GQA_SHARE_TIER2 670
@@ -124,14 +129,15 @@ int device_cus(int dev) {
 #define GQA_SHARE_ODD 920
 #endif
 
+// a.grid_wgs must be set: the shares depend on how many workgroups share a CU.
 void set_shares(gqa::StepArgs& a, int tier_size) {
-  static const int kTier[gqa::kShareTiers] = {1000, GQA_SHARE_TIER1, GQA_SHARE_TIER2,
-                                             GQA_SHARE_TIER3};
+  int tier[gqa::kShareTiers] = {1000, GQA_SHARE_TIER1, GQA_SHARE_TIER2, GQA_SHARE_TIER3};
+  if (tier_size > 0 && a.grid_wgs == 2 * tier_size) tier[1] = GQA_SHARE_TIER1_OF_TWO;
   // tier_size 0 (unknown) or a grid of one tier: plain equal shares
   a.tier_size = tier_size > 0 ? tier_size : (1 << 28);
   for (int t = 0; t < gqa::kShareTiers; ++t) {
-    a.share[2 * t] = kTier[t];
-    a.share[2 * t + 1] = kTier[t] * GQA_SHARE_ODD / 1000;
+    a.share[2 * t] = tier[t];
+    a.share[2 * t + 1] = tier[t] * GQA_SHARE_ODD / 1000;
   }
 }
 

@@ -52,6 +52,9 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format
 #ifndef GQA_BALANCED_MIN_WAVES_PER_SIMD
 #define GQA_BALANCED_MIN_WAVES_PER_SIMD 2
 #endif
+#ifndef GQA_BALANCED_WGS_PER_CU
+#define GQA_BALANCED_WGS_PER_CU 0  // build-time override of balanced_wgs_per_cu (0: none)
+#endif
 #ifndef GQA_KV_LOAD_POLICY
 #define GQA_KV_LOAD_POLICY 2   // cache-policy bits of the K/V loads: 2 = non-temporal
 #endif
@@ -556,6 +559,18 @@ __device__ __forceinline__ void record_piece(const StepArgs& a, int head, bool w
   }
   if (first) a.head_pieces[head] = (int)slot;
   if (last) a.head_pieces[heads + head] = w;
+}
+
+// Resident workgroups per CU of the balanced grids, contiguous and paged (0:
+// as many as fit): 2 for 16-bit and fp8 caches, all that fit for INT8.
+// Measured against 3 per CU: 0.3% / 0.9% / 0.7% faster on the 64k bf16,
+// 128k fp8 and ragged f16 steps and 1.7-1.9% on fp8 page pools, but 2.5%
+// slower on the 128k INT8 step, whose byte widening needs the third
+// workgroup's waves to hide its ALU latency. One per CU won 1.2% on 64k bf16
+// and lost 6% on fp8, 2.5% on the ragged batch and 47% on INT8.
+template <int KVT>
+constexpr int balanced_wgs_per_cu() {
+  return GQA_BALANCED_WGS_PER_CU > 0 ? GQA_BALANCED_WGS_PER_CU : (KVT == kI8 ? 0 : 2);
 }
 
 // Balanced split: slabs of 64 slots per (request, KV head).

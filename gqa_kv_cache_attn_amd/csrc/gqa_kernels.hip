@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gqa_device.h"
@@ -495,6 +496,7 @@ int balanced_grid_typed() {
           &per_cu, reinterpret_cast<const void*>(&gqa_balanced_attention_kernel<QT, KVT, G>),
           kThreads, 0) != hipSuccess)
     return 0;
+  if (balanced_wgs_per_cu<KVT>() > 0) per_cu = std::min(per_cu, balanced_wgs_per_cu<KVT>());
   return cus * per_cu;
 }
 

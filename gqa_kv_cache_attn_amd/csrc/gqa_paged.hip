@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gqa_device.h"
@@ -464,6 +465,7 @@ int paged_balanced_grid_typed() {
           &per_cu, reinterpret_cast<const void*>(&gqa_paged_balanced_kernel<QT, KVT, G>), kThreads,
           0) != hipSuccess)
     return 0;
+  if (balanced_wgs_per_cu<KVT>() > 0) per_cu = std::min(per_cu, balanced_wgs_per_cu<KVT>());
   return cus * per_cu;
 }
 
