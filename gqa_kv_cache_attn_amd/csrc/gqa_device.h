@@ -209,6 +209,8 @@ struct Planes {
 // the default one they stay cached between back-to-back steps, which a model
 // that runs other layers in between never sees, and a step that starts on
 // caches full of other data ran 20% slower than with the streaming policy.
+// (The contiguous cache reads its scales a block at a time instead; see
+// load_block_scales. The paged cache reads them per tile here.)
 __device__ __forceinline__ u32x2 load_scale_quad(__amdgpu_buffer_rsrc_t r, int tok, int c1,
                                                  bool quads) {
   if (quads && (tok + 4 <= c1 || tok >= c1))
@@ -220,7 +222,8 @@ __device__ __forceinline__ u32x2 load_scale_quad(__amdgpu_buffer_rsrc_t r, int t
   return (u32x2){h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
 }
 
-template <int KVT>
+// kScales = false leaves an INT8 tile's row scales to the caller.
+template <int KVT, bool kScales = true>
 __device__ __forceinline__ void load_tile(Tile<KVT>& t, const Planes& pl, int j0, int lane) {
   const int n16 = lane & 15, grp = lane >> 4;
   const __amdgpu_buffer_rsrc_t rk = pl.k, rv = pl.v;
@@ -233,7 +236,7 @@ __device__ __forceinline__ void load_tile(Tile<KVT>& t, const Planes& pl, int j0
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       t.v[e] = __builtin_amdgcn_raw_buffer_load_b64(rv, vo + e * kHeadDim, 0, kLoadAux);
-    if constexpr (KVT == kI8) {
+    if constexpr (KVT == kI8 && kScales) {
       t.ks = load_scale_quad(pl.ks, j0 + 4 * grp, pl.c1, pl.quads);
       t.vs = load_scale_quad(pl.vs, j0 + 4 * grp, pl.c1, pl.quads);
     }
@@ -247,6 +250,37 @@ __device__ __forceinline__ void load_tile(Tile<KVT>& t, const Planes& pl, int j0
     for (int e = 0; e < 4; ++e)
       t.v[e] = __builtin_amdgcn_raw_buffer_load_b128(rv, vo + e * (2 * kHeadDim), 0, kLoadAux);
   }
+}
+
+// The bf16 row scales of a 64-slot block (four tiles) of an INT8 cache, read
+// by one wave with one 2-byte load per lane and plane: lane l holds slot
+// base + l (one 128-byte line per plane; slots at or past c1 read 0). One
+// path for every block, whatever the alignment, so a wait for these loads
+// can be counted exactly. Tile t of the block gathers its scales with lane
+// shuffles.
+struct BlockScales {
+  u32 k, v;   // bf16 bits in the low half
+};
+
+__device__ __forceinline__ BlockScales load_block_scales(const Planes& pl, int base, int lane) {
+  BlockScales s;
+  s.k = __builtin_amdgcn_raw_buffer_load_b16(pl.ks, (base + lane) * 2, 0, kLoadAux);
+  s.v = __builtin_amdgcn_raw_buffer_load_b16(pl.vs, (base + lane) * 2, 0, kLoadAux);
+  return s;
+}
+
+// Scales of slots 16 t + 4 grp .. + 3 of the block into tile `t`.
+__device__ __forceinline__ void tile_scales(Tile<kI8>& t, const BlockScales& s, int tile,
+                                            int lane) {
+  const int src = 16 * tile + 4 * (lane >> 4);
+  u32 k[4], v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    k[r] = (u32)__shfl((int)s.k, src + r);
+    v[r] = (u32)__shfl((int)s.v, src + r);
+  }
+  t.ks = (u32x2){k[0] | (k[1] << 16), k[2] | (k[3] << 16)};
+  t.vs = (u32x2){v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
 }
 
 // The QK product wants K with one token per lane (lane n16 = token, 8 dims
