@@ -66,7 +66,9 @@ __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int
 // chunk's log2-domain max M, its sum of weights l and its unnormalised output
 // (o0, o1). Ends with a barrier, so the caller may call it again for another
 // range.
-template <int QT, int KVT, int G>
+// kBlocks (INT8 cache only, for long ranges): waves take whole 64-slot
+// blocks instead of every fourth tile; see the loop below.
+template <int QT, int KVT, int G, bool kBlocks = false>
 __device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, int c0, int c1,
                                              WorkgroupLds& lds, float& M, float& lsum, float& o0,
                                              float& o1) {
@@ -119,12 +121,14 @@ __device__ __forceinline__ void attend_range(const StepArgs& a, int b, int g, in
 #pragma unroll
   for (int c = 0; c < 8; ++c) st.o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (KVT == kI8) {
+  if constexpr (KVT == kI8 && kBlocks) {
     // INT8: each wave takes whole 64-slot blocks (wave w the blocks at
     // c0 + 64 w + 256 k, four tiles each), so every 128-byte line of a scale
     // plane is read once, by one wave, with one load a block ahead. With the
     // waves' tiles interleaved, four waves read each line at different times
-    // and, streamed, it was fetched again (1.8% more HBM bytes).
+    // and, streamed, it was fetched again (1.8% more HBM bytes). Short ranges
+    // (a chunk of one block) would leave three waves idle: they keep the
+    // interleaved order.
     int base = __builtin_amdgcn_readfirstlane(c0 + 64 * wave);
     if (base < c1) {
       u32x4* sk = lds.k[wave];
@@ -327,7 +331,7 @@ __device__ __forceinline__ void balanced_unit(const StepArgs& a, const int* s_pr
     const int c0 = (s - seg_start) * kSlab;
     const int c1 = min((pe - seg_start) * kSlab, L);
     float M, lsum, o0, o1;
-    attend_range<QT, KVT, G>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
+    attend_range<QT, KVT, G, KVT == kI8>(a, b, g, c0, c1, lds, M, lsum, o0, o1);
     const size_t head = ((size_t)b * kKvHeads + g) * G + er;
     const bool whole = s == seg_start && pe == seg_end;
     const size_t slot = 2 * (size_t)u + (s == s0 ? 0 : 1);

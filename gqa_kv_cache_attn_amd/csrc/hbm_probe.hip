@@ -1,6 +1,8 @@
 // HBM measurement kernels for the roofline context of the decode kernels:
-//   - a read-only stream (16-byte loads, xor-folded so nothing is optimised
-//     away) that gives the practical read ceiling of the device, and
+//   - read-only streams (16-byte loads, xor-folded so nothing is optimised
+//     away: grid-stride, chunked, and the decode kernels' persistent split
+//     through bounded buffer descriptors) that give the practical read
+//     ceiling of the device, and
 //   - a plain copy of known size, used to scale rocprofv3's FETCH_SIZE /
 //     WRITE_SIZE counters into bytes.
 // Not part of the decode path; built into libgqa_hbm_probe.so.
@@ -48,6 +50,30 @@ __global__ __launch_bounds__(256) void read_chunks_kernel(const u32x4* __restric
   if (x == 0x9e3779b9u) sink[0] = x;
 }
 
+// The decode kernels' access pattern: workgroup w of W streams elements
+// [w n / W, (w + 1) n / W) through a buffer descriptor bounded at its range,
+// DEPTH non-temporal 16-byte loads in flight per lane.
+template <int DEPTH>
+__global__ __launch_bounds__(256) void read_split_kernel(const u32x4* __restrict__ src, uint64_t n,
+                                                         uint32_t* __restrict__ sink) {
+  const uint64_t W = gridDim.x, w = blockIdx.x;
+  const uint64_t lo = w * n / W, hi = (w + 1) * n / W;
+  const uint32_t bytes = (uint32_t)((hi - lo) * 16);   // the host keeps a range below 4 GiB
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4*>(src + lo), 0, (int)bytes, 0x00020000);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (uint32_t off = threadIdx.x * 16u; off < bytes; off += DEPTH * 256u * 16u) {
+    u32x4 v[DEPTH];
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k)   // past the range: reads 0, no traffic
+      v[k] = __builtin_amdgcn_raw_buffer_load_b128(r, off + k * 256u * 16u, 0, 2);
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) acc ^= v[k];
+  }
+  const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (x == 0x9e3779b9u) sink[0] = x;
+}
+
 __global__ __launch_bounds__(256) void copy_stream_kernel(const u32x4* __restrict__ src,
                                                           u32x4* __restrict__ dst, uint64_t n) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -73,6 +99,22 @@ __attribute__((visibility("default"))) int gqa_probe_read_chunks(const void* src
                                                                  int workgroups, hipStream_t stream) {
   hipLaunchKernelGGL(read_chunks_kernel, dim3(workgroups), dim3(256), 0, stream,
                      static_cast<const u32x4*>(src), bytes / 16, chunk_bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+// depth: 8 or 16 loads in flight per lane; bytes / workgroups must stay below 4 GiB.
+__attribute__((visibility("default"))) int gqa_probe_read_split(const void* src, uint64_t bytes,
+                                                                int depth, uint32_t* sink,
+                                                                int workgroups, hipStream_t stream) {
+  if (workgroups < 1 || bytes / 16 / (uint64_t)workgroups >= (1ull << 28) ||
+      (depth != 8 && depth != 16))
+    return (int)hipErrorInvalidValue;
+  if (depth == 8)
+    hipLaunchKernelGGL(read_split_kernel<8>, dim3(workgroups), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
+  else
+    hipLaunchKernelGGL(read_split_kernel<16>, dim3(workgroups), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(src), bytes / 16, sink);
   return (int)hipGetLastError();
 }
 

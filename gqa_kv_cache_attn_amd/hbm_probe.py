@@ -2,8 +2,10 @@
 
     python -m gqa_kv_cache_attn_amd.hbm_probe [--mode read|copy|both] [--gib 2] [--iters 20]
 
-read: a streaming read of a buffer far larger than the caches, over several
-      grid sizes; the best average is the device's practical read ceiling.
+read: streaming reads of a buffer far larger than the caches (grid-stride,
+      contiguous chunks, and the decode kernels' persistent split through
+      bounded buffer descriptors), over several grid sizes and load depths;
+      the best average is the device's practical read ceiling.
 copy: a plain copy of known size (``--gib`` read + ``--gib`` written); under
       ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` its counter readings
       give the scale between counter units and bytes.
@@ -35,6 +37,9 @@ def _lib():
     lib.gqa_probe_read_chunks.restype = ctypes.c_int
     lib.gqa_probe_read_chunks.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32,
                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.gqa_probe_read_split.restype = ctypes.c_int
+    lib.gqa_probe_read_split.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.gqa_probe_copy.restype = ctypes.c_int
     lib.gqa_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
                                    ctypes.c_void_p]
@@ -90,6 +95,18 @@ def main():
                 per_chunk[f"{chunk_kib}KiB/{wgs}wg"] = round(gbps, 1)
                 best = max(best, gbps)
         res["read_chunks_GBps"] = per_chunk
+        per_split = {}
+        for depth in (8, 16):
+            for wgs in (256, 512, 768, 1024, 2048):
+                def runs():
+                    assert lib.gqa_probe_read_split(src.data_ptr(), nbytes, depth, sink.data_ptr(),
+                                                    wgs, stream.cuda_stream) == 0
+                runs()
+                ms = _time(runs, args.iters, stream)
+                gbps = nbytes / (statistics.fmean(ms) * 1e-3) / 1e9
+                per_split[f"depth{depth}/{wgs}wg"] = round(gbps, 1)
+                best = max(best, gbps)
+        res["read_split_GBps"] = per_split
         res["read_ceiling_GBps"] = round(best, 1)
     if args.mode in ("copy", "both"):
         dst = torch.empty_like(src)
