@@ -112,7 +112,15 @@ __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, in
   c1 = __builtin_amdgcn_readfirstlane(c1);
   L = __builtin_amdgcn_readfirstlane(L);
   constexpr int Hq = kKvHeads * G;
-  const int tid = threadIdx.x;
+  int tid = threadIdx.x;
+  if constexpr (KVT == kI8) {
+    // Hide the thread index from the optimiser (an empty asm statement, no
+    // instruction): otherwise the lane-derived addresses and constants of the
+    // tile loop are hoisted out of the balanced kernel's loop over pieces and
+    // stay live across it, 171-174 VGPRs instead of 155, which leaves room
+    // for two workgroups per CU instead of the three INT8 needs.
+    asm volatile("" : "+v"(tid));
+  }
   const int lane = tid & 63;
   // Uniform per wave; saying so keeps each tile's descriptors (which depend on
   // the wave's slot) in scalar registers instead of a waterfall loop per load.

@@ -91,13 +91,17 @@ WORKLOADS = [
 ]
 
 # Paged pool, several query tokens per request: the verify pass of a step
-# with 2 draft tokens (T = 3) over 16-slot pages, the 64k bf16 shape; and a
-# single-token fp8 pool of 64-slot pages, the 128k fp8 shape.
+# with 2 draft tokens (T = 3) over 16-slot pages, the 64k bf16 shape; a
+# single-token fp8 pool of 64-slot pages, the 128k fp8 shape; and an INT8
+# pool with row scales at 16 query heads verifying one draft token (T = 2),
+# the 128k INT8 shape.
 PAGED_WORKLOADS = [
     Workload("gqa_decode_paged_b8_c65536_p16_bf16_t3", 8, 65536, 32768, 65536, "bf16", "bf16",
              q_scale=0.5, seed=1008, page_size=16, q_tokens=3),
     Workload("gqa_decode_paged_b16_c131072_p64_fp8kv_t1", 16, 131072, 65536, 131072, "bf16",
              "fp8_e4m3", k_scale=1.0 / 64, v_scale=1.0 / 64, seed=1009, page_size=64, q_tokens=1),
+    Workload("gqa_decode_paged_b16_c131072_p64_int8kv_16q_t2", 16, 131072, 65536, 131072, "bf16",
+             "int8", seed=1010, num_q_heads=16, page_size=64, q_tokens=2),
 ]
 WORKLOADS_BY_NAME = {w.name: w for w in WORKLOADS + PAGED_WORKLOADS}
 
