@@ -207,3 +207,78 @@ def test_paged_append_argument_errors():
         b.gqa_kv_append_paged(pool, table, flat[:2 * 2 * 8 * 128].view(2, 2, 8, 128), k, pos)
     torch.cuda.synchronize()
     assert torch.equal(pool, before)
+
+
+# ---------------------------------------------------------------- captured decode loop
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8_e4m3"])
+def test_captured_decode_loop_matches_eager_steps(paged, kd):
+    """One decode step captured once and replayed: append the step's new rows at
+    the current lengths, advance the lengths on the device, attend. Nothing in
+    it allocates or waits on the host, so it replays; every replay must equal
+    the same calls made eagerly on a copy of the state, and the last one the
+    oracle."""
+    b = binding()
+    fp8 = kd == "fp8_e4m3"
+    B, C, T = 4, 2048, (2 if paged else 1)
+    ks = vs = 1 / 64 if fp8 else 1.0
+    w = Workload("loop", B, C, 100, C - 8, "bf16", kd, q_scale=0.9, k_scale=ks, v_scale=vs,
+                 seed=71, page_size=16 if paged else 0, q_tokens=T)
+
+    def state():
+        inp = make_paged_inputs(w, device="cuda") if paged else make_inputs(w, device="cuda")
+        out = torch.empty_like(inp["q"])
+        if paged:
+            prep = b.prepare_gqa_decode_paged(inp["q"], inp["kv_pages"], inp["block_table"],
+                                              inp["seq_lens"], out, inp["q_scale"],
+                                              k_scale=ks, v_scale=vs)
+        else:
+            prep = b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
+                                        k_scale=ks, v_scale=vs)
+        return inp, out, prep
+
+    shape = (B, T, 8, 128) if paged else (B, 8, 128)
+    k_new = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    v_new = torch.zeros_like(k_new)
+
+    def step(inp, prep):
+        if paged:
+            b.gqa_kv_append_paged(inp["kv_pages"], inp["block_table"], k_new, v_new,
+                                  inp["seq_lens"], ks, vs)
+        else:
+            b.gqa_kv_append(inp["kv"], k_new, v_new, inp["seq_lens"], ks, vs)
+        inp["seq_lens"].add_(T)
+        b.launch_gqa_decode_prepared(prep)
+
+    g_inp, g_out, g_prep = state()       # the captured copy
+    e_inp, e_out, e_prep = state()       # the eager copy (same seed, same contents)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b.launch_gqa_decode_prepared(g_prep)   # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(g_inp, g_prep)
+
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(72)
+    for i in range(4):
+        k_new.copy_(torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16))
+        v_new.copy_(torch.randn(shape, generator=gen, device="cuda").to(torch.bfloat16))
+        graph.replay()
+        torch.cuda.synchronize()
+        step(e_inp, e_prep)                  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(g_inp["seq_lens"], e_inp["seq_lens"]), i
+        assert torch.equal(g_out.view(torch.int16), e_out.view(torch.int16)), i
+    cache = "kv_pages" if paged else "kv"
+    assert torch.equal(g_inp[cache].view(torch.uint8), e_inp[cache].view(torch.uint8))
+    if paged:
+        compare_paged(g_out, g_inp, range(B), f"captured loop paged {kd}")
+    else:
+        compare(g_out, oracle_pairs(g_inp, all_pairs(B)), g_inp, f"captured loop {kd}")
+    del graph
+    g_prep.destroy()
+    e_prep.destroy()
