@@ -60,8 +60,10 @@ struct Paging {
 // best for 16-bit and fp8 caches alike; 768 = 256 CUs x 3 resident workgroups).
 constexpr int64_t kChunkBytes = 1 << 20;
 constexpr int64_t kFillWorkgroups = 768;
-// Balanced split: host-only plans assume 256 CUs x 3 resident workgroups;
-// prepare and the convenience call use the device's own figure (capped).
+// Balanced split: host-only plans assume a nominal 256 CUs x 3 workgroups;
+// prepare and the convenience call size the grid for the device and cache
+// type (balanced_wgs_per_cu: 2 per CU for 16-bit and fp8, 3 for INT8 on
+// MI355X), capped at kMaxBalancedGrid.
 constexpr int kNominalBalancedGrid = 768;
 constexpr int kMaxBalancedGrid = 4096;
 // A dispatch counts its work-items in 32 bits: at most this many 256-thread

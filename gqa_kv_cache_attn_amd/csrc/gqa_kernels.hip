@@ -288,11 +288,13 @@ __global__ __launch_bounds__(kThreads) void gqa_combine_kernel(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Balanced split. The work of a step is 8 * sum_b ceil(L_b / 64) slabs of 64
-// slots, ordered request-major then KV head. A persistent grid of W
-// workgroups (as many as the device keeps resident) gives workgroup w the
-// slab range [w N / W, (w+1) N / W), so every workgroup streams the same
-// number of bytes whatever the length mix. A range crosses (request, KV head)
+// Balanced split. The work of a step is N = 8 * sum_b ceil(L_b / 64) slabs
+// of 64 slots, ordered request-major then KV head. A persistent grid of W
+// workgroups (all resident at once: balanced_wgs_per_cu per CU) gives
+// workgroup w the slab range [bound(w), bound(w + 1)), bound(w) = N S(w) /
+// S(W) with S(w) the summed shares of workgroups 0 .. w-1, so each workgroup
+// streams a share of the bytes matched to how fast the hardware serves it,
+// whatever the length mix. A range crosses (request, KV head)
 // boundaries: heads it covers whole are normalised and written directly; its
 // first and last piece, when they are only part of a head, become partials
 // in slots 2w and 2w + 1, which the balanced combine merges per head.

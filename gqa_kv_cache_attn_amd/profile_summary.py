@@ -34,12 +34,38 @@ _SOURCES = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace (string literals kept as
+    they are), so an edit to comments alone leaves the digest unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            if not c.isspace():
+                out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_digest(kernel: str = "gqa_balanced_attention_kernel") -> str:
-    """Digest of the sources the named kernel is built from."""
+    """Digest of the code (comments and whitespace left out) of the sources
+    the named kernel is built from."""
     h = hashlib.sha256()
     for name in _SOURCES["paged" if "paged" in kernel else "contiguous"]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
