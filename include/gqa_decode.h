@@ -135,8 +135,9 @@ typedef struct gqa_desc {
  * route 2 (balanced split, the automatic choice above capacity 64 for up to
  * 4096 requests when the cache holds at least 768 slabs of 64 slots across
  * all (request, KV head) pairs; smaller problems use the chunked split): a
- * persistent grid of num_workgroups workgroups shares the
- * step's 64-slot slabs evenly (computed on the device from the lengths);
+ * persistent grid of num_workgroups workgroups (all resident at once)
+ * shares the step's 64-slot slabs out in proportion to how fast the
+ * hardware serves each workgroup (computed on the device from the lengths);
  * heads a workgroup covers whole are written directly, the rest are merged
  * by the combine kernel. num_splits is 0 (varies per head), chunk_tokens 64. */
 typedef struct gqa_plan {
