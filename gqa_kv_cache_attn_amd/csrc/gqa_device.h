@@ -283,6 +283,36 @@ __device__ __forceinline__ void tile_scales(Tile<kI8>& t, const BlockScales& s, 
   t.vs = (u32x2){v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
 }
 
+// The same scales repacked once per block into quads: lane m (< 16) holds the
+// scales of slots 4 m .. 4 m + 3 of the block (lanes 16-63 repeat lanes 0-15),
+// so a tile gathers its quads with two shuffles per plane from one source
+// lane per lane group, instead of four. Fewer lane addresses stay live across
+// the tile loop.
+struct BlockQuads {
+  u32x2 k, v;
+};
+
+__device__ __forceinline__ BlockQuads pack_block_scales(const BlockScales& s, int lane) {
+  const int src = 4 * (lane & 15);
+  u32 k[4], v[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    k[r] = (u32)__shfl((int)s.k, src + r);
+    v[r] = (u32)__shfl((int)s.v, src + r);
+  }
+  BlockQuads q;
+  q.k = (u32x2){k[0] | (k[1] << 16), k[2] | (k[3] << 16)};
+  q.v = (u32x2){v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+  return q;
+}
+
+// Quads of slots 16 t + 4 grp .. + 3 of the block into tile `t`.
+__device__ __forceinline__ void tile_scales(Tile<kI8>& t, const BlockQuads& q, int tile, int lane) {
+  const int src = 4 * tile + (lane >> 4);
+  t.ks = (u32x2){(u32)__shfl((int)q.k[0], src), (u32)__shfl((int)q.k[1], src)};
+  t.vs = (u32x2){(u32)__shfl((int)q.v[0], src), (u32)__shfl((int)q.v[1], src)};
+}
+
 // The QK product wants K with one token per lane (lane n16 = token, 8 dims
 // per lane), the opposite of the row-per-16-lanes layout the coalesced loads
 // deliver. The wave passes its K tile through its own LDS slice: token t's

@@ -87,12 +87,13 @@ struct PagedHead {
     return pl;
   }
 
-  // Lane i: page id of the tile that starts at slot first + 64 i. Indices past
-  // the range's last page read that page (such tiles read nothing); ids are
-  // clamped into the pool, so a bad table entry can give a wrong result but
-  // never an access outside the pool.
-  __device__ __forceinline__ int page_ids(int first, int last_index, int lane) const {
-    const int idx = min((first + kStep * lane) >> shift, last_index);
+  // Lane i: page id of the tile (or block) that starts at slot first +
+  // stride i. Indices past the range's last page read that page (such tiles
+  // read nothing); ids are clamped into the pool, so a bad table entry can
+  // give a wrong result but never an access outside the pool.
+  __device__ __forceinline__ int page_ids(int first, int last_index, int lane,
+                                          int stride = kStep) const {
+    const int idx = min((first + stride * lane) >> shift, last_index);
     return min(max(table_row[idx], 0), num_pages - 1);
   }
 };
@@ -103,7 +104,12 @@ struct PagedHead {
 // log2-domain max, sum of weights and unnormalised output at dims
 // 2 (t % 64) + {0, 1}; a row that saw no slot of the range gets M = -inf,
 // l = 0. Rows >= T*G are passed too and must be ignored. Ends with a barrier.
-template <int QT, int KVT, int G, class Emit>
+//
+// kBlocks (INT8 pools of pages of at least 64 slots; the caller checks): each
+// wave takes whole 64-slot blocks, as the contiguous balanced kernel does, so
+// each 128-byte line of a scale plane is read once. Otherwise the waves take
+// interleaved tiles.
+template <int QT, int KVT, int G, bool kBlocks = false, class Emit>
 __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, int c0, int c1,
                                              int L, PagedLds& lds, Emit&& emit) {
   b = __builtin_amdgcn_readfirstlane(b);
@@ -159,44 +165,99 @@ __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, in
 #pragma unroll
   for (int c = 0; c < 8; ++c) st.o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  const int first = c0 + kTile * wave;   // this wave's tile k starts at first + 64 k
-  if (first < c1) {
-    u32x4* sk = lds.k[wave];
-    const int last_index = (c1 - 1) >> ph.shift;
-    int base = 0;                                      // tile index held by lane 0
-    int ids = ph.page_ids(first, last_index, lane);
-    auto page_of = [&](int k) -> int {                 // k is uniform and never decreases
-      if (k - base >= 64) {
-        base = k;
-        ids = ph.page_ids(first + kStep * base, last_index, lane);
+  if constexpr (KVT == kI8 && kBlocks) {
+    // Whole 64-slot blocks, wave w the blocks at c0 + 64 w + 256 k; a block
+    // lies in one page (ranges start on 64-slot boundaries), so it takes one
+    // set of descriptors, and its scales one 2-byte load per lane and plane,
+    // fetched a block ahead like its first tile.
+    int base = __builtin_amdgcn_readfirstlane(c0 + 64 * wave);
+    if (base < c1) {
+      u32x4* sk = lds.k[wave];
+      const int last_index = (c1 - 1) >> ph.shift;
+      constexpr int kBlock = 4 * kStep;              // slots between a wave's blocks
+      int kb0 = 0;                                   // block index held by lane 0
+      int ids = ph.page_ids(base, last_index, lane, kBlock);
+      const int base0 = base;
+      auto page_of_block = [&](int kb) -> int {      // kb is uniform and never decreases
+        if (kb - kb0 >= 64) {
+          kb0 = kb;
+          ids = ph.page_ids(base0 + kBlock * kb0, last_index, lane, kBlock);
+        }
+        return __builtin_amdgcn_readlane(ids, kb - kb0);
+      };
+      int kb = 0, row, row_next;
+      Planes pl = ph.planes(base, page_of_block(0), row);
+      BlockQuads sc = pack_block_scales(load_block_scales(pl, row, lane), lane);
+      Tile<KVT> ta, tb;
+      load_tile<KVT, false>(ta, pl, row, lane);
+      for (;;) {
+        const Planes pl_next = ph.planes(base + kBlock, page_of_block(kb + 1), row_next);
+        load_tile<KVT, false>(tb, pl, row + kTile, lane);          // past c1: reads 0
+        const BlockScales sc_next = load_block_scales(pl_next, row_next, lane);
+        tile_scales(ta, sc, 0, lane);
+        process_tile<QT, KVT, kRowsMax>(st, ta, qf, sk, base, lim, lane, a.scale_log2);
+        if (base + kTile >= c1) break;
+        load_tile<KVT, false>(ta, pl, row + 2 * kTile, lane);
+        tile_scales(tb, sc, 1, lane);
+        process_tile<QT, KVT, kRowsMax>(st, tb, qf, sk, base + kTile, lim, lane, a.scale_log2);
+        if (base + 2 * kTile >= c1) break;
+        load_tile<KVT, false>(tb, pl, row + 3 * kTile, lane);
+        tile_scales(ta, sc, 2, lane);
+        process_tile<QT, KVT, kRowsMax>(st, ta, qf, sk, base + 2 * kTile, lim, lane,
+                                        a.scale_log2);
+        if (base + 3 * kTile >= c1) break;
+        load_tile<KVT, false>(ta, pl_next, row_next, lane);       // the next block's first tile
+        tile_scales(tb, sc, 3, lane);
+        process_tile<QT, KVT, kRowsMax>(st, tb, qf, sk, base + 3 * kTile, lim, lane,
+                                        a.scale_log2);
+        base += kBlock;
+        ++kb;
+        if (base >= c1) break;
+        sc = pack_block_scales(sc_next, lane);
+        pl = pl_next;
+        row = row_next;
       }
-      return __builtin_amdgcn_readlane(ids, k - base);
-    };
-    Tile<KVT> ta, tb;
-    int row;
-    int j0 = first;
-    int k = 0;
-    {
-      const Planes pl = ph.planes(j0, page_of(0), row);
-      load_tile<KVT>(ta, pl, row, lane);
     }
-    for (;;) {
+  } else {
+    const int first = c0 + kTile * wave;   // this wave's tile k starts at first + 64 k
+    if (first < c1) {
+      u32x4* sk = lds.k[wave];
+      const int last_index = (c1 - 1) >> ph.shift;
+      int base = 0;                                      // tile index held by lane 0
+      int ids = ph.page_ids(first, last_index, lane);
+      auto page_of = [&](int k) -> int {                 // k is uniform and never decreases
+        if (k - base >= 64) {
+          base = k;
+          ids = ph.page_ids(first + kStep * base, last_index, lane);
+        }
+        return __builtin_amdgcn_readlane(ids, k - base);
+      };
+      Tile<KVT> ta, tb;
+      int row;
+      int j0 = first;
+      int k = 0;
       {
-        const Planes pl = ph.planes(j0 + kStep, page_of(k + 1), row);
-        load_tile<KVT>(tb, pl, row, lane);
-      }
-      process_tile<QT, KVT, kRowsMax>(st, ta, qf, sk, j0, lim, lane, a.scale_log2);
-      j0 += kStep;
-      ++k;
-      if (j0 >= c1) break;
-      {
-        const Planes pl = ph.planes(j0 + kStep, page_of(k + 1), row);
+        const Planes pl = ph.planes(j0, page_of(0), row);
         load_tile<KVT>(ta, pl, row, lane);
       }
-      process_tile<QT, KVT, kRowsMax>(st, tb, qf, sk, j0, lim, lane, a.scale_log2);
-      j0 += kStep;
-      ++k;
-      if (j0 >= c1) break;
+      for (;;) {
+        {
+          const Planes pl = ph.planes(j0 + kStep, page_of(k + 1), row);
+          load_tile<KVT>(tb, pl, row, lane);
+        }
+        process_tile<QT, KVT, kRowsMax>(st, ta, qf, sk, j0, lim, lane, a.scale_log2);
+        j0 += kStep;
+        ++k;
+        if (j0 >= c1) break;
+        {
+          const Planes pl = ph.planes(j0 + kStep, page_of(k + 1), row);
+          load_tile<KVT>(ta, pl, row, lane);
+        }
+        process_tile<QT, KVT, kRowsMax>(st, tb, qf, sk, j0, lim, lane, a.scale_log2);
+        j0 += kStep;
+        ++k;
+        if (j0 >= c1) break;
+      }
     }
   }
 
@@ -330,10 +391,11 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_combine_kernel(StepArgs a)
 }
 
 // Balanced split over the logical slots (the contiguous kernel's scheme):
-// workgroup w takes slabs [w N / W, (w+1) N / W); heads covered whole are
+// workgroup w takes slabs [bound(w), bound(w + 1)); heads covered whole are
 // written directly, first and last pieces go to slots 2w and 2w + 1 of
-// kRowsMax rows each.
-template <int QT, int KVT, int G>
+// kRowsMax rows each. kBlocks: see attend_paged (INT8 pools of pages of at
+// least 64 slots).
+template <int QT, int KVT, int G, bool kBlocks>
 __global__ __launch_bounds__(kThreads, GQA_PAGED_MIN_WAVES_PER_SIMD) void
 gqa_paged_balanced_kernel(StepArgs a) {
   using E = Elem<QT>;
@@ -353,7 +415,6 @@ gqa_paged_balanced_kernel(StepArgs a) {
   if (w == 0)   // the combine kernel reads the same prefix
     for (int i = tid; i <= B; i += kThreads) a.slab_prefix[i] = s_pref[i];
 
-  const int ed = lane * 2;
   const int64_t total = share_prefix(a, W);
   const int s0 = balanced_bound(a, w, N, total);
   const int s1 = balanced_bound(a, w + 1, N, total);
@@ -383,9 +444,11 @@ gqa_paged_balanced_kernel(StepArgs a) {
     const bool whole = s == seg_start && pe == seg_end;
     const size_t slot = 2 * (size_t)w + (s == s0 ? 0 : 1);
     record_piece(a, b * kKvHeads + g, whole, s == seg_start, pe == seg_end, slot, w);
-    attend_paged<QT, KVT, G>(a, b, g, c0, c1, L, lds,
-                             [&](int row, float M, float lsum, float o0, float o1) {
+    attend_paged<QT, KVT, G, kBlocks>(a, b, g, c0, c1, L, lds,
+                                      [&](int row, float M, float lsum, float o0, float o1) {
       if (row >= R) return;
+      int ed = lane * 2;
+      if constexpr (kBlocks) asm volatile("" : "+v"(ed));   // not hoisted across pieces
       if (whole) {
         const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
         E::store2(static_cast<char*>(a.out) + (query_row<G>(b, g, row, T) * kHeadDim + ed) * 2,
@@ -441,8 +504,17 @@ hipError_t enqueue_paged_typed(const StepArgs& a, hipStream_t stream, hipEvent_t
   hipError_t e;
   const dim3 heads((unsigned)a.batch * kKvHeads);
   if (a.grid_wgs > 0) {
-    hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G>), dim3(a.grid_wgs), dim3(kThreads), 0,
-                       stream, a);
+    // INT8 pools of pages of at least 64 slots: whole 64-slot blocks per wave.
+    bool blocks = false;
+    if constexpr (KVT == kI8) {
+      blocks = a.page_shift >= 6;
+      if (blocks)
+        hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, true>), dim3(a.grid_wgs),
+                           dim3(kThreads), 0, stream, a);
+    }
+    if (!blocks)
+      hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, false>), dim3(a.grid_wgs),
+                         dim3(kThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_mid != nullptr && (e = hipEventRecord(ev_mid, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL((gqa_paged_balanced_combine_kernel<QT, G>), heads, dim3(kThreads), 0, stream,
@@ -470,7 +542,7 @@ int paged_balanced_grid_typed() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&gqa_paged_balanced_kernel<QT, KVT, G>), kThreads,
+          &per_cu, reinterpret_cast<const void*>(&gqa_paged_balanced_kernel<QT, KVT, G, false>), kThreads,
           0) != hipSuccess)
     return 0;
   if (balanced_wgs_per_cu<KVT>() > 0) per_cu = std::min(per_cu, balanced_wgs_per_cu<KVT>());

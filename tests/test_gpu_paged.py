@@ -61,14 +61,27 @@ def test_paged_parity_on_every_route(qd, kd, hq, T, P, num_splits):
 
 @pytest.mark.parametrize("qd,kd,hq,T", PCASES, ids=PIDS)
 @pytest.mark.parametrize("case", ["fewer_slabs_than_workgroups", "one_long_head", "mixed_with_empty"])
-def test_paged_balanced_split_partitions(qd, kd, hq, T, case):
+@pytest.mark.parametrize("P", [32, 64])
+def test_paged_balanced_split_partitions(qd, kd, hq, T, case, P):
+    _balanced_partition_case(qd, kd, hq, T, case, P)
+
+
+@pytest.mark.parametrize("qd,T", [("bf16", 2), ("f16", 5)])
+@pytest.mark.parametrize("case", ["fewer_slabs_than_workgroups", "one_long_head", "mixed_with_empty"])
+@pytest.mark.parametrize("P", [128, 256])
+def test_paged_int8_block_order_on_large_pages(qd, T, case, P):
+    """int8 pools with pages of 64 slots or more walk 64-slot blocks."""
+    _balanced_partition_case(qd, "int8", 16, T, case, P)
+
+
+def _balanced_partition_case(qd, kd, hq, T, case, P):
     if case == "fewer_slabs_than_workgroups":
         B, C, lens = 6, 4096, [T, 65, 200, 17 + T, 128, 129]
     elif case == "one_long_head":
         B, C, lens = 1, 70000, [69999]
     else:
         B, C, lens = 7, 5000, [0, 4999, T, 0, 5000, 2500, 64]
-    w = _pw(qd, kd, hq, T, C=C, B=B, P=32, seed=230 + len(case))
+    w = _pw(qd, kd, hq, T, C=C, B=B, P=P, seed=230 + len(case) + P)
     inp = make_paged_inputs(w, device="cuda", seq_lens=torch.tensor(lens, dtype=torch.int32))
     out = torch.full_like(inp["q"], float("nan"))
     out, prep = run_paged(inp, "prepared", out=out)
@@ -91,13 +104,14 @@ def test_paged_short_route(qd, kd, hq, T):
 
 @pytest.mark.parametrize("kd", ["bf16", "fp8_e4m3", "int8"])
 @pytest.mark.parametrize("num_splits", [None, 1, 4])
-def test_paged_garbage_outside_the_prefix_is_never_read(kd, num_splits):
+@pytest.mark.parametrize("P", [32, 128])
+def test_paged_garbage_outside_the_prefix_is_never_read(kd, num_splits, P):
     """NaN in every page no request uses, and in every slot past a length."""
     hq = 16 if kd == "int8" else 32
-    w = _pw("bf16", kd, hq, 2, C=700, B=4, P=32, seed=260)
+    w = _pw("bf16", kd, hq, 2, C=700, B=4, P=P, seed=260)
     lens = torch.tensor([2, 250, 333, 699], dtype=torch.int32)
     inp = make_paged_inputs(w, device="cuda", seq_lens=lens)
-    pool, table, P = inp["kv_pages"], inp["block_table"], 32
+    pool, table = inp["kv_pages"], inp["block_table"]
     used = torch.zeros(pool.shape[0], dtype=torch.bool, device="cuda")
     nan = {"fp8_e4m3": 0x7F, "int8": 127}.get(kd, float("nan"))
     for b, L in enumerate(lens.tolist()):
