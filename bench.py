@@ -14,7 +14,7 @@ duration from HIP events recorded on the launch stream around every timed
 launch, against 8 TB/s), cold-cache microseconds per call, and the CPU
 oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps 50] [--warmup 10] [--workload NAME] [--num-splits N]
+    python bench.py [--steps 50] [--warmup 200] [--workload NAME] [--num-splits N]
 """
 
 from __future__ import annotations
@@ -40,7 +40,9 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; the clocks take some tens of milliseconds "
+                         "of steady load to settle after the idle input setup")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--num-splits", type=int, default=0, help="0 = automatic")
     ap.add_argument("--fused-combine", action="store_true",
