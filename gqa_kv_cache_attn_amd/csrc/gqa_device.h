@@ -525,13 +525,39 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// NB partial O rows base + j0 + u (u < NB) of a merge, loaded together and
+// accumulated with their weights, which lane j of wk holds for row base + j.
+// Rows at or past cnt get weight 0 and read the fallback row instead.
+template <int NB, typename RowFn>
+__device__ __forceinline__ void merge_batch(const float2* po, RowFn& row, size_t fallback, int base,
+                                            int j0, int cnt, float wk, int lane, float& o0,
+                                            float& o1) {
+  float f[NB];
+  float2 v[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int j = j0 + u;
+    f[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), min(j, 63)));
+    if (j >= cnt) f[u] = 0.f;
+    const size_t r = f[u] != 0.f ? row(base + j) : fallback;
+    v[u] = po[r * (kHeadDim / 2) + lane];
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    o0 += f[u] * v[u].x;
+    o1 += f[u] * v[u].y;
+  }
+}
+
 // Log-sum-exp merge of n partial rows of one query head, run by one wave
 // (lane l owns dims 2l and 2l + 1):
 //   M = max_k m_k,  out = v_scale * sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k
 // row(k) gives the k-th partial row. A row whose max is -inf is empty (a
 // workgroup that had no slabs marked it): it gets weight 0 and its O row,
 // possibly stale, is never read. The (m, l) pairs of 64 rows at a time are
-// loaded one per lane, so the whole merge costs two dependent loads.
+// loaded one per lane; the O rows follow in batches of 32, 16 and then 8
+// independent loads, so a head split into 64 pieces (one request spread over
+// the whole grid) waits for two rounds of loads, not eight.
 template <int QT, typename RowFn>
 __device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, char* outp) {
   using E = Elem<QT>;
@@ -554,23 +580,15 @@ __device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, 
       }
     }
     const int cnt = min(64, n - base);
-    for (int j0 = 0; j0 < cnt; j0 += 8) {   // 8 independent row loads in flight
-      float f[8];
-      float2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = j0 + u;
-        f[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), min(j, 63)));
-        if (j >= cnt) f[u] = 0.f;
-        const size_t r = f[u] != 0.f ? row(base + j) : fallback;
-        v[u] = po[r * (kHeadDim / 2) + lane];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        o0 += f[u] * v[u].x;
-        o1 += f[u] * v[u].y;
-      }
+    int j0 = 0;
+    for (; cnt - j0 >= 32; j0 += 32)
+      merge_batch<32>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
+    if (cnt - j0 >= 16) {
+      merge_batch<16>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
+      j0 += 16;
     }
+    for (; j0 < cnt; j0 += 8)
+      merge_batch<8>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
   }
   const float inv = a.v_scale / wave_sum(lloc);
   E::store2(outp, o0 * inv, o1 * inv);
