@@ -343,7 +343,9 @@ GQA_API gqa_status_t gqa_validate_args_int8(const gqa_desc_t* desc, const void* 
  * (num_splits as for prepare_gqa_decode). Runs without a GPU, so a balanced
  * plan assumes a nominal 768 workgroups (256 CUs x 3); prepare sizes the grid
  * for the device and the cache type (on MI355X 512 workgroups for 16-bit and
- * fp8 caches, up to 768 for INT8) and reports it in its plan. */
+ * fp8 caches, up to 768 for INT8) and reports it in its plan. With a 16-bit or
+ * INT8 cache, a single request or a cache of at most 256 MiB of K+V at
+ * capacity takes one workgroup per CU instead (256 here and on MI355X). */
 GQA_API gqa_status_t gqa_plan_decode(const gqa_desc_t* desc, int32_t num_splits,
                                      gqa_plan_t* plan);
 

@@ -142,6 +142,12 @@ def balanced_ws(B, G=768, rows_per_slot=4):
     return 2 * G * rows_per_slot * 130 * 4 + ((4 * (B + 1 + 2 * 8 * B) + 255) // 256) * 256
 
 
+def nominal_balanced_grid(B, C, slot_bytes=2 * 128 * 2):
+    """Host-only plans: 256 CUs x 3 workgroups, or (16-bit and INT8 caches)
+    one per CU for a single request or at most 256 MiB of K+V at capacity."""
+    return 256 if B == 1 or B * 8 * C * slot_bytes <= 256 << 20 else 768
+
+
 @pytest.mark.parametrize("C", [65, 100, 1000, 1024, 8192, 65536, 131072])
 @pytest.mark.parametrize("B", [1, 8, 32, 4096])
 def test_auto_plan_is_the_balanced_split(B, C):
@@ -149,8 +155,23 @@ def test_auto_plan_is_the_balanced_split(B, C):
     if B * 8 * -(-C // 64) < 768:      # too small to fill the grid: chunked split
         assert p["route"] == 1
         return
-    assert p == {"route": 2, "num_splits": 0, "chunk_tokens": 64, "num_workgroups": 768,
-                 "workspace_bytes": balanced_ws(B)}
+    G = nominal_balanced_grid(B, C)
+    assert p == {"route": 2, "num_splits": 0, "chunk_tokens": 64, "num_workgroups": G,
+                 "workspace_bytes": balanced_ws(B, G)}
+
+
+@pytest.mark.parametrize("kv,slot", [(b.GQA_BF16, 512), (b.GQA_FP8_E4M3, 256),
+                                     (b.GQA_INT8_ROWSCALE, 260)])
+def test_small_problems_take_one_balanced_workgroup_per_cu(kv, slot):
+    """16-bit and INT8 caches; fp8 keeps the resident grid."""
+    hq = 16 if kv == b.GQA_INT8_ROWSCALE else 32
+    ks = 1 / 64 if kv == b.GQA_FP8_E4M3 else 1.0
+    for B, C in [(1, 131072), (1, 1 << 20), (2, 65536), (4, 32768), (16, 4096), (64, 4096),
+                 (8, 65536)]:
+        p = b.gqa_plan(desc(batch=B, capacity=C, kv=kv, hq=hq, ks=ks, vs=ks))
+        assert p["route"] == 2
+        small = kv != b.GQA_FP8_E4M3 and (B == 1 or B * 8 * C * slot <= 256 << 20)
+        assert p["num_workgroups"] == (256 if small else 768), (B, C)
 
 
 @pytest.mark.parametrize("C", [65, 1000, 8192, 65536, 131072])
