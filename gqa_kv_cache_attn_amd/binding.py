@@ -161,8 +161,16 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+# torch's current-stream lookup that returns the raw handle without building
+# a Stream object (about a microsecond less per launch); the public call is
+# the fallback where this build of torch lacks it.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_handle(stream, device) -> int:
     if stream is None:
+        if _raw_current_stream is not None:
+            return _raw_current_stream(device.index)
         stream = torch.cuda.current_stream(device)
     if isinstance(stream, int):
         return stream
@@ -230,6 +238,7 @@ class GqaPrepared:
         self._handle = handle
         self.tensors = tensors   # keeps q/kv/seq_lens/out alive as long as the handle
         self.desc = desc
+        self.device = tensors["O"].device
 
     @property
     def handle(self) -> int:
@@ -376,8 +385,7 @@ def prepare_gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_tabl
 
 def launch_gqa_decode_prepared(prepared: GqaPrepared, stream=None) -> torch.Tensor:
     """Enqueue the prepared step (no allocation, no host sync); returns O."""
-    dev = prepared.out.device
-    _check(_launch(prepared.handle, _stream_handle(stream, dev)))
+    _check(_launch(prepared.handle, _stream_handle(stream, prepared.device)))
     return prepared.out
 
 
