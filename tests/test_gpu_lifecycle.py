@@ -177,3 +177,31 @@ def test_convenience_calls_with_different_plans_share_the_workspace_safely():
         out, _ = run_decode(inp, "convenience")
         pairs = all_pairs(B) if B <= 8 else [(b, (3 * b) % 8) for b in range(B)]
         compare(out, oracle_pairs(inp, pairs), inp, f"workspace reuse {i} (B={B}, C={C}, {kd})")
+
+
+@pytest.mark.parametrize("kd,hq,B,C,one_per_cu", [
+    ("bf16", 32, 1, 65536, True),        # a single request
+    ("int8", 16, 1, 16384, True),
+    ("bf16", 32, 16, 4096, True),        # 256 MiB of K+V at capacity
+    ("fp8_e4m3", 32, 1, 65536, False),   # fp8 keeps the resident grid
+    ("bf16", 32, 8, 32768, False),       # 512 MiB at capacity
+])
+def test_balanced_grid_follows_the_problem_size(kd, hq, B, C, one_per_cu):
+    """prepare sizes the balanced grid for the device: one workgroup per CU for
+    small 16-bit / INT8 problems, every resident slot otherwise; both give the
+    oracle's result."""
+    inp = _inputs(B=B, C=C, kd=kd, hq=hq, seed=40 + B)
+    out = torch.full_like(inp["q"], float("nan"))
+    prep = _prepare(inp, out)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    W = prep.plan["num_workgroups"]
+    assert prep.plan["route"] == 2
+    if one_per_cu:
+        assert W == cus, (W, cus)
+    else:
+        assert W > cus and W % cus == 0, (W, cus)
+    binding().launch_gqa_decode_prepared(prep)
+    torch.cuda.synchronize()
+    pairs = [(b, g) for b in range(B) for g in range(8)][:16]
+    compare(out, oracle_pairs(inp, pairs), inp, f"grid {W} {kd} B={B} C={C}")
+    prep.destroy()
