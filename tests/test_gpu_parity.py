@@ -336,3 +336,27 @@ def test_batch_zero_is_a_no_op():
     out = b.gqa_decode(q, kv, lens)
     assert out.shape == (0, 32, 128)
 
+
+
+@pytest.mark.parametrize("kd,hq", [("bf16", 32), ("int8", 16)])
+def test_maximum_capacity_every_slot_valid(kd, hq):
+    """The largest accepted capacity (2^22 slots) with every slot valid: the last
+    KV head's planes start 15 GiB (bf16) / 7.5 GiB (INT8) into the cache.
+    q_scale = 4 concentrates each row's weights on a few dozen slots spread
+    over the whole range (dropping its upper half would move outputs by ~0.3),
+    so a wrong offset anywhere in it shows. Automatic (balanced, one request:
+    one workgroup per CU) and a 64-way chunked split."""
+    C = 1 << 22
+    w = Workload(f"max_capacity_{kd}", 1, C, C, C, "bf16", kd, q_scale=4.0, seed=2222,
+                 num_q_heads=hq)
+    inp = make_inputs(w, device="cuda")
+    assert int(inp["seq_lens"][0]) == C
+    ref = oracle_pairs(inp, [(0, 7), (0, 0)])
+    for ns in (None, 64):
+        out = torch.full_like(inp["q"], float("nan"))
+        out, prep = run_decode(inp, "prepared", num_splits=ns, out=out)
+        assert prep.plan["route"] == (2 if ns is None else 1)
+        compare(out, ref, inp, f"max capacity {kd} S={ns}")
+        prep.destroy()
+    del inp
+    torch.cuda.empty_cache()
