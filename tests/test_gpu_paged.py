@@ -19,8 +19,8 @@ from gpu_util import (
     run_decode,
     run_paged,
 )
-from gqa_kv_cache_attn_amd.inputs import PAGED_WORKLOADS, make_inputs, make_paged_inputs
-from oracle import gqa_decode_head
+from gqa_kv_cache_attn_amd.inputs import PAGED_WORKLOADS, make_inputs, make_paged_inputs, storage_bits
+from oracle import decode_int8_rows, decode_storage, gqa_decode_head
 
 pytestmark = pytest.mark.gpu
 
@@ -248,3 +248,53 @@ def test_paged_argument_errors_enqueue_nothing():
         b.gqa_decode_paged(*args, 1.0, alias, kv_scales=inp["kv_scales"])
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
+
+
+def _head_rows(inp, b, plane, g, L):
+    """Decoded fp64 rows [L, 128] of KV head g of request b, gathered page by page
+    through the block table."""
+    P = inp["page_size"]
+    n = -(-L // P)
+    ids = inp["block_table"][b, :n].long()
+    rows = inp["kv_pages"][:, plane, g].index_select(0, ids).reshape(n * P, -1)[:L]
+    if inp["kv_dtype"] == "int8":
+        sc = inp["kv_scales"][:, plane, g].index_select(0, ids).reshape(n * P)[:L]
+        return decode_int8_rows(storage_bits(rows), storage_bits(sc))
+    return decode_storage(storage_bits(rows), inp["kv_dtype"])
+
+
+@pytest.mark.parametrize("kd,hq,T,P", [("bf16", 32, 1, 16), ("int8", 16, 2, 64)])
+def test_paged_maximum_capacity_every_slot_valid(kd, hq, T, P):
+    """A request as long as the largest accepted capacity (2^22 slots) in a
+    shuffled pool: 262144 pages of 16 slots (bf16, a 16 GiB pool) or 65536 of 64
+    (INT8, the block order), so page offsets pass 2^31 bytes. A large q_scale
+    (4; 8 for INT8, whose k_scale here is 0.5) concentrates the weights on a
+    few dozen slots spread over the range.
+    Oracle: the contiguous definition on the head's rows gathered through the
+    table, each token with its causal prefix."""
+    C = 1 << 22
+    w = _pw("bf16", kd, hq, T, C=C, B=1, P=P, seed=2424, q_scale=8.0 if kd == "int8" else 4.0)
+    inp = make_paged_inputs(w, device="cuda", seq_lens=torch.tensor([C], dtype=torch.int32))
+    G = hq // 8
+    q = decode_storage(storage_bits(inp["q"][0]), "bf16")          # [T, Hq, 128]
+    refs = {}
+    for g in (0, 7):
+        k, v = _head_rows(inp, 0, 0, g, C), _head_rows(inp, 0, 1, g, C)
+        refs[g] = np.stack([gqa_decode_head(q[t, G * g:G * g + G], k[:C - T + 1 + t],
+                                            v[:C - T + 1 + t], inp["q_scale"], inp["k_scale"],
+                                            inp["v_scale"]) for t in range(T)])
+        del k, v
+    for ns in (None, 64):
+        out = torch.full_like(inp["q"], float("nan"))
+        out, prep = run_paged(inp, "prepared", num_splits=ns, out=out)
+        assert prep.plan["route"] == (2 if ns is None else 1)
+        got = decoded_out(out, "bf16")[0]
+        for g, ref in refs.items():
+            err = np.abs(got[:, G * g:G * g + G] - ref)
+            assert np.all(np.isfinite(err)), (g, ns)
+            assert (err - out_ulp(ref, "bf16")).max() <= 2e-3, (g, ns, err.max())
+        print(f"[parity] paged max capacity {kd} P={P} T={T} S={ns}: "
+              f"max_abs_ref={max(np.abs(r).max() for r in refs.values()):.3e}", flush=True)
+        prep.destroy()
+    del inp
+    torch.cuda.empty_cache()
