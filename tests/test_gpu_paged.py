@@ -298,3 +298,18 @@ def test_paged_maximum_capacity_every_slot_valid(kd, hq, T, P):
         prep.destroy()
     del inp
     torch.cuda.empty_cache()
+
+
+def test_paged_batch_of_4096_requests():
+    """The most requests the paged balanced split takes (one LDS prefix entry per
+    request), with ragged lengths and two query tokens."""
+    B = 4096
+    w = _pw("bf16", "bf16", 32, 2, C=256, B=B, P=16, seed=4096)
+    lens = torch.randint(2, 257, (B,), generator=torch.Generator().manual_seed(7), dtype=torch.int32)
+    inp = make_paged_inputs(w, device="cuda", seq_lens=lens)
+    out = torch.full_like(inp["q"], float("nan"))
+    out, prep = run_paged(inp, "prepared", out=out)
+    assert prep.plan["route"] == 2
+    compare_paged(out, inp, list(range(0, B, 211)) + [B - 1], "paged batch 4096")
+    assert torch.isfinite(out.float()).all()
+    prep.destroy()

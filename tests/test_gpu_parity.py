@@ -360,3 +360,20 @@ def test_maximum_capacity_every_slot_valid(kd, hq):
         prep.destroy()
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("B,route", [(4096, 2), (4097, 1)])
+def test_batch_limits(B, route):
+    """4096 requests, the most the balanced split takes (its slab prefix has
+    one LDS entry per request), and 4097, which the automatic plan hands to
+    the chunked split. Ragged lengths U[1, 256]; oracle on a sample of heads
+    that includes the first and last request."""
+    w = Workload(f"batch_{B}", B, 256, 1, 256, "bf16", "bf16", q_scale=0.8, seed=B)
+    inp = make_inputs(w, device="cuda")
+    out = torch.full_like(inp["q"], float("nan"))
+    out, prep = run_decode(inp, "prepared", out=out)
+    assert prep.plan["route"] == route
+    pairs = [(b, (3 * b) % 8) for b in list(range(0, B, 97)) + [B - 2, B - 1]]
+    compare(out, oracle_pairs(inp, pairs), inp, f"batch {B}")
+    assert torch.isfinite(out.float()).all()
+    prep.destroy()
