@@ -100,6 +100,18 @@ def read_traffic(kernel, workload, num_splits):
         return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_paged(inp, w, budget_s):
     """Time the paged fp64 oracle (as it stands) one request at a time until the budget."""
     import numpy as np
@@ -141,6 +153,9 @@ def cpu_baseline_paged(inp, w, budget_s):
         "sample": f"{done} of {w.batch} requests of {w.name}, {nbytes / 1e6:.1f} MB of algorithmic "
                   f"bytes, {spent:.2f} s (fp64 numpy incl. decoding the stored pages and the "
                   f"slot-by-slot gather; D2H copy excluded)",
+        "seconds": round(spent, 3),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
     }
 
 
@@ -191,6 +206,7 @@ def cpu_baseline(inp, w, budget_s):
                   f"(fp64 numpy incl. decoding the stored {w.kv_dtype} values; D2H copy excluded)",
         "seconds": round(spent, 3),
         "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
     }
 
 
