@@ -9,7 +9,7 @@ Modules:
   gqa_oracle  vectorised fp64 numpy definition of the decode step, plus the
               exact decoders for the stored KV/query formats.
   brute       pure-Python loops (math.fsum / math.exp) for tiny inputs.
-  kv_append   the cache write before a decode step (fp8 quantise-on-write).
+  kv_append   the cache write before a decode step (fp8 and INT8 quantise-on-write).
   paged       decode over a paged cache (page pool + block table) with T
               query tokens per request, causal among themselves, and the
               append of T new tokens per request into the pool.

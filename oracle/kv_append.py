@@ -18,13 +18,23 @@ sides take the rounding decision identically); the result is rounded to
 nearest, ties to even; magnitudes at or above 448 (the largest finite E4M3FN
 value) saturate to +-448 instead of becoming NaN; a NaN input stores the NaN
 code 0x7F; positions outside [0, capacity) write nothing.
+
+An INT8 cache (the Orin Qwen3-VL doc, "INT8 KV cache": INT8 mirrors with one
+BF16 scale per (position, KV head) row) is written row by row. The doc does
+not say how a row is quantised; the same doc quantises its INT8 weights
+symmetrically with scale = amax / 127 ("Weight quantization" table), and that
+reading is taken per row: y = x / k_scale (or v_scale), scale = max|y| / 127
+rounded to bf16, code = y / scale rounded to the nearest integer (ties to
+even) and clamped to +-127. Every division is an fp32 division and every
+rounding decision is taken on fp32 values, the kernel's precision. A row
+whose bf16 scale is 0 (all zeros) stores code 0.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-from .gqa_oracle import HEAD_DIM, NUM_KV_HEADS
+from .gqa_oracle import HEAD_DIM, NUM_KV_HEADS, decode_bf16_bits
 
 E4M3_MAX = 448.0
 
@@ -95,3 +105,56 @@ def kv_append_reference(kv_bits: np.ndarray, k_new_f32: np.ndarray, v_new_f32: n
             out[b, 0, :, p, :] = new_bits[0][b]
             out[b, 1, :, p, :] = new_bits[1][b]
     return out
+
+
+INT8_MAX = 127
+
+
+def f32_to_bf16_bits(values_f32) -> np.ndarray:
+    """Round finite fp32 values to bfloat16 (nearest, ties to even); bit patterns.
+
+    bf16 keeps the sign, the 8-bit exponent and the top 7 fraction bits of an
+    fp32. Rounding the dropped 16 bits: add just under half of the kept
+    unit (0x7FFF), plus one more when the kept part is odd, so an exact half
+    goes to the even neighbour; a carry out of the fraction moves into the
+    exponent, which is the next binade's correct value.
+    """
+    b = np.asarray(values_f32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def quantise_int8_rows(values_f32, scale: float):
+    """Rows [..., 128] of fp32 values -> (int8 codes [..., 128], bf16 scale bits [...]).
+
+    y = x / scale; s = bf16(max|y| / 127); code = rint(y / s) clamped to
+    +-127 (0 where s is 0). All arithmetic in fp32 (see the module notes).
+    """
+    x = np.asarray(values_f32, dtype=np.float32)
+    with np.errstate(all="ignore"):
+        y = (x / np.float32(scale)).astype(np.float32)
+        amax = np.max(np.abs(y), axis=-1)
+        s_bits = f32_to_bf16_bits((amax / np.float32(INT8_MAX)).astype(np.float32))
+        s = decode_bf16_bits(s_bits).astype(np.float32)   # exact
+        q = np.rint((y / s[..., None]).astype(np.float32))   # np.rint: ties to even
+    q = np.where(s[..., None] > 0, q, 0.0)
+    codes = np.clip(q, -INT8_MAX, INT8_MAX).astype(np.int8)
+    return codes, s_bits
+
+
+def kv_append_int8_reference(kv_codes, scale_bits, k_new_f32, v_new_f32, positions,
+                             k_scale: float = 1.0, v_scale: float = 1.0):
+    """Return copies of an INT8 cache (codes [B,2,8,C,128], bf16 scale bits
+    [B,2,8,C]) after appending one token per request: the K row of KV head g
+    of request b goes to slot positions[b] of plane 0 with its row scale, the
+    V row to plane 1. Positions outside [0, C) write nothing."""
+    codes = np.array(kv_codes, copy=True)
+    scales = np.array(scale_bits, copy=True)
+    B, _, H, C, D = codes.shape
+    assert H == NUM_KV_HEADS and D == HEAD_DIM and scales.shape == (B, 2, H, C)
+    for b in range(B):
+        p = int(positions[b])
+        if p < 0 or p >= C:
+            continue
+        codes[b, 0, :, p, :], scales[b, 0, :, p] = quantise_int8_rows(k_new_f32[b], k_scale)
+        codes[b, 1, :, p, :], scales[b, 1, :, p] = quantise_int8_rows(v_new_f32[b], v_scale)
+    return codes, scales

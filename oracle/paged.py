@@ -43,7 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 from .gqa_oracle import HEAD_DIM, NUM_KV_HEADS, gqa_decode_head
-from .kv_append import quantise_fp8
+from .kv_append import quantise_fp8, quantise_int8_rows
 
 
 def gather_pages(kv_pages: np.ndarray, table_row, length: int, page_size: int) -> np.ndarray:
@@ -145,3 +145,33 @@ def kv_append_paged_reference(pool_bits: np.ndarray, block_table, positions, k_n
                 out[page, 0, :, row, :] = new_bits[0][b][t]
                 out[page, 1, :, row, :] = new_bits[1][b][t]
     return out
+
+
+def kv_append_paged_int8_reference(pool_codes, pool_scale_bits, block_table, positions, k_new_f32,
+                                   v_new_f32, k_scale: float = 1.0, v_scale: float = 1.0):
+    """Return copies of an INT8 pool (codes [num_pages, 2, 8, P, 128], bf16
+    scale bits [num_pages, 2, 8, P]) after appending T tokens per request,
+    each row quantised as in kv_append.quantise_int8_rows. Slots and pages
+    are found as in kv_append_paged_reference; tokens are written in (b, t)
+    order."""
+    codes = np.array(pool_codes, copy=True)
+    scales = np.array(pool_scale_bits, copy=True)
+    num_pages, _, H, P, D = codes.shape
+    assert H == NUM_KV_HEADS and D == HEAD_DIM and scales.shape == (num_pages, 2, H, P)
+    table = np.asarray(block_table)
+    B, max_pages = table.shape
+    T = np.asarray(k_new_f32).shape[1]
+    for b in range(B):
+        for t in range(T):
+            s = int(positions[b]) + t
+            if s < 0 or s >= max_pages * P:
+                continue
+            page = int(table[b, s // P])
+            if not 0 <= page < num_pages:
+                continue
+            row = s % P
+            codes[page, 0, :, row, :], scales[page, 0, :, row] = \
+                quantise_int8_rows(k_new_f32[b][t], k_scale)
+            codes[page, 1, :, row, :], scales[page, 1, :, row] = \
+                quantise_int8_rows(v_new_f32[b][t], v_scale)
+    return codes, scales

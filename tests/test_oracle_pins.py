@@ -379,3 +379,131 @@ def test_int8_row_scales_act_per_token():
         gap = qrows[r, 0] * 10 * (0.25 - 0.5) / math.sqrt(HEAD_DIM)
         w1 = 1 / (1 + math.exp(-gap))
         assert out[r, 1] == pytest.approx((1 - w1) * 40.0 + w1 * (-3.75), rel=1e-14)
+
+
+# ---------------------------------------------------------------- KV append (INT8 rows)
+from fractions import Fraction  # noqa: E402
+
+from oracle.kv_append import (  # noqa: E402
+    f32_to_bf16_bits,
+    kv_append_int8_reference,
+    quantise_int8_rows,
+)
+
+
+def _bf16_bits_torch(x32):
+    return torch.from_numpy(np.asarray(x32, np.float32)).to(torch.bfloat16).view(torch.int16) \
+        .numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch():
+    """Library special case: torch's fp32 -> bf16 cast rounds to nearest-even."""
+    rng = np.random.default_rng(51)
+    x = (rng.standard_normal(50000) * np.exp2(rng.integers(-60, 60, 50000))).astype(np.float32)
+    # exact ties (dropped half = 0x8000) with odd and even kept parts, and carries
+    # out of the fraction into the exponent
+    kept = rng.integers(0x0080, 0x7F70, 4000, dtype=np.uint32)   # finite normals, no carry to Inf
+    ties = ((kept << 16) | np.uint32(0x8000)).view(np.float32)
+    carry = np.array([0x3FFFFFFF, 0x3FFF8000, 0x3FFF7FFF, 0x407FFFFF], np.uint32).view(np.float32)
+    for v in (x, ties, -ties, carry):
+        assert np.array_equal(f32_to_bf16_bits(v), _bf16_bits_torch(v))
+
+
+def test_bf16_rounding_anchor_values():
+    vals = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 2 - 2.0 ** -9, -0.0, 127 / 127.0],
+                    np.float32)
+    assert [hex(v) for v in f32_to_bf16_bits(vals)] == \
+        ["0x3f80", "0x3f80", "0x3f82", "0x4000", "0x8000", "0x3f80"]
+
+
+def _row_cases():
+    rng = np.random.default_rng(52)
+    rows = [rng.standard_normal((6, HEAD_DIM)) * np.exp2(rng.integers(-20, 20, (6, 1))),
+            rng.uniform(-1, 1, (4, HEAD_DIM)) * 1e-30,
+            rng.integers(-300, 300, (4, HEAD_DIM)).astype(np.float64),   # many exact quotients
+            np.eye(4, HEAD_DIM) * 3.5 - 1.25]
+    return [r.astype(np.float32) for r in rows]
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37, 4.0])
+def test_int8_rows_round_trip_within_half_a_step(scale):
+    """Decoded through the decode oracle, every stored value is within half a
+    quantisation step of y = x / scale; the scale is max|y| / 127 to bf16
+    precision; the largest element maps to +-126 or +-127 with its sign."""
+    for x in _row_cases():
+        codes, sbits = quantise_int8_rows(x, scale)
+        y = (x / np.float32(scale)).astype(np.float64)
+        s = decode_bf16_bits(sbits)
+        amax = np.abs(y).max(axis=1)
+        assert np.all(np.abs(s - amax / 127) <= amax / 127 * 2.0 ** -8)
+        err = np.abs(decode_int8_rows(codes, sbits) - y)
+        assert np.all(err <= 0.5 * s[:, None] * (1 + 1e-6)), err.max()
+        top = np.argmax(np.abs(y), axis=1)
+        ctop = codes[np.arange(len(x)), top].astype(int)
+        assert np.all(np.isin(np.abs(ctop), [126, 127]))
+        assert np.all(np.sign(ctop) == np.sign(y[np.arange(len(x)), top]))
+        assert np.abs(codes.astype(int)).max() <= 127
+
+
+def test_int8_rows_codes_are_nearest_integers_brute_force():
+    """Each code is the integer nearest to y / s (ties to even) in exact
+    arithmetic, clamped to +-127, except where the exact quotient lies within
+    2^-16 of a tie and the fp32 quotient's rounding may pick either side."""
+    for x in _row_cases():
+        codes, sbits = quantise_int8_rows(x[:2], 1.0)
+        s = decode_bf16_bits(sbits)
+        for r in range(2):
+            S = Fraction(float(s[r]))
+            for d in range(HEAD_DIM):
+                q = Fraction(float(x[r, d])) / S
+                lo = math.floor(q)
+                frac = q - lo
+                if abs(frac - Fraction(1, 2)) < Fraction(1, 1 << 16):
+                    assert codes[r, d] in (max(-127, min(127, lo)), max(-127, min(127, lo + 1)))
+                    continue
+                want = lo + 1 if frac > Fraction(1, 2) else lo
+                assert codes[r, d] == max(-127, min(127, want)), (r, d, float(q))
+
+
+def test_int8_rows_exact_ties_go_to_the_even_code():
+    """max|y| = 127 makes the scale exactly 1, so y / s = y: halves are exact
+    ties and take the even neighbour (126.5 -> 126, -4.5 -> -4, 3.5 -> 4)."""
+    row = np.zeros(HEAD_DIM, np.float32)
+    vals = [127.0, 2.5, 3.5, -4.5, 0.5, -0.5, 126.5, -1.5, 5.25, -6.75]
+    row[:len(vals)] = vals
+    codes, sbits = quantise_int8_rows(row[None], 1.0)
+    assert sbits[0] == 0x3F80   # 1.0
+    assert codes[0, :len(vals)].tolist() == [127, 2, 4, -4, 0, 0, 126, -2, 5, -7]
+    assert not codes[0, len(vals):].any()
+
+
+def test_int8_rows_zero_rows_sign_symmetry_and_scale_division():
+    z = np.zeros((3, HEAD_DIM), np.float32)
+    codes, sbits = quantise_int8_rows(z, 1.0)
+    assert not codes.any() and not sbits.any()
+    for x in _row_cases():
+        c, sb = quantise_int8_rows(x, 1.0)
+        cn, sbn = quantise_int8_rows(-x, 1.0)
+        assert np.array_equal(cn, -c) and np.array_equal(sbn, sb)
+        k = np.float32(0.3)
+        assert all(np.array_equal(u, v) for u, v in
+                   zip(quantise_int8_rows(x, 0.3), quantise_int8_rows((x / k).astype(np.float32), 1.0)))
+
+
+def test_kv_append_int8_writes_only_the_target_slots():
+    rng = np.random.default_rng(53)
+    B, C = 3, 7
+    codes = rng.integers(-127, 128, size=(B, 2, NUM_KV_HEADS, C, HEAD_DIM)).astype(np.int8)
+    sbits = rng.integers(0, 1 << 15, size=(B, 2, NUM_KV_HEADS, C)).astype(np.uint16)
+    k_new = rng.standard_normal((B, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    v_new = rng.standard_normal((B, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    out, osc = kv_append_int8_reference(codes, sbits, k_new, v_new, [6, -1, 7], 0.5, 2.0)
+    assert np.array_equal(out[1:], codes[1:]) and np.array_equal(osc[1:], sbits[1:])
+    mask = np.ones(C, dtype=bool)
+    mask[6] = False
+    assert np.array_equal(out[0][:, :, mask], codes[0][:, :, mask])
+    assert np.array_equal(osc[0][:, :, mask], sbits[0][:, :, mask])
+    kc, ks = quantise_int8_rows(k_new[0], 0.5)
+    vc, vs = quantise_int8_rows(v_new[0], 2.0)
+    assert np.array_equal(out[0, 0, :, 6], kc) and np.array_equal(osc[0, 0, :, 6], ks)
+    assert np.array_equal(out[0, 1, :, 6], vc) and np.array_equal(osc[0, 1, :, 6], vs)

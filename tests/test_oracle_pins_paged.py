@@ -11,9 +11,9 @@ import torch
 
 from oracle import HEAD_DIM, NUM_KV_HEADS, decode_int8_rows, gqa_decode_reference
 from oracle.brute import brute_decode
-from oracle.kv_append import kv_append_reference, quantise_fp8
-from oracle.paged import (gather_pages, gqa_decode_multi, gqa_decode_paged_reference,
-                          kv_append_paged_reference)
+from oracle.kv_append import (kv_append_int8_reference, kv_append_reference, quantise_fp8,
+                               quantise_int8_rows)
+from oracle.paged import (gather_pages, gqa_decode_multi, gqa_decode_paged_reference, kv_append_paged_int8_reference, kv_append_paged_reference)
 
 
 def _scatter_case(rng, B, P, max_pages, lens, spare=3, dtype=np.float64):
@@ -223,3 +223,51 @@ def test_append_skips_slots_and_pages_out_of_range():
     want[5, 0, :, 15] = quantise_fp8(k[3, 0], 1.0)
     want[5, 1, :, 15] = quantise_fp8(v[3, 0], 1.0)
     assert np.array_equal(got, want)
+
+
+
+def test_int8_append_on_an_identity_table_is_the_contiguous_int8_append():
+    rng = np.random.default_rng(54)
+    B, C = 3, 16
+    codes = rng.integers(-127, 128, size=(B, 2, NUM_KV_HEADS, C, HEAD_DIM)).astype(np.int8)
+    sbits = rng.integers(0, 1 << 15, size=(B, 2, NUM_KV_HEADS, C)).astype(np.uint16)
+    k = rng.standard_normal((B, 1, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    v = rng.standard_normal((B, 1, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    pos = [0, 15, 9]
+    table = np.arange(B).reshape(B, 1)
+    got = kv_append_paged_int8_reference(codes, sbits, table, pos, k, v, 0.5, 2.0)
+    want = kv_append_int8_reference(codes, sbits, k[:, 0], v[:, 0], pos, 0.5, 2.0)
+    assert all(np.array_equal(g, w) for g, w in zip(got, want))
+
+
+def test_int8_append_lands_at_its_slots_and_skips_what_is_out_of_range():
+    """Through the separately pinned gather: slot positions[b] + t holds token
+    t's rows and row scales (across a page boundary too); slots past the
+    table and entries outside the pool write nothing; all else is unchanged."""
+    rng = np.random.default_rng(55)
+    P, B, T, max_pages, num_pages = 16, 4, 3, 3, 12
+    codes = rng.integers(-127, 128, size=(num_pages, 2, NUM_KV_HEADS, P, HEAD_DIM)).astype(np.int8)
+    sbits = rng.integers(0, 1 << 15, size=(num_pages, 2, NUM_KV_HEADS, P)).astype(np.uint16)
+    k = rng.standard_normal((B, T, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    v = rng.standard_normal((B, T, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    table = np.array([[3, 7, 1], [0, -1, 2], [4, num_pages, 6], [8, 9, 11]])
+    # 0: crosses pages; 1: t = 2 hits entry -1; 2: t = 0 hits entry num_pages;
+    # 3: t >= 1 lies past the table
+    pos = [P - 1, P - 2, 2 * P - 1, 3 * P - 1]
+    got, gsc = kv_append_paged_int8_reference(codes, sbits, table, pos, k, v, 0.25, 4.0)
+    touched = np.zeros((num_pages, P), dtype=bool)
+    for b in range(B):
+        for t in range(T):
+            s_ = pos[b] + t
+            if s_ >= max_pages * P or not 0 <= table[b, s_ // P] < num_pages:
+                continue
+            page, row = table[b, s_ // P], s_ % P
+            kc, ks = quantise_int8_rows(k[b, t], 0.25)
+            vc, vs = quantise_int8_rows(v[b, t], 4.0)
+            assert np.array_equal(got[page, 0, :, row], kc) and np.array_equal(gsc[page, 0, :, row], ks)
+            assert np.array_equal(got[page, 1, :, row], vc) and np.array_equal(gsc[page, 1, :, row], vs)
+            touched[page, row] = True
+    assert touched.sum() == 3 + 2 + 2 + 1
+    keep = ~touched
+    assert np.array_equal(got.transpose(0, 3, 1, 2, 4)[keep], codes.transpose(0, 3, 1, 2, 4)[keep])
+    assert np.array_equal(gsc.transpose(0, 3, 1, 2)[keep], sbits.transpose(0, 3, 1, 2)[keep])
