@@ -358,31 +358,38 @@ def main():
     # KV append (the cache write before each step): the step's new tokens (one
     # per request, T for a paged verify pass) at slots L_b .. L_b + T - 1, past
     # the valid prefix, so the decode inputs are unchanged (slots past the
-    # cache write nothing). An INT8 cache's rows and scales are written by the
-    # caller: not timed here.
-    append_us = None
-    if w.kv_dtype != "int8":
-        shape = (w.batch, w.q_tokens, 8, 128) if paged else (w.batch, 8, 128)
-        k_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
-        v_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
-        slots = inp["seq_lens"].clone()
-        if paged:
-            def append():
-                b.gqa_kv_append_paged(inp["kv_pages"], inp["block_table"], k_new, v_new, slots,
-                                      inp["k_scale"], inp["v_scale"], num_q_heads=w.num_q_heads)
-        else:
-            def append():
-                b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
-        for _ in range(3):
-            append()
-        a_begin, a_end = new_event(), new_event()
-        torch.cuda.synchronize()
-        a_begin.record(stream)
-        for _ in range(K):
-            append()
-        a_end.record(stream)
-        torch.cuda.synchronize()
-        append_us = round(a_begin.elapsed_time(a_end) / K * 1e3, 2)
+    # cache write nothing). An INT8 cache is quantised row by row on the way.
+    shape = (w.batch, w.q_tokens, 8, 128) if paged else (w.batch, 8, 128)
+    k_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
+    v_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
+    slots = inp["seq_lens"].clone()
+    int8 = w.kv_dtype == "int8"
+    if paged and int8:
+        def append():
+            b.gqa_kv_append_paged_int8(inp["kv_pages"], inp["kv_scales"], inp["block_table"],
+                                       k_new, v_new, slots, inp["k_scale"], inp["v_scale"],
+                                       num_q_heads=w.num_q_heads)
+    elif paged:
+        def append():
+            b.gqa_kv_append_paged(inp["kv_pages"], inp["block_table"], k_new, v_new, slots,
+                                  inp["k_scale"], inp["v_scale"], num_q_heads=w.num_q_heads)
+    elif int8:
+        def append():
+            b.gqa_kv_append_int8(inp["kv"], inp["kv_scales"], k_new, v_new, slots,
+                                 inp["k_scale"], inp["v_scale"], num_q_heads=w.num_q_heads)
+    else:
+        def append():
+            b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
+    for _ in range(3):
+        append()
+    a_begin, a_end = new_event(), new_event()
+    torch.cuda.synchronize()
+    a_begin.record(stream)
+    for _ in range(K):
+        append()
+    a_end.record(stream)
+    torch.cuda.synchronize()
+    append_us = round(a_begin.elapsed_time(a_end) / K * 1e3, 2)
 
     # Cold-cache calls: a 512 MiB write evicts the caches before each timed call.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -109,6 +109,9 @@ _plan_paged = _sig("gqa_plan_decode_paged", ctypes.c_int, [_PDescP, _i32, _PlanP
 _last_error = _sig("gqa_last_error", ctypes.c_char_p, [])
 _append = _sig("gqa_kv_append", ctypes.c_int, [_DescP, _vp, _vp, _vp, _vp, _vp])
 _append_paged = _sig("gqa_kv_append_paged", ctypes.c_int, [_PDescP, _vp, _vp, _vp, _vp, _vp, _vp])
+_append_int8 = _sig("gqa_kv_append_int8", ctypes.c_int, [_DescP, _vp, _vp, _vp, _vp, _vp, _vp])
+_append_paged_int8 = _sig("gqa_kv_append_paged_int8", ctypes.c_int,
+                          [_PDescP, _vp, _vp, _vp, _vp, _vp, _vp, _vp])
 
 
 class GqaError(RuntimeError):
@@ -450,6 +453,73 @@ def gqa_kv_append_paged(kv_pages: torch.Tensor, block_table: torch.Tensor, k_new
     with torch.cuda.device(kv_pages.device):
         st = _append_paged(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(positions),
                            _ptr(block_table), _ptr(kv_pages), _stream_handle(stream, kv_pages.device))
+    _check(st)
+    return kv_pages
+
+
+def gqa_kv_append_int8(kv: torch.Tensor, kv_scales: torch.Tensor, k_new: torch.Tensor,
+                       v_new: torch.Tensor, positions: torch.Tensor, k_scale: float = 1.0,
+                       v_scale: float = 1.0, num_q_heads: int = NUM_Q_HEADS_2TO1,
+                       stream=None) -> torch.Tensor:
+    """Quantise k_new/v_new [batch, 8, 128] row by row into an int8 cache kv
+    [batch, 2, 8, capacity, 128] and its bf16 row scales kv_scales
+    [batch, 2, 8, capacity] at slot positions[b]; returns kv."""
+    _check_devices(kv, kv_scales, k_new, v_new, positions)
+    if positions.dtype != torch.int32:
+        raise ValueError("positions must be int32")
+    if kv.dtype != torch.int8 or kv_scales.dtype != torch.bfloat16:
+        raise ValueError("kv must be int8 and kv_scales bfloat16")
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same shape and dtype")
+    if k_new.dim() != 3 or kv.dim() != 5 or k_new.shape[0] != kv.shape[0] or \
+            tuple(kv_scales.shape) != tuple(kv.shape[:4]):
+        raise ValueError("k_new/v_new must be [batch, 8, 128], kv [batch, 2, 8, capacity, 128] "
+                         "and kv_scales [batch, 2, 8, capacity]")
+    if kv.shape[2] != k_new.shape[1] or kv.shape[4] != k_new.shape[2]:
+        raise ValueError("kv and k_new disagree on KV heads or head_dim")
+    desc = GqaDesc(batch=kv.shape[0], capacity=kv.shape[3], num_q_heads=num_q_heads,
+                   num_kv_heads=k_new.shape[1], head_dim=k_new.shape[2],
+                   q_dtype=_dtype_code(k_new, "q"), kv_dtype=GQA_INT8_ROWSCALE,
+                   k_scale=k_scale, v_scale=v_scale, flags=0)
+    with torch.cuda.device(kv.device):
+        st = _append_int8(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(positions), _ptr(kv),
+                          _ptr(kv_scales), _stream_handle(stream, kv.device))
+    _check(st)
+    return kv
+
+
+def gqa_kv_append_paged_int8(kv_pages: torch.Tensor, kv_scales: torch.Tensor,
+                             block_table: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             positions: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
+                             num_q_heads: int = NUM_Q_HEADS_2TO1, stream=None) -> torch.Tensor:
+    """Quantise k_new/v_new [batch, T, 8, 128] row by row into an int8 page pool
+    kv_pages [num_pages, 2, 8, page_size, 128] and its bf16 row scales kv_scales
+    [num_pages, 2, 8, page_size] at slots positions[b] + t through block_table;
+    returns kv_pages."""
+    _check_devices(kv_pages, kv_scales, block_table, k_new, v_new, positions)
+    if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("positions and block_table must be int32")
+    if kv_pages.dtype != torch.int8 or kv_scales.dtype != torch.bfloat16:
+        raise ValueError("kv_pages must be int8 and kv_scales bfloat16")
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must have the same shape and dtype")
+    if k_new.dim() != 4 or kv_pages.dim() != 5 or block_table.dim() != 2 or \
+            block_table.shape[0] != k_new.shape[0] or kv_pages.shape[1] != 2 or \
+            tuple(kv_scales.shape) != tuple(kv_pages.shape[:4]):
+        raise ValueError("k_new/v_new must be [batch, T, 8, 128], kv_pages "
+                         "[num_pages, 2, 8, page_size, 128], kv_scales [num_pages, 2, 8, page_size] "
+                         "and block_table [batch, max_pages]")
+    if kv_pages.shape[2] != k_new.shape[2] or kv_pages.shape[4] != k_new.shape[3]:
+        raise ValueError("kv_pages and k_new disagree on KV heads or head_dim")
+    desc = GqaPagedDesc(batch=k_new.shape[0], q_tokens=k_new.shape[1], num_q_heads=num_q_heads,
+                        num_kv_heads=k_new.shape[2], head_dim=k_new.shape[3],
+                        q_dtype=_dtype_code(k_new, "q"), kv_dtype=GQA_INT8_ROWSCALE,
+                        k_scale=k_scale, v_scale=v_scale, flags=0, page_size=kv_pages.shape[3],
+                        num_pages=kv_pages.shape[0], max_pages=block_table.shape[1])
+    with torch.cuda.device(kv_pages.device):
+        st = _append_paged_int8(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(positions),
+                                _ptr(block_table), _ptr(kv_pages), _ptr(kv_scales),
+                                _stream_handle(stream, kv_pages.device))
     _check(st)
     return kv_pages
 

@@ -701,6 +701,135 @@ gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const v
   return GQA_OK;
 }
 
+// The KV append entry points; int8 = the _int8 forms, which write an
+// INT8_ROWSCALE cache and its bf16 row scales (the others reject one).
+gqa_status_t check_append_dtype(int kv_dtype, bool int8, const char* name) {
+  if (int8 && kv_dtype != GQA_INT8_ROWSCALE)
+    return fail(GQA_ERR_INVALID_ARG, "%s_int8 needs kv dtype INT8_ROWSCALE (got %d)", name, kv_dtype);
+  if (!int8 && kv_dtype == GQA_INT8_ROWSCALE)
+    return fail(GQA_ERR_INVALID_ARG, "%s does not write an INT8_ROWSCALE cache; use %s_int8", name,
+                name);
+  return GQA_OK;
+}
+
+gqa_status_t append_contiguous(const gqa_desc_t* desc, const void* k_new, const void* v_new,
+                               const int32_t* positions, void* kv, void* kv_scales, bool int8,
+                               hipStream_t stream) {
+  gqa_status_t st = check_desc(desc);
+  if (st != GQA_OK) return st;
+  st = check_append_dtype(desc->kv_dtype, int8, "gqa_kv_append");
+  if (st != GQA_OK) return st;
+  if (desc->batch == 0) return ok();
+  if (!k_new || !v_new || !positions || !kv || (int8 && !kv_scales))
+    return fail(GQA_ERR_INVALID_ARG, "k_new, v_new, positions, kv%s must be non-NULL",
+                int8 ? " and kv_scales" : "");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv, 16) || !aligned(positions, 4) ||
+      (int8 && !aligned(kv_scales, 2)))
+    return fail(GQA_ERR_INVALID_ARG,
+                "k_new, v_new and kv must be 16-byte aligned, positions 4-byte aligned%s",
+                int8 ? " and kv_scales 2-byte aligned" : "");
+  if (desc->batch > kMaxLaunchWorkgroups)   // one workgroup per request
+    return fail(GQA_ERR_INVALID_ARG, "batch too large for one append launch (%d)", desc->batch);
+  const size_t B = (size_t)desc->batch;
+  const size_t row_bytes = B * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * elem_bytes(desc->q_dtype);
+  const size_t rows = B * 2 * GQA_NUM_KV_HEADS * (size_t)desc->capacity;
+  const size_t kv_bytes = rows * GQA_HEAD_DIM * elem_bytes(desc->kv_dtype);
+  const size_t pos_bytes = B * sizeof(int32_t);
+  if (ranges_overlap(kv, kv_bytes, k_new, row_bytes) || ranges_overlap(kv, kv_bytes, v_new, row_bytes) ||
+      ranges_overlap(kv, kv_bytes, positions, pos_bytes))
+    return fail(GQA_ERR_ALIAS, "kv must not overlap k_new, v_new or positions");
+  if (int8) {
+    const size_t sc_bytes = rows * 2;
+    if (ranges_overlap(kv_scales, sc_bytes, kv, kv_bytes) ||
+        ranges_overlap(kv_scales, sc_bytes, k_new, row_bytes) ||
+        ranges_overlap(kv_scales, sc_bytes, v_new, row_bytes) ||
+        ranges_overlap(kv_scales, sc_bytes, positions, pos_bytes))
+      return fail(GQA_ERR_ALIAS, "kv_scales must not overlap kv, k_new, v_new or positions");
+  }
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != GQA_OK) return st;
+  gqa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.positions = positions;
+  a.kv = kv;
+  a.kv_scales = kv_scales;
+  a.batch = desc->batch;
+  a.capacity = desc->capacity;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
+  hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+gqa_status_t append_paged(const gqa_paged_desc_t* desc, const void* k_new, const void* v_new,
+                          const int32_t* positions, const int32_t* block_table, void* kv_pages,
+                          void* kv_scales, bool int8, hipStream_t stream) {
+  gqa_desc_t d;
+  Paging pg;
+  gqa_status_t st = check_paged_desc(desc, &d, &pg);
+  if (st != GQA_OK) return st;
+  st = check_append_dtype(desc->kv_dtype, int8, "gqa_kv_append_paged");
+  if (st != GQA_OK) return st;
+  if (desc->batch == 0) return ok();
+  if (!k_new || !v_new || !positions || !block_table || !kv_pages || (int8 && !kv_scales))
+    return fail(GQA_ERR_INVALID_ARG,
+                "k_new, v_new, positions, block_table, kv_pages%s must be non-NULL",
+                int8 ? " and kv_scales" : "");
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv_pages, 16) ||
+      !aligned(positions, 4) || !aligned(block_table, 4) || (int8 && !aligned(kv_scales, 2)))
+    return fail(GQA_ERR_INVALID_ARG,
+                "k_new, v_new and kv_pages must be 16-byte aligned, positions and block_table "
+                "4-byte aligned%s", int8 ? ", kv_scales 2-byte aligned" : "");
+  if ((int64_t)desc->batch * desc->q_tokens > kMaxLaunchWorkgroups)   // one workgroup per token
+    return fail(GQA_ERR_INVALID_ARG, "batch x q_tokens too large for one append launch");
+  const size_t B = (size_t)desc->batch;
+  const size_t row_bytes =
+      B * (size_t)desc->q_tokens * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * elem_bytes(desc->q_dtype);
+  const size_t pool_bytes = pool_bytes_of(desc);
+  const size_t pos_bytes = B * sizeof(int32_t);
+  const size_t table_bytes = B * (size_t)desc->max_pages * sizeof(int32_t);
+  if (ranges_overlap(kv_pages, pool_bytes, k_new, row_bytes) ||
+      ranges_overlap(kv_pages, pool_bytes, v_new, row_bytes) ||
+      ranges_overlap(kv_pages, pool_bytes, positions, pos_bytes) ||
+      ranges_overlap(kv_pages, pool_bytes, block_table, table_bytes))
+    return fail(GQA_ERR_ALIAS, "kv_pages must not overlap k_new, v_new, positions or block_table");
+  if (int8) {
+    const size_t sc_bytes =
+        (size_t)desc->num_pages * 2 * GQA_NUM_KV_HEADS * (size_t)desc->page_size * 2;
+    if (ranges_overlap(kv_scales, sc_bytes, kv_pages, pool_bytes) ||
+        ranges_overlap(kv_scales, sc_bytes, k_new, row_bytes) ||
+        ranges_overlap(kv_scales, sc_bytes, v_new, row_bytes) ||
+        ranges_overlap(kv_scales, sc_bytes, positions, pos_bytes) ||
+        ranges_overlap(kv_scales, sc_bytes, block_table, table_bytes))
+      return fail(GQA_ERR_ALIAS,
+                  "kv_scales must not overlap kv_pages, k_new, v_new, positions or block_table");
+  }
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != GQA_OK) return st;
+  gqa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.positions = positions;
+  a.kv = kv_pages;
+  a.kv_scales = kv_scales;
+  a.batch = desc->batch;
+  a.tokens = desc->q_tokens;
+  a.capacity = d.capacity;
+  a.k_scale = desc->k_scale;
+  a.v_scale = desc->v_scale;
+  a.block_table = block_table;
+  a.max_pages = desc->max_pages;
+  a.page_shift = pg.page_shift;
+  a.num_pages = desc->num_pages;
+  hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
+  if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -860,92 +989,28 @@ GQA_API gqa_status_t gqa_decode_paged(const gqa_paged_desc_t* desc, const void* 
 
 GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,
                                    const int32_t* positions, void* kv, hipStream_t stream) {
-  gqa_status_t st = check_desc(desc);
-  if (st != GQA_OK) return st;
-  if (desc->kv_dtype == GQA_INT8_ROWSCALE)
-    return fail(GQA_ERR_INVALID_ARG, "gqa_kv_append does not write an INT8_ROWSCALE cache");
-  if (desc->batch == 0) return ok();
-  if (!k_new || !v_new || !positions || !kv)
-    return fail(GQA_ERR_INVALID_ARG, "k_new, v_new, positions and kv must be non-NULL");
-  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv, 16) || !aligned(positions, 4))
-    return fail(GQA_ERR_INVALID_ARG,
-                "k_new, v_new and kv must be 16-byte aligned and positions 4-byte aligned");
-  if (desc->batch > kMaxLaunchWorkgroups)   // one workgroup per request
-    return fail(GQA_ERR_INVALID_ARG, "batch too large for one append launch (%d)", desc->batch);
-  const size_t B = (size_t)desc->batch;
-  const size_t row_bytes = B * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * elem_bytes(desc->q_dtype);
-  const size_t kv_bytes =
-      B * 2 * GQA_NUM_KV_HEADS * (size_t)desc->capacity * GQA_HEAD_DIM * elem_bytes(desc->kv_dtype);
-  if (ranges_overlap(kv, kv_bytes, k_new, row_bytes) || ranges_overlap(kv, kv_bytes, v_new, row_bytes) ||
-      ranges_overlap(kv, kv_bytes, positions, B * sizeof(int32_t)))
-    return fail(GQA_ERR_ALIAS, "kv must not overlap k_new, v_new or positions");
-  int dev = -1;
-  st = check_device(&dev);
-  if (st != GQA_OK) return st;
-  gqa::AppendArgs a;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.positions = positions;
-  a.kv = kv;
-  a.batch = desc->batch;
-  a.capacity = desc->capacity;
-  a.k_scale = desc->k_scale;
-  a.v_scale = desc->v_scale;
-  hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
-  if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return append_contiguous(desc, k_new, v_new, positions, kv, nullptr, false, stream);
+}
+
+GQA_API gqa_status_t gqa_kv_append_int8(const gqa_desc_t* desc, const void* k_new,
+                                        const void* v_new, const int32_t* positions, void* kv,
+                                        void* kv_scales, hipStream_t stream) {
+  return append_contiguous(desc, k_new, v_new, positions, kv, kv_scales, true, stream);
 }
 
 GQA_API gqa_status_t gqa_kv_append_paged(const gqa_paged_desc_t* desc, const void* k_new,
                                          const void* v_new, const int32_t* positions,
                                          const int32_t* block_table, void* kv_pages,
                                          hipStream_t stream) {
-  gqa_desc_t d;
-  Paging pg;
-  gqa_status_t st = check_paged_desc(desc, &d, &pg);
-  if (st != GQA_OK) return st;
-  if (desc->kv_dtype == GQA_INT8_ROWSCALE)
-    return fail(GQA_ERR_INVALID_ARG, "gqa_kv_append_paged does not write an INT8_ROWSCALE pool");
-  if (desc->batch == 0) return ok();
-  if (!k_new || !v_new || !positions || !block_table || !kv_pages)
-    return fail(GQA_ERR_INVALID_ARG,
-                "k_new, v_new, positions, block_table and kv_pages must be non-NULL");
-  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(kv_pages, 16) ||
-      !aligned(positions, 4) || !aligned(block_table, 4))
-    return fail(GQA_ERR_INVALID_ARG,
-                "k_new, v_new and kv_pages must be 16-byte aligned, positions and block_table "
-                "4-byte aligned");
-  if ((int64_t)desc->batch * desc->q_tokens > kMaxLaunchWorkgroups)   // one workgroup per token
-    return fail(GQA_ERR_INVALID_ARG, "batch x q_tokens too large for one append launch");
-  const size_t B = (size_t)desc->batch;
-  const size_t row_bytes =
-      B * (size_t)desc->q_tokens * GQA_NUM_KV_HEADS * GQA_HEAD_DIM * elem_bytes(desc->q_dtype);
-  const size_t pool_bytes = pool_bytes_of(desc);
-  if (ranges_overlap(kv_pages, pool_bytes, k_new, row_bytes) ||
-      ranges_overlap(kv_pages, pool_bytes, v_new, row_bytes) ||
-      ranges_overlap(kv_pages, pool_bytes, positions, B * sizeof(int32_t)) ||
-      ranges_overlap(kv_pages, pool_bytes, block_table, B * (size_t)desc->max_pages * sizeof(int32_t)))
-    return fail(GQA_ERR_ALIAS, "kv_pages must not overlap k_new, v_new, positions or block_table");
-  int dev = -1;
-  st = check_device(&dev);
-  if (st != GQA_OK) return st;
-  gqa::AppendArgs a;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  a.positions = positions;
-  a.kv = kv_pages;
-  a.batch = desc->batch;
-  a.tokens = desc->q_tokens;
-  a.capacity = d.capacity;
-  a.k_scale = desc->k_scale;
-  a.v_scale = desc->v_scale;
-  a.block_table = block_table;
-  a.max_pages = desc->max_pages;
-  a.page_shift = pg.page_shift;
-  a.num_pages = desc->num_pages;
-  hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
-  if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return append_paged(desc, k_new, v_new, positions, block_table, kv_pages, nullptr, false, stream);
+}
+
+GQA_API gqa_status_t gqa_kv_append_paged_int8(const gqa_paged_desc_t* desc, const void* k_new,
+                                              const void* v_new, const int32_t* positions,
+                                              const int32_t* block_table, void* kv_pages,
+                                              void* kv_scales, hipStream_t stream) {
+  return append_paged(desc, k_new, v_new, positions, block_table, kv_pages, kv_scales, true,
+                      stream);
 }
 
 }  // extern "C"

@@ -62,8 +62,10 @@ struct AppendArgs {
   int32_t batch;
   int32_t tokens = 1;        // new tokens per request
   int32_t capacity;          // slots a request can address (paged: max_pages << page_shift)
-  float k_scale;             // fp8 cache: stored code = e4m3(k / k_scale)
+  float k_scale;             // fp8 cache: stored code = e4m3(k / k_scale); INT8: rows of k / k_scale
   float v_scale;
+  void* kv_scales = nullptr; // INT8 cache: bf16 row scales, [batch, 2, 8, capacity] or
+                             // [num_pages, 2, 8, 1 << page_shift]
   // Page pool (block_table != nullptr): slot j of request b is row j % page
   // size of page block_table[b * max_pages + j / page size]; entries outside
   // [0, num_pages) are skipped.

@@ -457,8 +457,19 @@ hipError_t enqueue_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mi
 // contiguous cache or through the block table into a page pool. An fp8
 // cache stores e4m3(x / scale), per-tensor scales as in the Thor FP8-KV
 // notes; the division is an IEEE fp32 division and the code the nearest
-// E4M3FN value (ties to even), saturating at +-448.
+// E4M3FN value (ties to even), saturating at +-448. An INT8 cache (the Orin
+// Qwen3-VL doc's INT8 mirrors, one bf16 scale per (position, KV head) row)
+// stores each row symmetrically, as that doc quantises its INT8 weights:
+// y = x / scale, row scale s = bf16(max|y| / 127), code = the integer nearest
+// to y / s (ties to even) clamped to +-127, all in fp32 (0 where s is 0).
 // ---------------------------------------------------------------------------
+// fp32 -> bf16 bits, nearest with ties to even (finite and infinite inputs):
+// add just under half of the kept unit, plus one if the kept part is odd.
+__device__ __forceinline__ u32 f32_to_bf16_rne(float x) {
+  const u32 b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ u32 f32_to_e4m3fn_sat(float x) {
   const u32 bits = __float_as_uint(x);
   const u32 sign = (bits >> 24) & 0x80u;
@@ -519,6 +530,30 @@ __global__ __launch_bounds__(256) void gqa_kv_append_kernel(AppendArgs a) {
       w[i >> 2] |= f32_to_e4m3fn_sat(__fdiv_rn(x, scale)) << (8 * (i & 3));
     }
     *reinterpret_cast<u32x2*>(static_cast<char*>(a.kv) + dst) = (u32x2){w[0], w[1]};
+  } else if constexpr (KVT == kI8) {
+    const float scale = plane ? a.v_scale : a.k_scale;
+    float y[8];
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      y[i] = __fdiv_rn((i & 1) ? E::hi(in[i >> 1]) : E::lo(in[i >> 1]), scale);
+      m = fmaxf(m, fabsf(y[i]));
+    }
+    // The 16 threads of a row are lanes 16k .. 16k + 15 of one wave, and a
+    // row's threads leave early only together (slot and page are per row).
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const u32 sb = f32_to_bf16_rne(__fdiv_rn(m, 127.f));
+    const float s = __uint_as_float(sb << 16);
+    u32 w[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q = s > 0.f ? fminf(fmaxf(__builtin_rintf(__fdiv_rn(y[i], s)), -127.f), 127.f)
+                              : 0.f;
+      w[i >> 2] |= ((u32)(int)q & 0xffu) << (8 * (i & 3));
+    }
+    *reinterpret_cast<u32x2*>(static_cast<char*>(a.kv) + dst) = (u32x2){w[0], w[1]};
+    if (chunk == 0) static_cast<uint16_t*>(a.kv_scales)[dst_row] = (uint16_t)sb;
   } else {
     *reinterpret_cast<u32x4*>(static_cast<char*>(a.kv) + dst * 2) = in;
   }
@@ -557,6 +592,10 @@ hipError_t enqueue_kv_append(const AppendArgs& a, int src_dtype, int kv_dtype, h
   if (src_dtype == kF16 && kv_dtype == kF16) return enqueue_append_typed<kF16, kF16>(a, stream);
   if (src_dtype == kBF16 && kv_dtype == kFP8) return enqueue_append_typed<kBF16, kFP8>(a, stream);
   if (src_dtype == kF16 && kv_dtype == kFP8) return enqueue_append_typed<kF16, kFP8>(a, stream);
+  if (a.kv_scales != nullptr && src_dtype == kBF16 && kv_dtype == kI8)
+    return enqueue_append_typed<kBF16, kI8>(a, stream);
+  if (a.kv_scales != nullptr && src_dtype == kF16 && kv_dtype == kI8)
+    return enqueue_append_typed<kF16, kI8>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -299,10 +299,28 @@ GQA_API gqa_status_t gqa_prepared_plan(const gqa_prepared_t* handle, gqa_plan_t*
  * saturating to +-448, NaN stored as 0x7F. Positions outside [0, capacity)
  * write nothing. kv must not overlap k_new, v_new or positions
  * (GQA_ERR_ALIAS). Asynchronous on `stream`; allocates nothing. An INT8
- * cache is rejected (GQA_ERR_INVALID_ARG): its rows and scales are written
- * by the caller. */
+ * cache is rejected (GQA_ERR_INVALID_ARG); gqa_kv_append_int8 writes one. */
 GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, const void* v_new,
                                    const int32_t* positions, void* kv, hipStream_t stream);
+
+/* As gqa_kv_append, for an INT8_ROWSCALE cache: writes each new K and V row
+ * of 128 values as int8 codes into kv and its bf16 row scale into kv_scales
+ * [batch, 2, 8, capacity] (2-byte aligned; the layout gqa_decode_int8 reads).
+ * The Orin Qwen3-VL doc ("INT8 KV cache") keeps INT8 mirrors with one BF16
+ * scale per (position, KV head) row without saying how a row is quantised;
+ * this follows that doc's symmetric INT8 weight rule (scale = amax / 127,
+ * "Weight quantization" table) per row: y = x / k_scale (V: v_scale),
+ * s = max|y| / 127 rounded to bf16 (nearest, ties to even), code = y / s
+ * rounded to the nearest integer (ties to even) and clamped to +-127; a row
+ * whose s is 0 stores code 0. Every division is an IEEE fp32 division, so the
+ * decode's code * s * k_scale gives back x to within half a step. Rows with a
+ * non-finite value store unspecified codes and scale. kv_scales must not
+ * overlap kv, k_new, v_new or positions (GQA_ERR_ALIAS); a non-INT8
+ * descriptor is rejected (GQA_ERR_INVALID_ARG). Asynchronous on `stream`;
+ * allocates nothing. */
+GQA_API gqa_status_t gqa_kv_append_int8(const gqa_desc_t* desc, const void* k_new,
+                                        const void* v_new, const int32_t* positions, void* kv,
+                                        void* kv_scales, hipStream_t stream);
 
 /* Append desc->q_tokens new tokens per request to a page pool: token t of
  * request b lands at slot s = positions[b] + t, i.e. row s % page_size of
@@ -323,11 +341,23 @@ GQA_API gqa_status_t gqa_kv_append(const gqa_desc_t* desc, const void* k_new, co
  * must not land on the same page row (which one is stored is then
  * unspecified). kv_pages must not overlap k_new, v_new, positions or
  * block_table (GQA_ERR_ALIAS). Asynchronous on `stream`; allocates nothing.
- * An INT8 pool is rejected (GQA_ERR_INVALID_ARG). */
+ * An INT8 pool is rejected (GQA_ERR_INVALID_ARG); gqa_kv_append_paged_int8
+ * writes one. */
 GQA_API gqa_status_t gqa_kv_append_paged(const gqa_paged_desc_t* desc, const void* k_new,
                                          const void* v_new, const int32_t* positions,
                                          const int32_t* block_table, void* kv_pages,
                                          hipStream_t stream);
+
+/* As gqa_kv_append_paged, for an INT8_ROWSCALE pool: each row is quantised
+ * as in gqa_kv_append_int8 and its bf16 scale goes to row `s % page_size` of
+ * page block_table[b][s / page_size] in kv_scales [num_pages, 2, 8,
+ * page_size] (2-byte aligned; the layout gqa_decode_paged reads). kv_scales
+ * must not overlap kv_pages, k_new, v_new, positions or block_table
+ * (GQA_ERR_ALIAS); a non-INT8 descriptor is rejected (GQA_ERR_INVALID_ARG). */
+GQA_API gqa_status_t gqa_kv_append_paged_int8(const gqa_paged_desc_t* desc, const void* k_new,
+                                              const void* v_new, const int32_t* positions,
+                                              const int32_t* block_table, void* kv_pages,
+                                              void* kv_scales, hipStream_t stream);
 
 /* Host-only validation of a call's arguments (never touches a device, so it
  * runs without a GPU). Same checks and status codes as prepare_gqa_decode,

@@ -271,6 +271,22 @@ void append_and_device_paths(bool have_device) {
   EXPECT(gqa_kv_append_paged(&pd, reinterpret_cast<const char*>(Q) + 4, Q, LENS, TABLE, OUT,
                              nullptr) == GQA_ERR_INVALID_ARG);
 
+  // INT8 appends: INT8 descriptors only, a scales buffer overlapping nothing.
+  const gqa_desc_t d8 = desc(2, 1024, GQA_INT8_ROWSCALE, GQA_BF16, 16);
+  void* const sc = const_cast<void*>(SCALES);
+  EXPECT(gqa_kv_append_int8(&d8, Q, Q, LENS, OUT, nullptr, nullptr) == GQA_ERR_INVALID_ARG);
+  EXPECT(gqa_kv_append_int8(&d, Q, Q, LENS, OUT, sc, nullptr) == GQA_ERR_INVALID_ARG);
+  EXPECT(gqa_kv_append_int8(&d8, Q, Q, LENS, OUT, OUT, nullptr) == GQA_ERR_ALIAS);
+  EXPECT(gqa_kv_append_int8(&d8, Q, Q, LENS, OUT, static_cast<char*>(sc) + 1, nullptr) ==
+         GQA_ERR_INVALID_ARG);
+  EXPECT(gqa_kv_append(&d8, Q, Q, LENS, OUT, nullptr) == GQA_ERR_INVALID_ARG);
+  const gqa_paged_desc_t pd8 = pdesc(2, 2, 16, 64, 32, GQA_INT8_ROWSCALE, 16);
+  EXPECT(gqa_kv_append_paged_int8(&pd8, Q, Q, LENS, TABLE, OUT, nullptr, nullptr) ==
+         GQA_ERR_INVALID_ARG);
+  EXPECT(gqa_kv_append_paged_int8(&pd, Q, Q, LENS, TABLE, OUT, sc, nullptr) == GQA_ERR_INVALID_ARG);
+  EXPECT(gqa_kv_append_paged_int8(&pd8, Q, Q, LENS, TABLE, OUT, const_cast<int32_t*>(TABLE),
+                                  nullptr) == GQA_ERR_ALIAS);
+
   gqa_prepared_t* h = nullptr;
   EXPECT(launch_gqa_decode_prepared(nullptr, nullptr) == GQA_ERR_INVALID_ARG);
   EXPECT(gqa_prepared_workspace_bytes(nullptr) == 0);
@@ -286,6 +302,8 @@ void append_and_device_paths(bool have_device) {
     EXPECT(std::strlen(gqa_last_error()) > 0);
     EXPECT(gqa_decode(&d, Q, KV, LENS, 1.f, OUT, nullptr) != GQA_OK);
     EXPECT(gqa_kv_append(&d, Q, Q, LENS, OUT, nullptr) != GQA_OK);
+    EXPECT(gqa_kv_append_int8(&d8, Q, Q, LENS, OUT, sc, nullptr) != GQA_OK);
+    EXPECT(gqa_kv_append_paged_int8(&pd8, Q, Q, LENS, TABLE, OUT, sc, nullptr) != GQA_OK);
     EXPECT(prepare_gqa_decode_paged(&pd, Q, KV, nullptr, TABLE, LENS, 1.f, OUT, 0, &h) != GQA_OK &&
            !h);
   }

@@ -388,3 +388,45 @@ def test_paged_append_rejects_bad_arguments_without_touching_a_device():
     assert call(pdesc(T=5)) == INVALID                           # 5 tokens x 4 heads > 16 rows
     assert call(pdesc(kv=b.GQA_INT8_ROWSCALE, hq=16)) == INVALID and "INT8" in b.last_error()
     assert call(pdesc(batch=0), None, None, None, None, None) == OK
+
+
+def test_int8_append_rejects_bad_arguments_without_touching_a_device():
+    """gqa_kv_append_int8 / gqa_kv_append_paged_int8: INT8 descriptors only, a
+    2-byte aligned scales buffer that overlaps nothing; the plain forms refuse
+    an INT8 cache and name the _int8 form."""
+    K, V, P, KV_ = (1 << 30), (5 << 30), (3 << 30), (2 << 30)
+    d = desc(batch=2, capacity=16, kv=b.GQA_INT8_ROWSCALE, hq=16)
+    cache_bytes = 2 * 2 * 8 * 16 * 128
+    scale_bytes = 2 * 2 * 8 * 16 * 2
+    app = b._append_int8
+
+    def call(desc_, k=K, v_=V, pos=P, kv=KV_, sc=SC):
+        return app(ctypes.byref(desc_), k, v_, pos, kv, sc, None)
+
+    assert call(d, sc=None) == INVALID
+    assert call(d, sc=SC + 1) == INVALID                            # 2-byte alignment
+    assert call(d, sc=KV_ + cache_bytes - 2) == ALIAS               # scales inside the cache
+    assert call(d, k=SC + scale_bytes - 16) == ALIAS                # k_new inside the scales
+    assert call(d, pos=SC) == ALIAS
+    assert call(d, sc=KV_ + cache_bytes) not in (INVALID, ALIAS)    # adjacent: only the device check
+    assert call(desc(batch=2, capacity=16)) == INVALID and "INT8" in b.last_error()
+    assert b._append(ctypes.byref(d), K, V, P, KV_, None) == INVALID
+    assert "gqa_kv_append_int8" in b.last_error()
+    assert call(desc(batch=0, kv=b.GQA_INT8_ROWSCALE, hq=16), None, None, None, None, None) == OK
+
+    pd = pdesc(batch=2, T=2, P=16, num_pages=100, max_pages=8, kv=b.GQA_INT8_ROWSCALE, hq=16)
+    pool_bytes = 100 * 2 * 8 * 16 * 128
+    pscale_bytes = 100 * 2 * 8 * 16 * 2
+    papp = b._append_paged_int8
+
+    def pcall(desc_, k=K, v_=V, pos=P, table=TABLE, pool=POOL, sc=SC):
+        return papp(ctypes.byref(desc_), k, v_, pos, table, pool, sc, None)
+
+    assert pcall(pd, sc=None) == INVALID
+    assert pcall(pd, sc=SC + 1) == INVALID
+    assert pcall(pd, sc=POOL + pool_bytes - 2) == ALIAS
+    assert pcall(pd, table=SC + pscale_bytes - 4) == ALIAS          # block table inside the scales
+    assert pcall(pd, sc=POOL + pool_bytes) not in (INVALID, ALIAS)
+    assert pcall(pdesc(batch=2, T=2)) == INVALID and "INT8" in b.last_error()
+    assert b._append_paged(ctypes.byref(pd), K, V, P, TABLE, POOL, None) == INVALID
+    assert "gqa_kv_append_paged_int8" in b.last_error()
