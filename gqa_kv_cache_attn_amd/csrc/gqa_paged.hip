@@ -310,11 +310,18 @@ __device__ __forceinline__ size_t query_row(int b, int g, int row, int T) {
 
 // Zeros for every query row of (request b, KV head g): a request of length
 // <= 0, or rows whose causal limit leaves no slot.
+// Query rows of a head in the combine kernels: wave w of workgroup (head,
+// y) takes rows 4 y + w, 4 y + w + 4 gridDim.y, ...; the launch gives each
+// head ceil(T G / 4) workgroups, so every row has a wave of its own and the
+// merges of a head's rows wait for their loads together.
+__device__ __forceinline__ int first_row() { return (int)blockIdx.y * kWaves + (threadIdx.x >> 6); }
+__device__ __forceinline__ int row_stride() { return (int)gridDim.y * kWaves; }
+
 template <int QT, int G>
 __device__ __forceinline__ void zero_rows(const StepArgs& a, int b, int g) {
   const int T = a.q_tokens;
   const int ed = (threadIdx.x & 63) * 2;
-  for (int row = threadIdx.x >> 6; row < T * G; row += kWaves)
+  for (int row = first_row(); row < T * G; row += row_stride())
     Elem<QT>::store2(static_cast<char*>(a.out) + (query_row<G>(b, g, row, T) * kHeadDim + ed) * 2,
                      0.f, 0.f);
 }
@@ -377,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_combine_kernel(StepArgs a)
   const int T = a.q_tokens;
   const int lane = threadIdx.x & 63;
   const int S = a.num_splits;
-  for (int row = threadIdx.x >> 6; row < T * G; row += kWaves) {
+  for (int row = first_row(); row < T * G; row += row_stride()) {
     const size_t qrow = query_row<G>(b, g, row, T);
     char* outp = static_cast<char*>(a.out) + (qrow * kHeadDim + 2 * lane) * 2;
     const int limit = min(row_limit<G>(L, T, row), L);
@@ -485,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_balanced_combine_kernel(St
   if (first_slot < 0) return;
   const int wf = first_slot >> 1;
   const int wl = a.head_pieces[a.batch * kKvHeads + bg];
-  for (int row = threadIdx.x >> 6; row < T * G; row += kWaves) {
+  for (int row = first_row(); row < T * G; row += row_stride()) {
     char* outp = static_cast<char*>(a.out) + (query_row<G>(b, g, row, T) * kHeadDim + 2 * lane) * 2;
     if (row_limit<G>(L, T, row) <= 0) {   // sees no slot: every piece is empty
       E::store2(outp, 0.f, 0.f);
@@ -502,7 +509,8 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_balanced_combine_kernel(St
 template <int QT, int KVT, int G>
 hipError_t enqueue_paged_typed(const StepArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
   hipError_t e;
-  const dim3 heads((unsigned)a.batch * kKvHeads);
+  // Combine grid: per head, one workgroup per 4 query rows (one wave a row).
+  const dim3 heads((unsigned)a.batch * kKvHeads, (unsigned)((a.q_tokens * G + kWaves - 1) / kWaves));
   if (a.grid_wgs > 0) {
     // INT8 pools of pages of at least 64 slots: whole 64-slot blocks per wave.
     bool blocks = false;
