@@ -105,11 +105,12 @@ struct PagedHead {
 // 2 (t % 64) + {0, 1}; a row that saw no slot of the range gets M = -inf,
 // l = 0. Rows >= T*G are passed too and must be ignored. Ends with a barrier.
 //
-// kBlocks (INT8 pools of pages of at least 64 slots; the caller checks): each
-// wave takes whole 64-slot blocks, as the contiguous balanced kernel does, so
-// each 128-byte line of a scale plane is read once. Otherwise the waves take
-// interleaved tiles.
-template <int QT, int KVT, int G, bool kBlocks = false, class Emit>
+// kBlocks (INT8 pools; the caller checks): each wave takes whole 64-slot
+// blocks, as the contiguous balanced kernel does, so each 128-byte line of a
+// scale plane is read once. 1: pages of at least 64 slots (a block lies in
+// one page); 2: pages of 16 or 32 slots (a block spans 4 or 2 pages; the
+// scale pool must fit 32-bit offsets). 0: the waves take interleaved tiles.
+template <int QT, int KVT, int G, int kBlocks = 0, class Emit>
 __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, int c0, int c1,
                                              int L, PagedLds& lds, Emit&& emit) {
   b = __builtin_amdgcn_readfirstlane(b);
@@ -165,7 +166,101 @@ __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, in
 #pragma unroll
   for (int c = 0; c < 8; ++c) st.o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (KVT == kI8 && kBlocks) {
+  if constexpr (KVT == kI8 && kBlocks == 2) {
+    // Whole 64-slot blocks over pages of 16 or 32 slots: each of a block's
+    // four tiles gets the descriptors of its own page, and the block's row
+    // scales come from one 2-byte load per lane and plane through a
+    // descriptor over the whole scale pool, at the lane's page (slots at or
+    // past c1 get an offset past the pool: they read 0). Page ids come from
+    // the table four per block (its tiles' pages), sixteen blocks per load.
+    int base = __builtin_amdgcn_readfirstlane(c0 + 64 * wave);
+    if (base < c1) {
+      u32x4* sk = lds.k[wave];
+      const int last_index = (c1 - 1) >> ph.shift;
+      const int P = 1 << ph.shift;
+      constexpr int kBlock = 4 * kStep;              // slots between a wave's blocks
+      const int base0 = base;
+      // lane i: page of slot first + 256 (i / 4) + 16 (i % 4)
+      auto tile_ids = [&](int first) -> int {
+        const int idx = min((first + kBlock * (lane >> 2) + kTile * (lane & 3)) >> ph.shift,
+                            last_index);
+        return min(max(ph.table_row[idx], 0), ph.num_pages - 1);
+      };
+      int kb0 = 0;                                   // block held by lanes 0..3
+      int ids = tile_ids(base0);
+      const u32 pool_bytes = (u32)a.num_pages * (u32)(2 * kKvHeads * 2) * (u32)P;
+      const __amdgpu_buffer_rsrc_t ks_pool = make_rsrc(ph.scales, pool_bytes);
+      // Byte offset of the K scale of slot bbase + lane (the V scale is one
+      // plane further on, + 8 P 2 bytes); past the pool when at or past c1.
+      auto scale_offset = [&](int kb, int bbase) -> u32 {
+        const int page = __shfl(ids, 4 * (kb - kb0) + (lane >> 4));
+        const int slot = bbase + lane;
+        return slot < c1 ? (u32)page * (u32)(2 * kKvHeads * 2 * P) + (u32)(g * 2 * P) +
+                               (u32)((slot & (P - 1)) * 2)
+                         : 0xffffffffu;
+      };
+      auto load_scales = [&](u32 off) -> BlockScales {
+        BlockScales r;
+        r.k = __builtin_amdgcn_raw_buffer_load_b16(ks_pool, off, 0, kLoadAux);
+        r.v = __builtin_amdgcn_raw_buffer_load_b16(
+            ks_pool, off == 0xffffffffu ? off : off + (u32)(kKvHeads * 2 * P), 0, kLoadAux);
+        return r;
+      };
+      int kb = 0, row;
+      BlockQuads sc = pack_block_scales(load_scales(scale_offset(0, base)), lane);
+      Tile<KVT> ta, tb;
+      {
+        const Planes p0 = ph.planes(base, __builtin_amdgcn_readlane(ids, 0), row);
+        load_tile<KVT, false>(ta, p0, row, lane);
+      }
+      for (;;) {
+        // this block's tile pages, read before the ids may move on
+        const int o = 4 * (kb - kb0);
+        const int pg1 = __builtin_amdgcn_readlane(ids, o + 1);
+        const int pg2 = __builtin_amdgcn_readlane(ids, o + 2);
+        const int pg3 = __builtin_amdgcn_readlane(ids, o + 3);
+        if (kb + 1 - kb0 >= 16) {
+          kb0 = kb + 1;
+          ids = tile_ids(base0 + kBlock * kb0);
+        }
+        const int pgn = __builtin_amdgcn_readlane(ids, 4 * (kb + 1 - kb0));
+        {
+          const Planes p1 = ph.planes(base + kTile, pg1, row);
+          load_tile<KVT, false>(tb, p1, row, lane);                 // past c1: reads 0
+        }
+        const BlockScales sc_next = load_scales(scale_offset(kb + 1, base + kBlock));
+        tile_scales(ta, sc, 0, lane);
+        process_tile<QT, KVT, kRowsMax>(st, ta, qf, sk, base, lim, lane, a.scale_log2);
+        if (base + kTile >= c1) break;
+        {
+          const Planes p2 = ph.planes(base + 2 * kTile, pg2, row);
+          load_tile<KVT, false>(ta, p2, row, lane);
+        }
+        tile_scales(tb, sc, 1, lane);
+        process_tile<QT, KVT, kRowsMax>(st, tb, qf, sk, base + kTile, lim, lane, a.scale_log2);
+        if (base + 2 * kTile >= c1) break;
+        {
+          const Planes p3 = ph.planes(base + 3 * kTile, pg3, row);
+          load_tile<KVT, false>(tb, p3, row, lane);
+        }
+        tile_scales(ta, sc, 2, lane);
+        process_tile<QT, KVT, kRowsMax>(st, ta, qf, sk, base + 2 * kTile, lim, lane,
+                                        a.scale_log2);
+        if (base + 3 * kTile >= c1) break;
+        {
+          const Planes pn = ph.planes(base + kBlock, pgn, row);   // the next block's first tile
+          load_tile<KVT, false>(ta, pn, row, lane);
+        }
+        tile_scales(tb, sc, 3, lane);
+        process_tile<QT, KVT, kRowsMax>(st, tb, qf, sk, base + 3 * kTile, lim, lane,
+                                        a.scale_log2);
+        base += kBlock;
+        ++kb;
+        if (base >= c1) break;
+        sc = pack_block_scales(sc_next, lane);
+      }
+    }
+  } else if constexpr (KVT == kI8 && kBlocks == 1) {
     // Whole 64-slot blocks, wave w the blocks at c0 + 64 w + 256 k; a block
     // lies in one page (ranges start on 64-slot boundaries), so it takes one
     // set of descriptors, and its scales one 2-byte load per lane and plane,
@@ -400,9 +495,9 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_combine_kernel(StepArgs a)
 // Balanced split over the logical slots (the contiguous kernel's scheme):
 // workgroup w takes slabs [bound(w), bound(w + 1)); heads covered whole are
 // written directly, first and last pieces go to slots 2w and 2w + 1 of
-// kRowsMax rows each. kBlocks: see attend_paged (INT8 pools of pages of at
-// least 64 slots).
-template <int QT, int KVT, int G, bool kBlocks>
+// kRowsMax rows each. kBlocks: see attend_paged (INT8 pools: 1 for pages of
+// at least 64 slots, 2 for pages of 16 or 32).
+template <int QT, int KVT, int G, int kBlocks>
 __global__ __launch_bounds__(kThreads, GQA_PAGED_MIN_WAVES_PER_SIMD) void
 gqa_paged_balanced_kernel(StepArgs a) {
   using E = Elem<QT>;
@@ -455,7 +550,7 @@ gqa_paged_balanced_kernel(StepArgs a) {
                                       [&](int row, float M, float lsum, float o0, float o1) {
       if (row >= R) return;
       int ed = lane * 2;
-      if constexpr (kBlocks) asm volatile("" : "+v"(ed));   // not hoisted across pieces
+      if constexpr (kBlocks != 0) asm volatile("" : "+v"(ed));   // not hoisted across pieces
       if (whole) {
         const float inv = lsum > 0.f ? a.v_scale / lsum : 0.f;
         E::store2(static_cast<char*>(a.out) + (query_row<G>(b, g, row, T) * kHeadDim + ed) * 2,
@@ -512,16 +607,22 @@ hipError_t enqueue_paged_typed(const StepArgs& a, hipStream_t stream, hipEvent_t
   // Combine grid: per head, one workgroup per 4 query rows (one wave a row).
   const dim3 heads((unsigned)a.batch * kKvHeads, (unsigned)((a.q_tokens * G + kWaves - 1) / kWaves));
   if (a.grid_wgs > 0) {
-    // INT8 pools of pages of at least 64 slots: whole 64-slot blocks per wave.
-    bool blocks = false;
+    // INT8 pools: whole 64-slot blocks per wave, within one page (pages of
+    // 64+ slots) or across the pages of 16 or 32 slots a block spans, when
+    // the scale pool's offsets fit 32 bits.
+    int blocks = 0;
     if constexpr (KVT == kI8) {
-      blocks = a.page_shift >= 6;
-      if (blocks)
-        hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, true>), dim3(a.grid_wgs),
+      const int64_t scale_pool = (int64_t)a.num_pages * (2 * kKvHeads * 2) << a.page_shift;
+      blocks = a.page_shift >= 6 ? 1 : (scale_pool < (int64_t)UINT32_MAX ? 2 : 0);
+      if (blocks == 1)
+        hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, 1>), dim3(a.grid_wgs),
+                           dim3(kThreads), 0, stream, a);
+      else if (blocks == 2)
+        hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, 2>), dim3(a.grid_wgs),
                            dim3(kThreads), 0, stream, a);
     }
-    if (!blocks)
-      hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, false>), dim3(a.grid_wgs),
+    if (blocks == 0)
+      hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, 0>), dim3(a.grid_wgs),
                          dim3(kThreads), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev_mid != nullptr && (e = hipEventRecord(ev_mid, stream)) != hipSuccess) return e;
@@ -550,7 +651,7 @@ int paged_balanced_grid_typed() {
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&gqa_paged_balanced_kernel<QT, KVT, G, false>), kThreads,
+          &per_cu, reinterpret_cast<const void*>(&gqa_paged_balanced_kernel<QT, KVT, G, 0>), kThreads,
           0) != hipSuccess)
     return 0;
   if (balanced_wgs_per_cu<KVT>() > 0) per_cu = std::min(per_cu, balanced_wgs_per_cu<KVT>());

@@ -68,9 +68,10 @@ def test_paged_balanced_split_partitions(qd, kd, hq, T, case, P):
 
 @pytest.mark.parametrize("qd,T", [("bf16", 2), ("f16", 5)])
 @pytest.mark.parametrize("case", ["fewer_slabs_than_workgroups", "one_long_head", "mixed_with_empty"])
-@pytest.mark.parametrize("P", [128, 256])
-def test_paged_int8_block_order_on_large_pages(qd, T, case, P):
-    """int8 pools with pages of 64 slots or more walk 64-slot blocks."""
+@pytest.mark.parametrize("P", [16, 32, 128, 256])
+def test_paged_int8_block_order(qd, T, case, P):
+    """int8 pools walk 64-slot blocks on the balanced route: within one page
+    (128, 256) or across the 4 or 2 pages a block spans (16, 32)."""
     _balanced_partition_case(qd, "int8", 16, T, case, P)
 
 
@@ -127,6 +128,30 @@ def test_paged_garbage_outside_the_prefix_is_never_read(kd, num_splits, P):
         inp["kv_scales"][~used] = float("nan")
     out, _ = run_paged(inp, "prepared", num_splits=num_splits)
     compare_paged(out, inp, range(4), f"paged nan-garbage {kd}")
+
+
+@pytest.mark.parametrize("P", [16, 32, 64])
+def test_paged_int8_balanced_route_never_reads_past_the_prefix(P):
+    """The balanced route over an int8 pool: NaN codes and NaN row scales in
+    every unused page and every slot past a length (the block order's scale
+    loads must read 0 there, not the pool's other rows)."""
+    w = _pw("bf16", "int8", 16, 2, C=8192, B=4, P=P, seed=265)
+    lens = torch.tensor([2, 3000, 5001, 8191], dtype=torch.int32)
+    inp = make_paged_inputs(w, device="cuda", seq_lens=lens)
+    pool, table, sc = inp["kv_pages"], inp["block_table"], inp["kv_scales"]
+    used = torch.zeros(pool.shape[0], dtype=torch.bool, device="cuda")
+    for b, L in enumerate(lens.tolist()):
+        n = -(-L // P)
+        used[table[b, :n].long()] = True
+        last = int(table[b, n - 1])
+        if L % P:
+            pool[last, :, :, L % P:] = 127
+            sc[last, :, :, L % P:] = float("nan")
+    pool[~used] = 127
+    sc[~used] = float("nan")
+    out, prep = run_paged(inp, "prepared")
+    assert prep.plan["route"] == 2
+    compare_paged(out, inp, range(4), f"paged int8 balanced nan-garbage P={P}")
 
 
 @pytest.mark.parametrize("num_splits", [None, 1, 2])
