@@ -14,7 +14,7 @@ duration from HIP events recorded on the launch stream around every timed
 launch, against 8 TB/s), cold-cache microseconds per call, and the CPU
 oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps 50] [--warmup 200] [--workload NAME] [--num-splits N]
+    python bench.py [--steps 50] [--warmup W] [--workload NAME] [--num-splits N]
 """
 
 from __future__ import annotations
@@ -40,9 +40,11 @@ def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first; the clocks take some tens of milliseconds "
-                         "of steady load to settle after the idle input setup")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: at least 200 steps and at least "
+                         "2 s of them; the clocks take some tens of milliseconds of steady "
+                         "load to settle after the idle input setup, and right after other "
+                         "GPU work the memory can read ~5%% slower for a second or more)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--num-splits", type=int, default=0, help="0 = automatic")
     ap.add_argument("--fused-combine", action="store_true",
@@ -271,9 +273,18 @@ def main():
     plan["combine"] = "fused (last workgroup)" if args.fused_combine else "separate kernel"
     stream = torch.cuda.current_stream(dev)
 
-    K, W = args.steps, args.warmup
-    for _ in range(W):
-        b.launch_gqa_decode_prepared(prep)
+    K = args.steps
+    if args.warmup is not None:
+        W = args.warmup
+        for _ in range(W):
+            b.launch_gqa_decode_prepared(prep)
+    else:
+        W, w0 = 0, time.perf_counter()
+        while W < 200 or time.perf_counter() - w0 < 2.0:
+            for _ in range(50):
+                b.launch_gqa_decode_prepared(prep)
+            W += 50
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
     def new_event():
