@@ -215,9 +215,9 @@ def cpu_baseline(inp, w, budget_s):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the decode step is sharded by request/KV head/sequence only by design, not run).",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the library "
+              "runs the decode step on one GPU (sharding by request, KV head or sequence is a "
+              "design, not code).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -166,7 +166,7 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 # torch's current-stream lookup that returns the raw handle without building
 # a Stream object (about a microsecond less per launch); the public call is
-# the fallback where this build of torch lacks it.
+# the fallback where the installed torch lacks it.
 _raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
