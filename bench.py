@@ -58,6 +58,10 @@ def parse_args():
                     help="paged workloads: override the page size (slots per page)")
     ap.add_argument("--q-tokens", type=int, default=0,
                     help="paged workloads: override the query tokens per request")
+    ap.add_argument("--page-order", choices=("random", "ordered"), default="random",
+                    help="paged workloads: the block table as drawn (a random permutation "
+                         "of the pool) or each request's pages in pool order, as an "
+                         "allocator that hands out pages in turn gives them")
     ap.add_argument("--shape", default="",
                     help="override batch,capacity,len_lo,len_hi (e.g. 16,131072,65536,131072)")
     return ap.parse_args()
@@ -237,18 +241,24 @@ def main():
         B, C, lo, hi = (int(x) for x in args.shape.split(","))
         w = dataclasses.replace(w, batch=B, capacity=C, len_lo=lo, len_hi=hi,
                                 name=f"{w.name}[B={B},C={C},L={lo}..{hi}]")
-    if args.page_size or args.q_tokens:
+    if args.page_size or args.q_tokens or args.page_order != "random":
         if not w.page_size:
-            print("--page-size / --q-tokens apply to paged workloads only", file=sys.stderr)
+            print("--page-size / --q-tokens / --page-order apply to paged workloads only",
+                  file=sys.stderr)
             sys.exit(2)
         import dataclasses
         w = dataclasses.replace(w, page_size=args.page_size or w.page_size,
                                 q_tokens=args.q_tokens or w.q_tokens,
                                 name=f"{w.name}[P={args.page_size or w.page_size},"
-                                     f"T={args.q_tokens or w.q_tokens}]")
+                                     f"T={args.q_tokens or w.q_tokens}]"
+                                     + ("[pages in order]" if args.page_order == "ordered" else ""))
     print(f"[bench] device {arch}; workload {w.name}; generating inputs", file=sys.stderr, flush=True)
     paged = w.page_size > 0
     inp = make_paged_inputs(w, device=dev) if paged else make_inputs(w, device=dev)
+    if paged and args.page_order == "ordered":
+        B, max_pages = inp["block_table"].shape
+        inp["block_table"] = torch.arange(B * max_pages, device=dev,
+                                          dtype=torch.int32).reshape(B, max_pages)
     lens = inp["seq_lens"].cpu().tolist()
     nbytes = algorithmic_bytes(lens, w.kv_dtype, w.batch, w.num_q_heads, w.q_tokens, w.page_size)
     out = torch.empty_like(inp["q"])
@@ -438,7 +448,8 @@ def main():
         "dtype": {"fp8_e4m3": "fp8_e4m3->bf16", "int8": f"int8+bf16 row scales->{w.q_dtype}"}
                  .get(w.kv_dtype, w.kv_dtype),
         "data": "synthetic",
-        "config": {**w.describe(), "seq_lens_sum": int(sum(lens)),
+        "config": {**w.describe(), **({"page_order": args.page_order} if paged else {}),
+                   "seq_lens_sum": int(sum(lens)),
                    "algorithmic_bytes_per_step": nbytes, "plan": plan},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "us_per_call": round(ms_per_step * 1e3, 2),
