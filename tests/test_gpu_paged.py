@@ -199,6 +199,32 @@ def test_paged_equals_the_contiguous_entry_point_on_an_identity_table():
     assert torch.equal(out[:, 0].view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("P", [16, 64])
+def test_pages_in_pool_order_give_the_same_result_as_shuffled_pages(P):
+    """The same logical cache under the drawn (shuffled) table and with every
+    request's pages moved into pool order: the kernel sees the same rows in the
+    same slots, so the two outputs agree bit for bit (and with the oracle)."""
+    b = binding()
+    w = _pw("bf16", "bf16", 32, 3, C=8192, B=4, P=P, seed=285)
+    inp = make_paged_inputs(w, device="cuda")
+    table = inp["block_table"]
+    B, max_pages = table.shape
+    ordered = torch.arange(B * max_pages, dtype=torch.int32, device="cuda").view(B, max_pages)
+    pool_ordered = torch.empty_like(inp["kv_pages"])
+    pool_ordered[ordered.view(-1).long()] = inp["kv_pages"][table.view(-1).long()]
+    outs = []
+    for pool, tab in ((inp["kv_pages"], table), (pool_ordered, ordered)):
+        out = torch.empty_like(inp["q"])
+        prep = b.prepare_gqa_decode_paged(inp["q"], pool, tab, inp["seq_lens"], out,
+                                          inp["q_scale"])
+        assert prep.plan["route"] == 2   # the balanced split, as the bench workload takes
+        b.launch_gqa_decode_prepared(prep)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    compare_paged(outs[1], inp, [0, B - 1], f"{w.name}/pool order")
+
+
 @pytest.mark.parametrize("plan", ["balanced", "chunked"])
 def test_paged_graph_replay_with_rewritten_lengths_and_pages(plan):
     b = binding()
