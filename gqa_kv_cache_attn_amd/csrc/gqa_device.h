@@ -549,17 +549,52 @@ __device__ __forceinline__ void merge_batch(const float2* po, RowFn& row, size_t
   }
 }
 
+// merge_rows for n <= NB rows: the (m, l) pair of row k (lane k) and all NB
+// partial O rows are loaded before any of them is waited on, so the merge
+// costs one round trip to memory. Addresses depend only on n, not on the
+// weights; rows at or past n read the first row again and, like empty rows
+// (max -inf, O possibly stale), enter with weight 0 through a select.
+template <int NB, int QT, typename RowFn>
+__device__ __forceinline__ void merge_few(const StepArgs& a, int n, RowFn& row, char* outp) {
+  using E = Elem<QT>;
+  const int lane = threadIdx.x & 63;
+  const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+  const float2* po = reinterpret_cast<const float2*>(a.part_o);
+  const size_t fallback = row(0);
+  const float2 mv = ml[lane < n ? row(lane) : fallback];
+  float2 v[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) v[u] = po[(u < n ? row(u) : fallback) * (kHeadDim / 2) + lane];
+  const float mk = lane < n ? mv.x : -INFINITY;
+  const float M = wave_max(mk);   // finite: at least one row holds data
+  const float wk = mk != -INFINITY ? fast_exp2(mk - M) : 0.f;
+  const float lsum = wave_sum(wk != 0.f ? wk * mv.y : 0.f);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), u));
+    o0 = fmaf(f, f != 0.f ? v[u].x : 0.f, o0);
+    o1 = fmaf(f, f != 0.f ? v[u].y : 0.f, o1);
+  }
+  const float inv = a.v_scale / lsum;
+  E::store2(outp, o0 * inv, o1 * inv);
+}
+
 // Log-sum-exp merge of n partial rows of one query head, run by one wave
 // (lane l owns dims 2l and 2l + 1):
 //   M = max_k m_k,  out = v_scale * sum_k 2^(m_k - M) O_k / sum_k 2^(m_k - M) l_k
 // row(k) gives the k-th partial row. A row whose max is -inf is empty (a
 // workgroup that had no slabs marked it): it gets weight 0 and its O row,
-// possibly stale, is never read. The (m, l) pairs of 64 rows at a time are
+// possibly stale, never enters the sum. Up to 32 rows take merge_few's
+// single round of loads. Beyond that the (m, l) pairs of 64 rows at a time are
 // loaded one per lane; the O rows follow in batches of 32, 16 and then 8
 // independent loads, so a head split into 64 pieces (one request spread over
 // the whole grid) waits for two rounds of loads, not eight.
 template <int QT, typename RowFn>
 __device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, char* outp) {
+  if (n <= 8) return merge_few<8, QT>(a, n, row, outp);
+  if (n <= 16) return merge_few<16, QT>(a, n, row, outp);
+  if (n <= 32) return merge_few<32, QT>(a, n, row, outp);
   using E = Elem<QT>;
   const int lane = threadIdx.x & 63;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);

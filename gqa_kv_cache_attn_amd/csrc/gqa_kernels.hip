@@ -399,18 +399,22 @@ __global__ __launch_bounds__(kThreads) void gqa_balanced_combine_kernel(StepArgs
   if (r >= G) return;
   const size_t head = ((size_t)b * kKvHeads + g) * G + r;
   char* outp = static_cast<char*>(a.out) + (head * kHeadDim + 2 * lane) * 2;
-  const int nsb = (a.slab_prefix[b + 1] - a.slab_prefix[b]) / kKvHeads;
+  // Where the attention kernel put the head's pieces: the first piece's slot
+  // (-1: written whole) and the workgroup of the last piece. The workgroups
+  // in between hold the head in their first slot (or, with no slab, mark it
+  // empty). The empty asm takes the four values at once, so their loads
+  // issue together instead of one after another behind the branches below.
+  int first_slot = a.head_pieces[bg];
+  int wl = a.head_pieces[a.batch * kKvHeads + bg];
+  int p0 = a.slab_prefix[b], p1 = a.slab_prefix[b + 1];
+  asm volatile("" : "+s"(first_slot), "+s"(wl), "+s"(p0), "+s"(p1));
+  const int nsb = (p1 - p0) / kKvHeads;
   if (nsb == 0) {
     E::store2(outp, 0.f, 0.f);
     return;
   }
-  // Where the attention kernel put the head's pieces: the first piece's slot
-  // (-1: written whole) and the workgroup of the last piece. The workgroups
-  // in between hold the head in their first slot (or, with no slab, mark it empty).
-  const int first_slot = a.head_pieces[bg];
   if (first_slot < 0) return;
   const int wf = first_slot >> 1;
-  const int wl = a.head_pieces[a.batch * kKvHeads + bg];
   merge_rows<QT>(a, wl - wf + 1,
                  [&](int k) -> size_t {
                    return (k == 0 ? (size_t)first_slot : 2 * (size_t)(wf + k)) * kGroup + r;

@@ -575,18 +575,23 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_balanced_combine_kernel(St
   const int g = bg % kKvHeads;
   const int lane = threadIdx.x & 63;
   const int T = a.q_tokens;
-  const int L = min(max(a.seq_lens[b], 0), a.capacity);
-  const int nsb = (a.slab_prefix[b + 1] - a.slab_prefix[b]) / kKvHeads;
+  // The head's first-piece slot (-1: written whole) and last workgroup, as
+  // the attention kernel recorded them. The empty asm takes them with the
+  // length and the request's slab bounds at once, so the five loads issue
+  // together instead of one after another behind the branches below.
+  int first_slot = a.head_pieces[bg];
+  int wl = a.head_pieces[a.batch * kKvHeads + bg];
+  int len = a.seq_lens[b];
+  int p0 = a.slab_prefix[b], p1 = a.slab_prefix[b + 1];
+  asm volatile("" : "+s"(first_slot), "+s"(wl), "+s"(len), "+s"(p0), "+s"(p1));
+  const int L = min(max(len, 0), a.capacity);
+  const int nsb = (p1 - p0) / kKvHeads;
   if (nsb == 0) {
     zero_rows<QT, G>(a, b, g);
     return;
   }
-  // The head's first-piece slot (-1: written whole) and last workgroup, as
-  // the attention kernel recorded them.
-  const int first_slot = a.head_pieces[bg];
   if (first_slot < 0) return;
   const int wf = first_slot >> 1;
-  const int wl = a.head_pieces[a.batch * kKvHeads + bg];
   for (int row = first_row(); row < T * G; row += row_stride()) {
     char* outp = static_cast<char*>(a.out) + (query_row<G>(b, g, row, T) * kHeadDim + 2 * lane) * 2;
     if (row_limit<G>(L, T, row) <= 0) {   // sees no slot: every piece is empty
