@@ -140,16 +140,25 @@ int device_cus(int dev) {
 #ifndef GQA_SHARE_ODD
 #define GQA_SHARE_ODD 920
 #endif
+// The paged kernel at two workgroups per CU sees a larger odd-XCD gap: a sweep
+// of its odd share (840-920) was fastest at 860 on the 16-slot bf16 and 64-slot
+// fp8 pools (1.2-1.3% over 920); the INT8 pool (three per CU) was slower below
+// 920, and the contiguous kernels were within noise of 920 at 860-900.
+#ifndef GQA_SHARE_ODD_PAGED_TWO
+#define GQA_SHARE_ODD_PAGED_TWO 860
+#endif
 
 // a.grid_wgs must be set: the shares depend on how many workgroups share a CU.
-void set_shares(gqa::StepArgs& a, int tier_size) {
+void set_shares(gqa::StepArgs& a, int tier_size, bool paged) {
   int tier[gqa::kShareTiers] = {1000, GQA_SHARE_TIER1, GQA_SHARE_TIER2, GQA_SHARE_TIER3};
-  if (tier_size > 0 && a.grid_wgs == 2 * tier_size) tier[1] = GQA_SHARE_TIER1_OF_TWO;
+  const bool two = tier_size > 0 && a.grid_wgs == 2 * tier_size;
+  if (two) tier[1] = GQA_SHARE_TIER1_OF_TWO;
+  const int odd = paged && two ? GQA_SHARE_ODD_PAGED_TWO : GQA_SHARE_ODD;
   // tier_size 0 (unknown) or a grid of one tier: plain equal shares
   a.tier_size = tier_size > 0 ? tier_size : (1 << 28);
   for (int t = 0; t < gqa::kShareTiers; ++t) {
     a.share[2 * t] = tier[t];
-    a.share[2 * t + 1] = tier[t] * GQA_SHARE_ODD / 1000;
+    a.share[2 * t + 1] = tier[t] * odd / 1000;
   }
 }
 
@@ -389,7 +398,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.head_pieces = a.slab_prefix ? a.slab_prefix + d->batch + 1 : nullptr;
   a.fused_combine = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
   a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
-  set_shares(a, tier_size);
+  set_shares(a, tier_size, pg.on);
   a.batch = d->batch;
   a.capacity = d->capacity;
   a.num_splits = p.num_splits;
