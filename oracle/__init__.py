@@ -27,9 +27,11 @@ from .gqa_oracle import (  # noqa: F401
     GROUP,
     decode_bf16_bits,
     decode_e4m3fn_bits,
+    decode_e4m3fn_lookup,
     decode_f16_bits,
     decode_int8_rows,
     decode_storage,
+    e4m3fn_table,
     gqa_decode_head,
     gqa_decode_reference,
     gqa_decode_weights,

@@ -81,6 +81,34 @@ def decode_e4m3fn_bits(codes: np.ndarray) -> np.ndarray:
     return out
 
 
+def e4m3fn_table() -> np.ndarray:
+    """The 256 E4M3FN code values as fp64, index = code byte.
+
+    Built once by running decode_e4m3fn_bits (the format definition above) on
+    every code; a copy is returned so callers cannot alter the cached table.
+    """
+    global _E4M3FN_TABLE
+    if _E4M3FN_TABLE is None:
+        _E4M3FN_TABLE = decode_e4m3fn_bits(np.arange(256, dtype=np.uint8))
+    return _E4M3FN_TABLE.copy()
+
+
+_E4M3FN_TABLE = None
+
+
+def decode_e4m3fn_lookup(codes: np.ndarray) -> np.ndarray:
+    """decode_e4m3fn_bits by table lookup: the same values, one gather per byte.
+
+    The uint8 cache bytes are the float8_e4m3fn bit patterns (Thor FP8 KV
+    notes, patch 1 item 5), so decoding a byte is indexing the 256-entry
+    table of decoded codes; this is what makes a full-size fp8 cache
+    (gigabytes of codes) affordable on the CPU.
+    """
+    if _E4M3FN_TABLE is None:
+        e4m3fn_table()
+    return _E4M3FN_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
 def decode_bf16_bits(bits: np.ndarray) -> np.ndarray:
     """Decode bfloat16 bit patterns to fp64 (bf16 is the top half of an fp32)."""
     b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
@@ -112,7 +140,7 @@ def decode_storage(bits: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return decode_bf16_bits(bits)
     if dtype == "fp8_e4m3":
-        return decode_e4m3fn_bits(bits)
+        return decode_e4m3fn_lookup(bits)
     raise ValueError(f"unknown storage dtype {dtype!r}")
 
 

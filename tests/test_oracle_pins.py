@@ -20,7 +20,10 @@ from oracle import (
     NUM_Q_HEADS,
     decode_bf16_bits,
     decode_e4m3fn_bits,
+    decode_e4m3fn_lookup,
     decode_f16_bits,
+    decode_storage,
+    e4m3fn_table,
     gqa_decode_head,
     gqa_decode_reference,
     gqa_decode_weights,
@@ -68,6 +71,30 @@ def test_e4m3fn_anchor_values_from_spec():
                 assert got == want and math.copysign(1, got) == math.copysign(1, want), code_s
             n += 1
     assert n >= 10
+
+
+def test_e4m3fn_lookup_equals_the_definition_on_every_code():
+    """The table decoder is the definition decoder evaluated once per code:
+    equal on all 256 codes (NaN where it is NaN, signed zeros kept) and on a
+    multi-dimensional array of random bytes, the shape a cache slice has."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = decode_e4m3fn_bits(codes)
+    for got in (e4m3fn_table(), decode_e4m3fn_lookup(codes)):
+        assert got.dtype == np.float64 and got.shape == (256,)
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        fin = ~np.isnan(ref)
+        assert np.array_equal(got[fin], ref[fin])
+        assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    rng = np.random.default_rng(11)
+    arr = rng.integers(0, 256, size=(3, 2, 5, 128), dtype=np.uint8)
+    got, ref = decode_storage(arr, "fp8_e4m3"), decode_e4m3fn_bits(arr)
+    assert got.shape == arr.shape
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(ref)], ref[~np.isnan(ref)])
+    # The cached table cannot be altered through the copy e4m3fn_table returns.
+    t = e4m3fn_table()
+    t[:] = 0.0
+    assert decode_e4m3fn_lookup(np.array([0x38], dtype=np.uint8))[0] == 1.0
 
 
 def test_e4m3fn_all_finite_codes_exact_in_bf16_and_f16():
