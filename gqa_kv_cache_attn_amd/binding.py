@@ -186,17 +186,27 @@ def _check_devices(*ts):
         raise ValueError("q, kv, seq_lens and out must be on the same GPU")
 
 
+def _check_per_request(t: torch.Tensor, batch: int, name: str):
+    """seq_lens / positions: int32 [batch], contiguous. The kernels read one
+    entry per request, so a shorter tensor would be read past its end."""
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    if t.dim() != 1 or t.shape[0] != batch:
+        raise ValueError(f"{name} must be [batch] = [{batch}], got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def gqa_decode(q: torch.Tensor, kv: torch.Tensor, seq_lens: torch.Tensor,
                q_scale: float = 1.0, out: Optional[torch.Tensor] = None,
                k_scale: float = 1.0, v_scale: float = 1.0, stream=None) -> torch.Tensor:
     """Enqueue one decode step on the current stream; returns ``out``."""
     if out is None:
         out = torch.empty_like(q)
-    _check_devices(q, kv, seq_lens, out)
-    if seq_lens.dtype != torch.int32:
-        raise ValueError("seq_lens must be int32")
+    _check_per_request(seq_lens, q.shape[0] if q.dim() > 0 else -1, "seq_lens")
     if out.dtype != q.dtype or out.shape != q.shape:
         raise ValueError("out must match q's shape and dtype")
+    _check_devices(q, kv, seq_lens, out)
     desc = make_desc(q, kv, k_scale, v_scale)
     with torch.cuda.device(q.device):
         st = _gqa_decode(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(seq_lens), q_scale,
@@ -220,12 +230,11 @@ def gqa_decode_int8(q: torch.Tensor, kv: torch.Tensor, kv_scales: torch.Tensor,
     """gqa_decode over an int8 cache with bf16 row scales [batch, 2, 8, capacity]."""
     if out is None:
         out = torch.empty_like(q)
-    _check_devices(q, kv, kv_scales, seq_lens, out)
     _check_scales(kv, kv_scales)
-    if seq_lens.dtype != torch.int32:
-        raise ValueError("seq_lens must be int32")
+    _check_per_request(seq_lens, q.shape[0] if q.dim() > 0 else -1, "seq_lens")
     if out.dtype != q.dtype or out.shape != q.shape:
         raise ValueError("out must match q's shape and dtype")
+    _check_devices(q, kv, kv_scales, seq_lens, out)
     desc = make_desc(q, kv, k_scale, v_scale)
     with torch.cuda.device(q.device):
         st = _gqa_decode_int8(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(kv_scales),
@@ -280,11 +289,10 @@ def prepare_gqa_decode(q: torch.Tensor, kv: torch.Tensor, seq_lens: torch.Tensor
                        num_splits: Optional[int] = None, k_scale: float = 1.0,
                        v_scale: float = 1.0, fused_combine: bool = False) -> GqaPrepared:
     """Validate, plan and allocate the split workspace once (outside capture)."""
-    _check_devices(q, kv, seq_lens, out)
-    if seq_lens.dtype != torch.int32:
-        raise ValueError("seq_lens must be int32")
+    _check_per_request(seq_lens, q.shape[0] if q.dim() > 0 else -1, "seq_lens")
     if out.dtype != q.dtype or out.shape != q.shape:
         raise ValueError("out must match q's shape and dtype")
+    _check_devices(q, kv, seq_lens, out)
     desc = make_desc(q, kv, k_scale, v_scale, fused_combine)
     h = _vp()
     with torch.cuda.device(q.device):
@@ -299,12 +307,11 @@ def prepare_gqa_decode_int8(q: torch.Tensor, kv: torch.Tensor, kv_scales: torch.
                             num_splits: Optional[int] = None, k_scale: float = 1.0,
                             v_scale: float = 1.0, fused_combine: bool = False) -> GqaPrepared:
     """prepare_gqa_decode over an int8 cache with bf16 row scales."""
-    _check_devices(q, kv, kv_scales, seq_lens, out)
     _check_scales(kv, kv_scales)
-    if seq_lens.dtype != torch.int32:
-        raise ValueError("seq_lens must be int32")
+    _check_per_request(seq_lens, q.shape[0] if q.dim() > 0 else -1, "seq_lens")
     if out.dtype != q.dtype or out.shape != q.shape:
         raise ValueError("out must match q's shape and dtype")
+    _check_devices(q, kv, kv_scales, seq_lens, out)
     desc = make_desc(q, kv, k_scale, v_scale, fused_combine)
     h = _vp()
     with torch.cuda.device(q.device):
@@ -334,17 +341,26 @@ def make_paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.
 
 
 def _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out):
-    ts = [q, kv_pages, block_table, seq_lens, out] + ([kv_scales] if kv_scales is not None else [])
-    _check_devices(*ts)
-    if seq_lens.dtype != torch.int32 or block_table.dtype != torch.int32:
-        raise ValueError("seq_lens and block_table must be int32")
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    _check_per_request(seq_lens, q.shape[0] if q.dim() > 0 else -1, "seq_lens")
     if out.dtype != q.dtype or out.shape != q.shape:
         raise ValueError("out must match q's shape and dtype")
+    # The pool's rows must be as wide as q's (the kernels step rows at q's
+    # head_dim) and hold 8 KV heads; the C side sees only a pointer.
+    if q.dim() != 4 or kv_pages.dim() != 5 or kv_pages.shape[1] != 2 or \
+            kv_pages.shape[2] != NUM_KV_HEADS or kv_pages.shape[4] != HEAD_DIM or \
+            q.shape[3] != HEAD_DIM:
+        raise ValueError(f"q must be [batch, T, Hq, {HEAD_DIM}] and kv_pages "
+                         f"[num_pages, 2, {NUM_KV_HEADS}, page_size, {HEAD_DIM}], got q "
+                         f"{tuple(q.shape)} and kv_pages {tuple(kv_pages.shape)}")
     if (kv_scales is None) != (kv_pages.dtype != torch.int8):
         raise ValueError("kv_scales is required for (and only for) an int8 page pool")
     if kv_scales is not None and (kv_scales.dtype != torch.bfloat16 or
                                   tuple(kv_scales.shape) != tuple(kv_pages.shape[:4])):
         raise ValueError(f"kv_scales must be bf16 {tuple(kv_pages.shape[:4])}")
+    ts = [q, kv_pages, block_table, seq_lens, out] + ([kv_scales] if kv_scales is not None else [])
+    _check_devices(*ts)
 
 
 def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.Tensor,
@@ -406,13 +422,12 @@ def gqa_kv_append(kv: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                   positions: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
                   stream=None) -> torch.Tensor:
     """Write k_new/v_new [batch, 8, 128] at slot positions[b] of every KV head; returns kv."""
-    _check_devices(kv, k_new, v_new, positions)
-    if positions.dtype != torch.int32:
-        raise ValueError("positions must be int32")
+    _check_per_request(positions, k_new.shape[0] if k_new.dim() > 0 else -1, "positions")
     if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
         raise ValueError("k_new and v_new must have the same shape and dtype")
     if k_new.dim() != 3 or kv.dim() != 5 or k_new.shape[0] != kv.shape[0]:
         raise ValueError("k_new/v_new must be [batch, 8, 128] and kv [batch, 2, 8, capacity, 128]")
+    _check_devices(kv, k_new, v_new, positions)
     desc = GqaDesc(batch=kv.shape[0], capacity=kv.shape[3], num_q_heads=NUM_Q_HEADS,
                    num_kv_heads=k_new.shape[1], head_dim=k_new.shape[2],
                    q_dtype=_dtype_code(k_new, "q"), kv_dtype=_dtype_code(kv, "kv"),
@@ -434,9 +449,9 @@ def gqa_kv_append_paged(kv_pages: torch.Tensor, block_table: torch.Tensor, k_new
     kv_pages [num_pages, 2, 8, page_size, 128] through block_table [batch, max_pages];
     returns kv_pages. num_q_heads is the query-head count of the decode that
     shares the descriptor (T x query heads per KV head must fit its 16 rows)."""
-    _check_devices(kv_pages, block_table, k_new, v_new, positions)
-    if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
-        raise ValueError("positions and block_table must be int32")
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    _check_per_request(positions, k_new.shape[0] if k_new.dim() > 0 else -1, "positions")
     if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
         raise ValueError("k_new and v_new must have the same shape and dtype")
     if k_new.dim() != 4 or kv_pages.dim() != 5 or block_table.dim() != 2 or \
@@ -445,6 +460,7 @@ def gqa_kv_append_paged(kv_pages: torch.Tensor, block_table: torch.Tensor, k_new
                          "[num_pages, 2, 8, page_size, 128] and block_table [batch, max_pages]")
     if kv_pages.shape[2] != k_new.shape[2] or kv_pages.shape[4] != k_new.shape[3]:
         raise ValueError("kv_pages and k_new disagree on KV heads or head_dim")
+    _check_devices(kv_pages, block_table, k_new, v_new, positions)
     desc = GqaPagedDesc(batch=k_new.shape[0], q_tokens=k_new.shape[1], num_q_heads=num_q_heads,
                         num_kv_heads=k_new.shape[2], head_dim=k_new.shape[3],
                         q_dtype=_dtype_code(k_new, "q"), kv_dtype=_dtype_code(kv_pages, "kv"),
@@ -464,9 +480,7 @@ def gqa_kv_append_int8(kv: torch.Tensor, kv_scales: torch.Tensor, k_new: torch.T
     """Quantise k_new/v_new [batch, 8, 128] row by row into an int8 cache kv
     [batch, 2, 8, capacity, 128] and its bf16 row scales kv_scales
     [batch, 2, 8, capacity] at slot positions[b]; returns kv."""
-    _check_devices(kv, kv_scales, k_new, v_new, positions)
-    if positions.dtype != torch.int32:
-        raise ValueError("positions must be int32")
+    _check_per_request(positions, k_new.shape[0] if k_new.dim() > 0 else -1, "positions")
     if kv.dtype != torch.int8 or kv_scales.dtype != torch.bfloat16:
         raise ValueError("kv must be int8 and kv_scales bfloat16")
     if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
@@ -477,6 +491,7 @@ def gqa_kv_append_int8(kv: torch.Tensor, kv_scales: torch.Tensor, k_new: torch.T
                          "and kv_scales [batch, 2, 8, capacity]")
     if kv.shape[2] != k_new.shape[1] or kv.shape[4] != k_new.shape[2]:
         raise ValueError("kv and k_new disagree on KV heads or head_dim")
+    _check_devices(kv, kv_scales, k_new, v_new, positions)
     desc = GqaDesc(batch=kv.shape[0], capacity=kv.shape[3], num_q_heads=num_q_heads,
                    num_kv_heads=k_new.shape[1], head_dim=k_new.shape[2],
                    q_dtype=_dtype_code(k_new, "q"), kv_dtype=GQA_INT8_ROWSCALE,
@@ -496,9 +511,9 @@ def gqa_kv_append_paged_int8(kv_pages: torch.Tensor, kv_scales: torch.Tensor,
     kv_pages [num_pages, 2, 8, page_size, 128] and its bf16 row scales kv_scales
     [num_pages, 2, 8, page_size] at slots positions[b] + t through block_table;
     returns kv_pages."""
-    _check_devices(kv_pages, kv_scales, block_table, k_new, v_new, positions)
-    if positions.dtype != torch.int32 or block_table.dtype != torch.int32:
-        raise ValueError("positions and block_table must be int32")
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    _check_per_request(positions, k_new.shape[0] if k_new.dim() > 0 else -1, "positions")
     if kv_pages.dtype != torch.int8 or kv_scales.dtype != torch.bfloat16:
         raise ValueError("kv_pages must be int8 and kv_scales bfloat16")
     if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
@@ -511,6 +526,7 @@ def gqa_kv_append_paged_int8(kv_pages: torch.Tensor, kv_scales: torch.Tensor,
                          "and block_table [batch, max_pages]")
     if kv_pages.shape[2] != k_new.shape[2] or kv_pages.shape[4] != k_new.shape[3]:
         raise ValueError("kv_pages and k_new disagree on KV heads or head_dim")
+    _check_devices(kv_pages, kv_scales, block_table, k_new, v_new, positions)
     desc = GqaPagedDesc(batch=k_new.shape[0], q_tokens=k_new.shape[1], num_q_heads=num_q_heads,
                         num_kv_heads=k_new.shape[2], head_dim=k_new.shape[3],
                         q_dtype=_dtype_code(k_new, "q"), kv_dtype=GQA_INT8_ROWSCALE,

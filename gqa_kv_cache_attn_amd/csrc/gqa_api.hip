@@ -520,8 +520,12 @@ gqa_status_t decode_checked(const gqa_desc_t* desc, const void* q, const void* k
   }
 
   void* ws = nullptr;
+  // Held until the kernels are enqueued: another host thread that grows the
+  // same (device, stream) entry frees the old buffer only after this call's
+  // launches are in the stream ahead of its synchronisation.
+  std::unique_lock<std::mutex> lk(g_cache_mu, std::defer_lock);
   if (p.workspace_bytes > 0) {
-    std::lock_guard<std::mutex> lk(g_cache_mu);
+    lk.lock();
     CacheEntry& ce = g_cache[{dev, reinterpret_cast<uintptr_t>(stream)}];
     if (ce.bytes < p.workspace_bytes) {
       hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;

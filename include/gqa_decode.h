@@ -155,8 +155,11 @@ typedef struct gqa_prepared gqa_prepared_t;
  * live in a library-owned workspace cached per (device, stream) that only
  * grows; growing it allocates, so a call made while `stream` is capturing
  * that would need to grow it returns GQA_ERR_CAPTURE instead. Calls on the
- * same stream are ordered and may share the cache; the prepared pair below
- * is the capture-safe interface. */
+ * same stream are ordered and may share the cache. Calls from several host
+ * threads are safe: the cache lookup, any growth (which synchronises the
+ * stream before freeing the old buffer) and the enqueue happen under one
+ * lock, so no call launches with a buffer another call has freed. The
+ * prepared pair below is the capture-safe interface. */
 GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
                                 const int32_t* seq_lens, float q_scale, void* out,
                                 hipStream_t stream);

@@ -430,3 +430,87 @@ def test_int8_append_rejects_bad_arguments_without_touching_a_device():
     assert pcall(pdesc(batch=2, T=2)) == INVALID and "INT8" in b.last_error()
     assert b._append_paged(ctypes.byref(pd), K, V, P, TABLE, POOL, None) == INVALID
     assert "gqa_kv_append_paged_int8" in b.last_error()
+
+
+# ---------------------------------------------------------------- binding shape checks
+# The binding checks what the C side cannot see (it gets pointers only):
+# per-request tensors must have one entry per request, and a page pool's
+# rows must be as wide as q's. These checks run before the device check,
+# so CPU tensors reach them; correct shapes fail only at the device check.
+import torch  # noqa: E402
+
+
+def _contig(batch=2, C=64, lens=None, hq=32):
+    q = torch.zeros(batch, hq, 128, dtype=torch.float16)
+    kv = torch.zeros(batch, 2, 8, C, 128, dtype=torch.float16)
+    lens = torch.ones(batch if lens is None else lens, dtype=torch.int32)
+    return q, kv, lens, torch.empty_like(q)
+
+
+def test_binding_rejects_seq_lens_that_do_not_match_the_batch():
+    for n in (1, 3):
+        q, kv, lens, out = _contig(lens=n)
+        with pytest.raises(ValueError, match=r"seq_lens must be \[batch\]"):
+            b.gqa_decode(q, kv, lens, 1.0, out)
+        with pytest.raises(ValueError, match=r"seq_lens must be \[batch\]"):
+            b.prepare_gqa_decode(q, kv, lens, out)
+    q, kv, lens, out = _contig()
+    with pytest.raises(ValueError, match=r"seq_lens must be \[batch\]"):
+        b.gqa_decode(q, kv, lens.reshape(2, 1), 1.0, out)
+    with pytest.raises(ValueError, match="int32"):
+        b.gqa_decode(q, kv, lens.long(), 1.0, out)
+    # right shapes: only the device check is left
+    with pytest.raises(ValueError, match="same GPU"):
+        b.gqa_decode(q, kv, lens, 1.0, out)
+    q8 = torch.zeros(2, 16, 128, dtype=torch.bfloat16)
+    kv8 = torch.zeros(2, 2, 8, 64, 128, dtype=torch.int8)
+    sc8 = torch.zeros(2, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"seq_lens must be \[batch\]"):
+        b.gqa_decode_int8(q8, kv8, sc8, torch.ones(1, dtype=torch.int32), 1.0, torch.empty_like(q8))
+    with pytest.raises(ValueError, match=r"seq_lens must be \[batch\]"):
+        b.prepare_gqa_decode_int8(q8, kv8, sc8, torch.ones(3, dtype=torch.int32), torch.empty_like(q8))
+
+
+def _paged(batch=2, T=1, P=16, num_pages=8, max_pages=4, width=128, kv_heads=8):
+    q = torch.zeros(batch, T, 32, 128, dtype=torch.bfloat16)
+    pool = torch.zeros(num_pages, 2, kv_heads, P, width, dtype=torch.bfloat16)
+    table = torch.zeros(batch, max_pages, dtype=torch.int32)
+    return q, pool, table, torch.ones(batch, dtype=torch.int32), torch.empty_like(q)
+
+
+def test_binding_rejects_a_pool_whose_rows_are_not_as_wide_as_q():
+    q, pool, table, lens, out = _paged(width=64)
+    with pytest.raises(ValueError, match="kv_pages"):
+        b.gqa_decode_paged(q, pool, table, lens, 1.0, out)
+    with pytest.raises(ValueError, match="kv_pages"):
+        b.prepare_gqa_decode_paged(q, pool, table, lens, out)
+    q, pool, table, lens, out = _paged(kv_heads=4)
+    with pytest.raises(ValueError, match="kv_pages"):
+        b.gqa_decode_paged(q, pool, table, lens, 1.0, out)
+    q, pool, table, lens, out = _paged()
+    with pytest.raises(ValueError, match=r"seq_lens must be \[batch\]"):
+        b.gqa_decode_paged(q, pool, table, lens[:1], 1.0, out)
+    with pytest.raises(ValueError, match="same GPU"):
+        b.gqa_decode_paged(q, pool, table, lens, 1.0, out)
+
+
+def test_binding_rejects_positions_that_do_not_match_the_batch():
+    kv = torch.zeros(2, 2, 8, 64, 128, dtype=torch.float16)
+    k_new = torch.zeros(2, 8, 128, dtype=torch.float16)
+    short = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match=r"positions must be \[batch\]"):
+        b.gqa_kv_append(kv, k_new, k_new.clone(), short)
+    kv8 = torch.zeros(2, 2, 8, 64, 128, dtype=torch.int8)
+    sc8 = torch.zeros(2, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"positions must be \[batch\]"):
+        b.gqa_kv_append_int8(kv8, sc8, k_new, k_new.clone(), short)
+    _, pool, table, _, _ = _paged()
+    pk = torch.zeros(2, 1, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"positions must be \[batch\]"):
+        b.gqa_kv_append_paged(pool, table, pk, pk.clone(), torch.zeros(3, dtype=torch.int32))
+    pool8 = torch.zeros(8, 2, 8, 16, 128, dtype=torch.int8)
+    psc8 = torch.zeros(8, 2, 8, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"positions must be \[batch\]"):
+        b.gqa_kv_append_paged_int8(pool8, psc8, table, pk, pk.clone(), short)
+    with pytest.raises(ValueError, match="same GPU"):
+        b.gqa_kv_append(kv, k_new, k_new.clone(), torch.zeros(2, dtype=torch.int32))
