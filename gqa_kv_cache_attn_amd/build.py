@@ -21,9 +21,6 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libgqa_decode.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["gqa_kernels.hip", "gqa_paged.hip", "gqa_api.hip"]
-# HBM read-ceiling / copy-calibration kernels (measurement only, separate library).
-PROBE_SOURCES = ["hbm_probe.hip"]
-PROBE_LIB_PATH = os.path.join(PKG_DIR, "libgqa_hbm_probe.so")
 ARCH = "gfx950"
 
 
@@ -62,9 +59,8 @@ def _compile(sources, out_path, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the libraries (always; no staleness shortcut); return the decode library path."""
+    """Compile the library (always; no staleness shortcut); return its path."""
     _compile(SOURCES, LIB_PATH, verbose)
-    _compile(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

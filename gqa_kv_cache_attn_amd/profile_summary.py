@@ -6,12 +6,19 @@
         --fetch F_counter_collection.csv --write W_counter_collection.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N \\
         --algorithmic-bytes A --command "C" --out profiles/gqa_attention_kernel_W_traffic.txt
+    python -m gqa_kv_cache_attn_amd.profile_summary phases --trace K_kernel_trace.csv \\
+        --names direct,graph1,... --title T --command "C" --out profiles/X.txt
 
-`traffic` scales each counter by what it reads for the probe's plain copy of
-known size (copy_stream_kernel: N bytes read, N bytes written per launch), so
-counter units become bytes; it records the kernel-source digest the counters
-were taken with, and bench.py only reports the figure while that digest still
-matches the source.
+`traffic` scales each counter by what it reads for a plain elementwise pass
+of known size (torch's bitwise_not over a 1 GiB uint8 tensor into another:
+N bytes read, N bytes written per launch), so counter units become bytes; it
+records the kernel-source digest the counters were taken with, and bench.py
+only reports the figure while that digest still matches the source.
+
+`phases` splits a kernel trace of a bench.py run at the marker kernels bench
+places between its measurement passes (a fill of a 256-element tensor) and
+reports, per pass, the decode kernels' average durations, the gaps between
+consecutive kernels and the time per step.
 """
 
 from __future__ import annotations
@@ -24,7 +31,7 @@ import statistics
 
 from .build import CSRC
 
-COPY_MATCH = "copy_stream_kernel"
+COPY_MATCH = "bitwise_not"
 
 
 # Sources each kernel family is compiled from (the digest covers all of them).
@@ -98,8 +105,8 @@ def cmd_traffic(a):
     match = f"::{a.kernel}<"            # exact kernel name within the demangled signature
     fetch, nf = _counter_avg(a.fetch, match)
     write, nw = _counter_avg(a.write, match)
-    cfetch, _ = _counter_avg(a.copy_fetch, COPY_MATCH)
-    cwrite, _ = _counter_avg(a.copy_write, COPY_MATCH)
+    cfetch, _ = _counter_avg(a.copy_fetch, a.copy_match)
+    cwrite, _ = _counter_avg(a.copy_write, a.copy_match)
     fscale = a.copy_bytes / cfetch          # bytes per FETCH_SIZE unit
     wscale = a.copy_bytes / cwrite          # bytes per WRITE_SIZE unit
     fb, wb = fetch * fscale, write * wscale
@@ -107,7 +114,7 @@ def cmd_traffic(a):
         f"# HBM traffic per launch of the attention kernel ({a.kernel}), workload {a.workload}",
         "#",
         f"# command (FETCH_SIZE pass; WRITE_SIZE pass identical but for the counter): {a.command}",
-        f"# calibration: {COPY_MATCH} copies {a.copy_bytes} bytes per launch; it reads "
+        f"# calibration: {a.copy_match} reads and writes {a.copy_bytes} bytes per launch; it reads "
         f"FETCH_SIZE={cfetch:.1f} and WRITE_SIZE={cwrite:.1f}",
         f"# -> {fscale:.4f} bytes per FETCH_SIZE unit, {wscale:.4f} bytes per WRITE_SIZE unit",
         f"# dispatches averaged: fetch {nf}, write {nw}",
@@ -122,6 +129,47 @@ def cmd_traffic(a):
         f"fetch_over_algorithmic = {fb / a.algorithmic_bytes:.4f}",
         f"kernel_source_sha256_16 = {kernel_source_digest(a.kernel)}",
     ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cmd_phases(a):
+    rows = sorted(csv.DictReader(open(a.trace)), key=lambda r: int(r["Start_Timestamp"]))
+    # Passes: runs of decode kernels between marker kernels (bench places a
+    # marker before each pass). Other kernels (input generation) are dropped.
+    passes, cur, seen_marker = [], [], False
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "gqa" in name and "append" not in name:
+            if seen_marker:
+                cur.append(r)
+        elif "Fill" in name or "fill" in name:
+            if cur:
+                passes.append(cur)
+            cur, seen_marker = [], True
+    if cur:
+        passes.append(cur)
+    names = a.names.split(",")
+    passes = passes[-len(names):]
+    us = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    lines = [f"# {a.title}", "", f"command: {a.command}", "",
+             "| pass | steps | attention avg us | combine avg us | gap attention->combine us | "
+             "gap combine->attention us | us per step (first start to last end) |",
+             "|---|---|---|---|---|---|---|"]
+    for name, p in zip(names, passes):
+        att = [r for r in p if "combine" not in r["Kernel_Name"]]
+        com = [r for r in p if "combine" in r["Kernel_Name"]]
+        g_ac, g_ca = [], []
+        for x, y in zip(p, p[1:]):
+            gap = (int(y["Start_Timestamp"]) - int(x["End_Timestamp"])) / 1e3
+            (g_ac if "combine" in y["Kernel_Name"] else g_ca).append(gap)
+        span = (int(p[-1]["End_Timestamp"]) - int(p[0]["Start_Timestamp"])) / 1e3 / max(1, len(att))
+        f = lambda xs: f"{statistics.fmean(xs):.2f}" if xs else "-"
+        lines.append(f"| {name} | {len(att)} | {f([us(r) for r in att])} | {f([us(r) for r in com])} "
+                     f"| {f(g_ac)} | {f(g_ca)} | {span:.2f} |")
+    lines.append("")
+    lines.append(f"kernel_source_sha256_16 = {kernel_source_digest(a.kernel)}")
     with open(a.out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -145,8 +193,14 @@ def main():
     t.add_argument("--algorithmic-bytes", type=int, required=True)
     t.add_argument("--num-splits", type=int, default=0)
     t.add_argument("--kernel", default="gqa_balanced_attention_kernel")
+    t.add_argument("--copy-match", default=COPY_MATCH,
+                   help="substring naming the calibration kernel in the copy runs")
+    ph = sub.add_parser("phases")
+    for k in ("trace", "names", "title", "command", "out"):
+        ph.add_argument("--" + k, required=True)
+    ph.add_argument("--kernel", default="gqa_balanced_attention_kernel")
     a = ap.parse_args()
-    cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "phases": cmd_phases}[a.cmd](a)
 
 
 if __name__ == "__main__":

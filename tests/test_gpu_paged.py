@@ -165,7 +165,7 @@ def test_tokens_that_see_no_slot_get_zeros(num_splits):
     out, _ = run_paged(inp, "prepared", num_splits=num_splits, out=out)
     got = decoded_out(out, "f16")
     full = paged_oracle_request(inp, 2)
-    assert np.all(np.abs(got[2] - full) - out_ulp(full, "f16") <= 2e-3)
+    assert np.all(np.abs(got[2] - full) - 0.5 * out_ulp(full, "f16") <= 2e-3)
     for b, L in enumerate([1, 3]):
         pages = inp["kv_pages"].index_select(0, inp["block_table"][b, :1].long())
         kv = pages[0].double().cpu().numpy()           # the request's first page, [2, 8, 16, 128]
@@ -178,7 +178,7 @@ def test_tokens_that_see_no_slot_get_zeros(num_splits):
             for g in range(8):
                 ref = gqa_decode_head(q[t, 4 * g:4 * g + 4], kv[0, g, :visible], kv[1, g, :visible],
                                       inp["q_scale"])
-                err = np.abs(got[b, t, 4 * g:4 * g + 4] - ref) - out_ulp(ref, "f16")
+                err = np.abs(got[b, t, 4 * g:4 * g + 4] - ref) - 0.5 * out_ulp(ref, "f16")
                 assert err.max() <= 2e-3, (b, t, g)
 
 
@@ -343,7 +343,7 @@ def test_paged_maximum_capacity_every_slot_valid(kd, hq, T, P):
         for g, ref in refs.items():
             err = np.abs(got[:, G * g:G * g + G] - ref)
             assert np.all(np.isfinite(err)), (g, ns)
-            assert (err - out_ulp(ref, "bf16")).max() <= 2e-3, (g, ns, err.max())
+            assert (err - 0.5 * out_ulp(ref, "bf16")).max() <= 2e-3, (g, ns, err.max())
         print(f"[parity] paged max capacity {kd} P={P} T={T} S={ns}: "
               f"max_abs_ref={max(np.abs(r).max() for r in refs.values()):.3e}", flush=True)
         prep.destroy()
