@@ -99,6 +99,8 @@ _prepare_int8 = _sig("prepare_gqa_decode_int8", ctypes.c_int,
 _validate_int8 = _sig("gqa_validate_args_int8", ctypes.c_int,
                       [_DescP, _vp, _vp, _vp, _vp, _f32, _vp, _i32])
 _plan = _sig("gqa_plan_decode", ctypes.c_int, [_DescP, _i32, _PlanP])
+_decode_no_alloc = _sig("gqa_decode_no_alloc", ctypes.c_int,
+                        [_DescP, _vp, _vp, _vp, _vp, _f32, _vp, _vp])
 _decode_paged = _sig("gqa_decode_paged", ctypes.c_int,
                      [_PDescP, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp])
 _prepare_paged = _sig("prepare_gqa_decode_paged", ctypes.c_int,
@@ -238,6 +240,31 @@ def gqa_decode_int8(q: torch.Tensor, kv: torch.Tensor, kv_scales: torch.Tensor,
     desc = make_desc(q, kv, k_scale, v_scale)
     with torch.cuda.device(q.device):
         st = _gqa_decode_int8(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(kv_scales),
+                              _ptr(seq_lens), q_scale, _ptr(out), _stream_handle(stream, q.device))
+    _check(st)
+    return out
+
+
+# Bytes of the static device scratch gqa_decode_no_alloc uses as its workspace.
+NO_ALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def gqa_decode_no_alloc(q: torch.Tensor, kv: torch.Tensor, seq_lens: torch.Tensor,
+                        q_scale: float, out: torch.Tensor, k_scale: float = 1.0,
+                        v_scale: float = 1.0, kv_scales: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """gqa_decode (or, with kv_scales, gqa_decode_int8) with the library's static
+    scratch as the split workspace: nothing is allocated, here or in the library,
+    so ``out`` is required. Calls that overlap on one GPU race on the scratch."""
+    _check_per_request(seq_lens, q.shape[0] if q.dim() > 0 else -1, "seq_lens")
+    if out.dtype != q.dtype or out.shape != q.shape:
+        raise ValueError("out must match q's shape and dtype")
+    if kv_scales is not None:
+        _check_scales(kv, kv_scales)
+    desc = make_desc(q, kv, k_scale, v_scale)
+    _check_devices(*([q, kv, seq_lens, out] + ([kv_scales] if kv_scales is not None else [])))
+    with torch.cuda.device(q.device):
+        st = _decode_no_alloc(ctypes.byref(desc), _ptr(q), _ptr(kv), _ptr(kv_scales),
                               _ptr(seq_lens), q_scale, _ptr(out), _stream_handle(stream, q.device))
     _check(st)
     return out

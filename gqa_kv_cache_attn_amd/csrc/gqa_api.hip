@@ -613,6 +613,52 @@ gqa_status_t prepare_impl(const gqa_desc_t* desc, const void* q, const void* kv,
   return prepare_checked(desc, q, kv, scales, seq_lens, q_scale, out, num_splits, Paging(), handle);
 }
 
+// gqa_decode / gqa_decode_int8 with the static scratch as the split
+// workspace: the same plan, kernels and results, and no allocation.
+gqa_status_t decode_no_alloc_checked(const gqa_desc_t* desc, const void* q, const void* kv,
+                                     const void* scales, const int32_t* seq_lens, float q_scale,
+                                     void* out, hipStream_t stream) {
+  if (desc->flags != 0)
+    return fail(GQA_ERR_INVALID_ARG, "gqa_decode_no_alloc takes no flags (got 0x%x)",
+                (unsigned)desc->flags);
+  auto too_big = [](const gqa_plan_t& p) {
+    return fail(GQA_ERR_INVALID_ARG,
+                "this plan needs %llu workspace bytes; gqa_decode_no_alloc's static scratch "
+                "holds %llu (use gqa_decode or the prepared pair)",
+                (unsigned long long)p.workspace_bytes,
+                (unsigned long long)GQA_NO_ALLOC_SCRATCH_BYTES);
+  };
+  gqa_plan_t p;
+  gqa_status_t st = make_plan(desc, 0, &p);
+  if (st != GQA_OK) return st;
+  // The host-only plan already decides the chunked routes' workspace (and
+  // bounds the balanced one by a nominal grid), so an oversized request is
+  // refused before any device is touched.
+  if (p.route != 2 && p.workspace_bytes > GQA_NO_ALLOC_SCRATCH_BYTES) return too_big(p);
+  if (desc->batch == 0) return ok();
+  int dev = -1;
+  st = check_device(&dev);
+  if (st != GQA_OK) return st;
+  if (p.route == 2) {
+    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc, false), Paging(), device_cus(dev));
+    if (st != GQA_OK) return st;
+  }
+  void* ws = nullptr;
+  if (p.workspace_bytes > 0) {
+    if (p.workspace_bytes > GQA_NO_ALLOC_SCRATCH_BYTES) return too_big(p);
+    const hipError_t e = gqa::no_alloc_scratch(dev, &ws);
+    if (e != hipSuccess)
+      return fail(GQA_ERR_HIP, "looking up the no-alloc scratch on device %d failed: %s", dev,
+                  hipGetErrorString(e));
+  }
+  // Nothing in the workspace needs to start at zero here: without the fused
+  // merge, every partial row and bookkeeping word a launch reads was written
+  // by that launch.
+  return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws, Paging(),
+                           device_cus(dev)),
+                 desc, false, stream);
+}
+
 gqa_status_t decode_impl(const gqa_desc_t* desc, const void* q, const void* kv,
                          const void* scales, bool with_scales, const int32_t* seq_lens,
                          float q_scale, void* out, hipStream_t stream) {
@@ -937,6 +983,17 @@ GQA_API gqa_status_t gqa_decode_int8(const gqa_desc_t* desc, const void* q, cons
                                      const void* kv_scales, const int32_t* seq_lens,
                                      float q_scale, void* out, hipStream_t stream) {
   return decode_impl(desc, q, kv, kv_scales, true, seq_lens, q_scale, out, stream);
+}
+
+GQA_API gqa_status_t gqa_decode_no_alloc(const gqa_desc_t* desc, const void* q, const void* kv,
+                                         const void* kv_scales, const int32_t* seq_lens,
+                                         float q_scale, void* out, hipStream_t stream) {
+  const bool int8 = desc != nullptr && desc->kv_dtype == GQA_INT8_ROWSCALE;
+  gqa_status_t st = check_args(desc, q, kv, kv_scales, int8, seq_lens, q_scale, out);
+  if (st != GQA_OK) return st;
+  if (!int8 && kv_scales != nullptr)
+    return fail(GQA_ERR_INVALID_ARG, "kv_scales must be NULL unless the cache is INT8_ROWSCALE");
+  return decode_no_alloc_checked(desc, q, kv, kv_scales, seq_lens, q_scale, out, stream);
 }
 
 GQA_API gqa_status_t gqa_validate_args_paged(const gqa_paged_desc_t* desc, const void* q,

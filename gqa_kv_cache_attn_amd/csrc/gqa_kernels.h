@@ -77,6 +77,11 @@ struct AppendArgs {
 
 hipError_t enqueue_kv_append(const AppendArgs& args, int src_dtype, int kv_dtype, hipStream_t stream);
 
+// Device address, on device `dev` (which must be current), of the static
+// scratch array gqa_decode_no_alloc uses as its split workspace
+// (GQA_NO_ALLOC_SCRATCH_BYTES, 256-byte aligned). Looked up once per device.
+hipError_t no_alloc_scratch(int dev, void** ptr);
+
 // Workgroups of the balanced split that the current device keeps resident at
 // once (CUs x resident workgroups per CU); 0 if the query fails.
 int balanced_grid_size(int q_dtype, int kv_dtype, int num_q_heads);

@@ -31,10 +31,21 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <type_traits>
 
+#include "../../include/gqa_decode.h"
 #include "gqa_device.h"
 #include "gqa_kernels.h"
+
+// Split workspace of gqa_decode_no_alloc: a device array of fixed size in the
+// library's own code object, so that entry point never allocates. Each GPU
+// the library runs on holds its own copy until the process ends. In host
+// code `scratch` names a host-side stand-in, not device memory: only the
+// per-device address from hipGetSymbolAddress (gqa::no_alloc_scratch) is
+// ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[GQA_NO_ALLOC_SCRATCH_BYTES];
 
 namespace gqa {
 namespace {
@@ -585,6 +596,25 @@ int balanced_grid_typed() {
 }
 
 }  // namespace
+
+hipError_t no_alloc_scratch(int dev, void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return e;
+    }
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
+}
 
 int balanced_grid_size(int q_dtype, int kv_dtype, int num_q_heads) {
   return dispatch(q_dtype, kv_dtype, num_q_heads, 0,

@@ -215,6 +215,26 @@ GQA_API gqa_status_t prepare_gqa_decode_int8(const gqa_desc_t* desc, const void*
                                              const int32_t* seq_lens, float q_scale, void* out,
                                              int32_t num_splits, gqa_prepared_t** handle);
 
+/* ---- Allocation-free decode -------------------------------------------------
+ * For callers that cannot allocate device memory at all: code under hipGraph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. As
+ * gqa_decode (kv_scales NULL) or gqa_decode_int8 (kv_dtype INT8_ROWSCALE,
+ * kv_scales given): the same validation, plan, kernels and results, but the
+ * split workspace is a static device array of GQA_NO_ALLOC_SCRATCH_BYTES
+ * inside the library (one per GPU, held until the process ends) instead of
+ * an allocated buffer, so the call never allocates or frees anything. A plan
+ * whose workspace exceeds that size (very large batches on the chunked
+ * route) is rejected with GQA_ERR_INVALID_ARG, as is any flag. The caller
+ * still passes every input and out. All calls on one GPU share the one
+ * array: calls that can overlap on the device (different streams, or several
+ * host threads) race on it and must be ordered by the caller; calls on one
+ * stream are ordered. The first call on a device looks up the array's device
+ * address (hipGetSymbolAddress) and keeps it. */
+#define GQA_NO_ALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+GQA_API gqa_status_t gqa_decode_no_alloc(const gqa_desc_t* desc, const void* q, const void* kv,
+                                         const void* kv_scales, const int32_t* seq_lens,
+                                         float q_scale, void* out, hipStream_t stream);
+
 /* ---- Paged cache, several query tokens per request -------------------------
  * The decode step over a page pool, for one or more query tokens per request
  * (the verify pass of speculative decoding). The pages name a paged-KV decode

@@ -12,6 +12,7 @@ hipError_t enqueue_decode_step(const StepArgs&, int, int, hipStream_t, hipEvent_
   return hipErrorNoDevice;
 }
 int paged_balanced_grid_size(int, int, int) { return 0; }
+hipError_t no_alloc_scratch(int, void**) { return hipErrorNoDevice; }
 hipError_t enqueue_paged_decode_step(const StepArgs&, int, int, hipStream_t, hipEvent_t) {
   return hipErrorNoDevice;
 }

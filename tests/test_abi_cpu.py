@@ -514,3 +514,42 @@ def test_binding_rejects_positions_that_do_not_match_the_batch():
         b.gqa_kv_append_paged_int8(pool8, psc8, table, pk, pk.clone(), short)
     with pytest.raises(ValueError, match="same GPU"):
         b.gqa_kv_append(kv, k_new, k_new.clone(), torch.zeros(2, dtype=torch.int32))
+
+
+# ---------------------------------------------------------------- allocation-free decode
+def _no_alloc(d, q=Q, kv=KV, sc=None, lens=LENS, qs=1.0, out=OUT):
+    return b._decode_no_alloc(ctypes.byref(d), q, kv, sc, lens, qs, out, None)
+
+
+def test_no_alloc_refuses_what_it_cannot_do_without_touching_a_device():
+    # A batch beyond the balanced split's limit takes the chunked split, whose
+    # partials ([batch, 32, splits, 128] fp32) far exceed the static scratch:
+    # refused with a message that names the sizes, before any device check.
+    far = 1 << 42   # addresses far enough apart for a 1.3 TB cache
+    assert _no_alloc(desc(batch=5000, capacity=65536, q=b.GQA_F16, kv=b.GQA_F16),
+                     q=far, kv=2 * far, lens=3 * far, out=4 * far) == INVALID
+    msg = b.last_error()
+    assert "static scratch" in msg and str(4 << 20) in msg
+    d = desc()
+    d.flags = b.GQA_FLAG_FUSED_COMBINE
+    assert _no_alloc(d) == INVALID and "flags" in b.last_error()
+    assert _no_alloc(desc(), sc=SC) == INVALID and "kv_scales" in b.last_error()
+    assert _no_alloc(desc(kv=b.GQA_INT8_ROWSCALE, hq=16)) == INVALID       # INT8 needs its scales
+    assert _no_alloc(desc(), out=Q + 64) == ALIAS
+    assert _no_alloc(desc(), qs=float("nan")) == INVALID
+    assert _no_alloc(desc(batch=0), q=None, kv=None, lens=None, out=None) == OK
+    # Valid arguments get as far as the device check (no GPU here).
+    assert _no_alloc(desc(batch=8, capacity=65536)) not in (OK, INVALID, ALIAS)
+    assert _no_alloc(desc(kv=b.GQA_INT8_ROWSCALE, hq=16), sc=SC) not in (OK, INVALID, ALIAS)
+    assert b.NO_ALLOC_SCRATCH_BYTES == 4 << 20
+    assert "#define GQA_NO_ALLOC_SCRATCH_BYTES ((size_t)4 << 20)" in open(HEADER).read()
+
+
+def test_no_alloc_binding_needs_an_output_and_checks_shapes():
+    q, kv, lens, out = _contig()
+    with pytest.raises(TypeError):
+        b.gqa_decode_no_alloc(q, kv, lens, 1.0)                  # no out: it would allocate
+    with pytest.raises(ValueError, match=r"seq_lens must be \[batch\]"):
+        b.gqa_decode_no_alloc(q, kv, lens[:1], 1.0, out)
+    with pytest.raises(ValueError, match="same GPU"):
+        b.gqa_decode_no_alloc(q, kv, lens, 1.0, out)
