@@ -3,16 +3,20 @@
 
 A step is one prepared decode launch (attention kernel + log-sum-exp combine)
 over one batch of synthetic, seeded inputs already resident in HBM. The
-default workload is the long-context bf16 cache: 8 requests, capacity 65536,
-lengths uniform in [32768, 65536], 32 query / 8 KV heads, head_dim 128,
-q_scale 0.5.
+default (headline) workload is the largest one-GPU configuration: 16
+requests, capacity 131072, lengths uniform in [65536, 131072], 32 query / 8
+KV heads, head_dim 128, q bf16, an fp8_e4m3 cache with k_scale = v_scale =
+1/64, bf16 output.
 
 Printed: one JSON line with the whole-step KV-read throughput (GB/s of
 algorithmic bytes: the valid K/V prefixes plus q, out and the lengths), the
 attention kernel's roofline position (bytes per launch over its average
 duration from HIP events recorded on the launch stream around every timed
-launch, against 8 TB/s), cold-cache microseconds per call, and the CPU
-oracle timed on a bounded sample of the same workload.
+launch, against 8 TB/s), cold-cache microseconds per call, the CPU oracle
+timed on a bounded sample of the same workload, and under "configs" every
+one of the five decode configurations (the headline's figures included),
+each timed in this run as direct launches, as replays of a captured one-step
+graph and as replays of a captured sixteen-step graph.
 
     python bench.py [--steps 50] [--warmup W] [--workload NAME] [--num-splits N]
 """
@@ -32,7 +36,12 @@ if ROOT not in sys.path:
 
 METRIC = "GQA decode: achieved KV-read HBM GB/s (% of peak) and µs/call at 1 GPU"
 PEAK_HBM_GBPS = 8000.0
-DEFAULT_WORKLOAD = "gqa_decode_b8_c65536_bf16_long"
+DEFAULT_WORKLOAD = "gqa_decode_b16_c131072_fp8kv_long"
+# The five decode configurations, timed in every default run.
+CONFIG_WORKLOADS = ["gqa_decode_b1_c64_f16", "gqa_decode_b1_c1024_f16",
+                    "gqa_decode_b32_c8192_f16_ragged", "gqa_decode_b8_c65536_bf16_long",
+                    "gqa_decode_b16_c131072_fp8kv_long"]
+GRAPH_STEPS = 16    # steps captured in the multi-step graph
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -54,6 +63,8 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU-oracle time budget for the cpu_baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the five decode configurations besides the headline")
     ap.add_argument("--page-size", type=int, default=0,
                     help="paged workloads: override the page size (slots per page)")
     ap.add_argument("--q-tokens", type=int, default=0,
@@ -216,6 +227,193 @@ def cpu_baseline(inp, w, budget_s):
     }
 
 
+def _workload(args, name):
+    """The named workload with the command line's shape and paging overrides."""
+    import dataclasses
+
+    from gqa_kv_cache_attn_amd.inputs import WORKLOADS_BY_NAME
+    w = WORKLOADS_BY_NAME[name]
+    if args.shape:
+        B, C, lo, hi = (int(x) for x in args.shape.split(","))
+        w = dataclasses.replace(w, batch=B, capacity=C, len_lo=lo, len_hi=hi,
+                                name=f"{w.name}[B={B},C={C},L={lo}..{hi}]")
+    if args.page_size or args.q_tokens or args.page_order != "random":
+        if not w.page_size:
+            print("--page-size / --q-tokens / --page-order apply to paged workloads only",
+                  file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, page_size=args.page_size or w.page_size,
+                                q_tokens=args.q_tokens or w.q_tokens,
+                                name=f"{w.name}[P={args.page_size or w.page_size},"
+                                     f"T={args.q_tokens or w.q_tokens}]"
+                                     + ("[pages in order]" if args.page_order == "ordered" else ""))
+    return w
+
+
+class Case:
+    """One workload's inputs in HBM and its prepared decode step."""
+
+    def __init__(self, w, dev, num_splits=0, fused_combine=False, page_order="random"):
+        import torch
+
+        from gqa_kv_cache_attn_amd import binding as b
+        from gqa_kv_cache_attn_amd.inputs import make_inputs, make_paged_inputs
+        self.w, self.dev, self.b = w, dev, b
+        self.paged = w.page_size > 0
+        inp = make_paged_inputs(w, device=dev) if self.paged else make_inputs(w, device=dev)
+        if self.paged and page_order == "ordered":
+            B, max_pages = inp["block_table"].shape
+            inp["block_table"] = torch.arange(B * max_pages, device=dev,
+                                              dtype=torch.int32).reshape(B, max_pages)
+        self.inp = inp
+        self.lens = inp["seq_lens"].cpu().tolist()
+        self.nbytes = algorithmic_bytes(self.lens, w.kv_dtype, w.batch, w.num_q_heads,
+                                        w.q_tokens, w.page_size)
+        self.out = torch.empty_like(inp["q"])
+        if self.paged:
+            if fused_combine:
+                print("the paged entry points have no one-launch merge", file=sys.stderr)
+                sys.exit(2)
+            self.prep = b.prepare_gqa_decode_paged(
+                inp["q"], inp["kv_pages"], inp["block_table"], inp["seq_lens"], self.out,
+                inp["q_scale"], num_splits=num_splits, k_scale=inp["k_scale"],
+                v_scale=inp["v_scale"], kv_scales=inp["kv_scales"])
+        elif w.kv_dtype == "int8":
+            self.prep = b.prepare_gqa_decode_int8(
+                inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], self.out, inp["q_scale"],
+                num_splits=num_splits, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                fused_combine=fused_combine)
+        else:
+            self.prep = b.prepare_gqa_decode(
+                inp["q"], inp["kv"], inp["seq_lens"], self.out, inp["q_scale"],
+                num_splits=num_splits, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
+                fused_combine=fused_combine)
+        self.plan = self.prep.plan
+
+    def step(self):
+        self.b.launch_gqa_decode_prepared(self.prep)
+
+    def warm(self, seconds, min_steps=0):
+        """Untimed steps for at least `seconds` and `min_steps`; returns the count."""
+        import torch
+        n, t0 = 0, time.perf_counter()
+        while n < min_steps or time.perf_counter() - t0 < seconds:
+            for _ in range(50):
+                self.step()
+            n += 50
+            torch.cuda.synchronize()
+        return n
+
+    def destroy(self):
+        self.prep.destroy()
+
+
+def _event(stream):
+    import torch
+    e = torch.cuda.Event(enable_timing=True)
+    e.record(stream)            # creates the underlying HIP event
+    return e
+
+
+def _marker(dev, k):
+    """A tiny fill kernel between measurement passes, so a rocprofv3 kernel
+    trace of this run can be split into its passes (outside every timed region)."""
+    import torch
+    torch.full((256,), float(k + 1), device=dev)
+    torch.cuda.synchronize()
+
+
+def time_direct(case, K, stream):
+    """µs per step of K back-to-back prepared launches (events on the launch stream)."""
+    import torch
+    e0, e1 = _event(stream), _event(stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(K):
+        case.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / K
+
+
+def time_graph(case, K, stream, steps_per_graph):
+    """Capture `steps_per_graph` prepared launches in one torch CUDA graph and
+    replay it until at least K steps ran. Returns (µs per step on the GPU,
+    host µs per replay call, steps timed)."""
+    import torch
+    dev = case.dev
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        case.step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps_per_graph):
+            case.step()
+    # The first replays of a newly instantiated graph run slower; replay it
+    # for at least 0.2 s and 10 launches before the timed replays.
+    n, t0 = 0, time.perf_counter()
+    while n < 10 or time.perf_counter() - t0 < 0.2:
+        graph.replay()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    launches = -(-K // steps_per_graph)
+    e0, e1 = _event(stream), _event(stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(launches):
+        graph.replay()
+    h1 = time.perf_counter()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    steps = launches * steps_per_graph
+    del graph
+    return e0.elapsed_time(e1) * 1e3 / steps, (h1 - h0) * 1e6 / launches, steps
+
+
+def config_entry(case, direct_us, graph1, graph16):
+    gbps = case.nbytes / (direct_us * 1e-6) / 1e9
+    return {
+        "plan": case.plan,
+        "algorithmic_bytes_per_step": case.nbytes,
+        "us_per_call": round(direct_us, 2),
+        "pct_of_peak": round(100 * gbps / PEAK_HBM_GBPS, 2),
+        "us_per_call_graph_1step": round(graph1[0], 2),
+        "host_us_per_graph_1step_launch": round(graph1[1], 2),
+        "us_per_step_graph_16step": round(graph16[0], 2),
+        "pct_of_peak_graph_16step": round(100 * case.nbytes / (graph16[0] * 1e-6) / 1e9
+                                          / PEAK_HBM_GBPS, 2),
+    }
+
+
+def measure_config(name, args, dev, stream, phase):
+    """Direct, one-step-graph and sixteen-step-graph µs per step of one configuration."""
+    import torch
+    from gqa_kv_cache_attn_amd.inputs import WORKLOADS_BY_NAME
+    w = WORKLOADS_BY_NAME[name]      # as defined: the headline's overrides do not apply
+    print(f"[bench] config {w.name}", file=sys.stderr, flush=True)
+    case = Case(w, dev)
+    case.warm(0.3, 100)
+    K = max(args.steps, 48)
+    _marker(dev, phase)
+    direct = time_direct(case, K, stream)
+    _marker(dev, phase + 1)
+    g1 = time_graph(case, K, stream, 1)
+    _marker(dev, phase + 2)
+    g16 = time_graph(case, K, stream, GRAPH_STEPS)
+    entry = config_entry(case, direct, g1, g16)
+    entry["steps_timed"] = K
+    case.destroy()
+    del case
+    torch.cuda.empty_cache()
+    return entry
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -227,7 +425,6 @@ def main():
     import torch
 
     from gqa_kv_cache_attn_amd import binding as b
-    from gqa_kv_cache_attn_amd.inputs import WORKLOADS_BY_NAME, make_inputs, make_paged_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -235,82 +432,52 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     arch = torch.cuda.get_device_properties(dev).gcnArchName
-    w = WORKLOADS_BY_NAME[args.workload]
-    if args.shape:
-        import dataclasses
-        B, C, lo, hi = (int(x) for x in args.shape.split(","))
-        w = dataclasses.replace(w, batch=B, capacity=C, len_lo=lo, len_hi=hi,
-                                name=f"{w.name}[B={B},C={C},L={lo}..{hi}]")
-    if args.page_size or args.q_tokens or args.page_order != "random":
-        if not w.page_size:
-            print("--page-size / --q-tokens / --page-order apply to paged workloads only",
-                  file=sys.stderr)
-            sys.exit(2)
-        import dataclasses
-        w = dataclasses.replace(w, page_size=args.page_size or w.page_size,
-                                q_tokens=args.q_tokens or w.q_tokens,
-                                name=f"{w.name}[P={args.page_size or w.page_size},"
-                                     f"T={args.q_tokens or w.q_tokens}]"
-                                     + ("[pages in order]" if args.page_order == "ordered" else ""))
+    # Every pass runs on one non-default stream, as a serving loop's decode
+    # steps do; graphs are replayed on it too.
+    stream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(stream):
+        result = run(args, dev, arch, stream)
+    print(json.dumps(result), flush=True)
+
+
+def run(args, dev, arch, stream):
+    import torch
+
+    from gqa_kv_cache_attn_amd import binding as b
+    w = _workload(args, args.workload)
+
+    # The other decode configurations first (each with its own short warm-up),
+    # then the headline workload.
+    configs = {}
+    if not args.no_configs:
+        for i, name in enumerate(n for n in CONFIG_WORKLOADS if n != args.workload):
+            configs[name] = measure_config(name, args, dev, stream, 10 * (i + 1))
+
     print(f"[bench] device {arch}; workload {w.name}; generating inputs", file=sys.stderr, flush=True)
-    paged = w.page_size > 0
-    inp = make_paged_inputs(w, device=dev) if paged else make_inputs(w, device=dev)
-    if paged and args.page_order == "ordered":
-        B, max_pages = inp["block_table"].shape
-        inp["block_table"] = torch.arange(B * max_pages, device=dev,
-                                          dtype=torch.int32).reshape(B, max_pages)
-    lens = inp["seq_lens"].cpu().tolist()
-    nbytes = algorithmic_bytes(lens, w.kv_dtype, w.batch, w.num_q_heads, w.q_tokens, w.page_size)
-    out = torch.empty_like(inp["q"])
-    if paged:
-        if args.fused_combine:
-            print("the paged entry points have no one-launch merge", file=sys.stderr)
-            sys.exit(2)
-        prep = b.prepare_gqa_decode_paged(inp["q"], inp["kv_pages"], inp["block_table"],
-                                          inp["seq_lens"], out, inp["q_scale"],
-                                          num_splits=args.num_splits, k_scale=inp["k_scale"],
-                                          v_scale=inp["v_scale"], kv_scales=inp["kv_scales"])
-    elif w.kv_dtype == "int8":
-        prep = b.prepare_gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], out,
-                                         inp["q_scale"], num_splits=args.num_splits,
-                                         k_scale=inp["k_scale"], v_scale=inp["v_scale"],
-                                         fused_combine=args.fused_combine)
-    else:
-        prep = b.prepare_gqa_decode(inp["q"], inp["kv"], inp["seq_lens"], out, inp["q_scale"],
-                                    num_splits=args.num_splits, k_scale=inp["k_scale"],
-                                    v_scale=inp["v_scale"], fused_combine=args.fused_combine)
-    plan = prep.plan
+    case = Case(w, dev, args.num_splits, args.fused_combine, args.page_order)
+    paged, inp, out, nbytes, lens = case.paged, case.inp, case.out, case.nbytes, case.lens
+    plan = dict(case.plan)
     plan["combine"] = "fused (last workgroup)" if args.fused_combine else "separate kernel"
-    stream = torch.cuda.current_stream(dev)
 
     K = args.steps
     if args.warmup is not None:
         W = args.warmup
         for _ in range(W):
-            b.launch_gqa_decode_prepared(prep)
+            case.step()
     else:
-        W, w0 = 0, time.perf_counter()
-        while W < 200 or time.perf_counter() - w0 < 2.0:
-            for _ in range(50):
-                b.launch_gqa_decode_prepared(prep)
-            W += 50
-            torch.cuda.synchronize()
+        W = case.warm(2.0, 200)
     torch.cuda.synchronize()
-
-    def new_event():
-        e = torch.cuda.Event(enable_timing=True)
-        e.record(stream)            # creates the underlying HIP event
-        return e
 
     # Timed region: exactly K steps, synchronised on both sides, no other
     # work on the stream. `value` and ms_per_step come from here.
-    t_begin, t_end = new_event(), new_event()
+    _marker(dev, 100)
+    t_begin, t_end = _event(stream), _event(stream)
     torch.cuda.synchronize()
     print(f"[bench] plan {plan}; timing {K} steps", file=sys.stderr, flush=True)
     wall0 = time.perf_counter()
     t_begin.record(stream)
     for _ in range(K):
-        b.launch_gqa_decode_prepared(prep)
+        case.step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -320,10 +487,11 @@ def main():
     # stream right before the attention kernel, between it and the combine,
     # and after the combine. (Event packets add a few microseconds between
     # launches, which is why the step time above is taken without them.)
-    ev = [[new_event() for _ in range(3)] for _ in range(K)]
+    _marker(dev, 101)
+    ev = [[_event(stream) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize()
     for k in range(K):
-        b.launch_gqa_decode_prepared_timed(prep, ev[k][0], ev[k][1], ev[k][2])
+        b.launch_gqa_decode_prepared_timed(case.prep, ev[k][0], ev[k][1], ev[k][2])
     torch.cuda.synchronize()
     attn_ms = [e[0].elapsed_time(e[1]) for e in ev]
     comb_ms = [e[1].elapsed_time(e[2]) for e in ev]
@@ -331,28 +499,15 @@ def main():
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (attn_avg * 1e-3) / 1e9
 
-    # The same step replayed from a captured HIP graph (one launch per graph,
-    # K replays back to back), and through the convenience call.
-    graph = torch.cuda.CUDAGraph()
-    side = torch.cuda.Stream(dev)
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        b.launch_gqa_decode_prepared(prep)
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph):
-        b.launch_gqa_decode_prepared(prep)
-    graph.replay()
-    torch.cuda.synchronize()
-    g_begin, g_end = new_event(), new_event()
-    torch.cuda.synchronize()
-    g_begin.record(stream)
-    for _ in range(K):
-        graph.replay()
-    g_end.record(stream)
-    torch.cuda.synchronize()
-    graph_us = g_begin.elapsed_time(g_end) / K * 1e3
-    del graph
+    # The same step replayed from captured graphs: one step per graph, and
+    # sixteen steps per graph (a captured decode loop).
+    _marker(dev, 102)
+    g1 = time_graph(case, K, stream, 1)
+    _marker(dev, 103)
+    g16 = time_graph(case, K, stream, GRAPH_STEPS)
+    _marker(dev, 104)
+    if not args.no_configs or w.name in CONFIG_WORKLOADS:
+        configs[w.name] = {**config_entry(case, ms_per_step * 1e3, g1, g16), "steps_timed": K}
 
     def convenience():
         if paged:
@@ -367,7 +522,7 @@ def main():
                          k_scale=inp["k_scale"], v_scale=inp["v_scale"])
     for _ in range(3):
         convenience()
-    c_begin, c_end = new_event(), new_event()
+    c_begin, c_end = _event(stream), _event(stream)
     torch.cuda.synchronize()
     c_begin.record(stream)
     for _ in range(K):
@@ -380,6 +535,7 @@ def main():
     # per request, T for a paged verify pass) at slots L_b .. L_b + T - 1, past
     # the valid prefix, so the decode inputs are unchanged (slots past the
     # cache write nothing). An INT8 cache is quantised row by row on the way.
+    _marker(dev, 105)
     shape = (w.batch, w.q_tokens, 8, 128) if paged else (w.batch, 8, 128)
     k_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
     v_new = torch.randn(*shape, device=dev).to(inp["q"].dtype)
@@ -403,7 +559,7 @@ def main():
             b.gqa_kv_append(inp["kv"], k_new, v_new, slots, inp["k_scale"], inp["v_scale"])
     for _ in range(3):
         append()
-    a_begin, a_end = new_event(), new_event()
+    a_begin, a_end = _event(stream), _event(stream)
     torch.cuda.synchronize()
     a_begin.record(stream)
     for _ in range(K):
@@ -417,9 +573,9 @@ def main():
     cold = []
     for _ in range(args.cold_calls):
         flush.fill_(1)
-        e0, e1 = new_event(), new_event()
+        e0, e1 = _event(stream), _event(stream)
         e0.record(stream)
-        b.launch_gqa_decode_prepared(prep)
+        case.step()
         e1.record(stream)
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
@@ -453,7 +609,8 @@ def main():
                    "algorithmic_bytes_per_step": nbytes, "plan": plan},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "us_per_call": round(ms_per_step * 1e3, 2),
-        "us_per_call_graph_replay": round(graph_us, 2),
+        "us_per_call_graph_replay": round(g1[0], 2),
+        "us_per_step_graph_16step": round(g16[0], 2),
         "us_per_call_convenience": round(convenience_us, 2),
         "us_per_call_cold": {"p10": round(pct(cold, 10), 2), "p50": round(pct(cold, 50), 2),
                              "p90": round(pct(cold, 90), 2)} if cold else None,
@@ -470,6 +627,7 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
         },
+        "configs": configs,
         "wall_s_timed": round(wall, 4),
         "device": arch,
     }
@@ -477,8 +635,8 @@ def main():
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = (cpu_baseline_paged if paged else cpu_baseline)(inp, w,
                                                                                 args.cpu_seconds)
-    prep.destroy()
-    print(json.dumps(result), flush=True)
+    case.destroy()
+    return result
 
 
 if __name__ == "__main__":

@@ -66,7 +66,7 @@ class GqaPlan(ctypes.Structure):
     _fields_ = [
         ("route", ctypes.c_int32), ("num_splits", ctypes.c_int32),
         ("chunk_tokens", ctypes.c_int32), ("num_workgroups", ctypes.c_int32),
-        ("workspace_bytes", ctypes.c_uint64),
+        ("workspace_bytes", ctypes.c_uint64), ("fused_merge", ctypes.c_int32),
     ]
 
     def as_dict(self):

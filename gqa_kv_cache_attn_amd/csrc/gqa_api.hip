@@ -75,6 +75,10 @@ constexpr int kMaxBalancedGrid = 4096;
 // resident grid: their tiles carry half the bytes, and one workgroup per CU
 // ran 2-6% slower on single requests of 128k-256k slots.
 constexpr int64_t kSmallBalancedBytes = int64_t(256) << 20;
+// Automatic chunked plans that merge inside the attention kernel: at most
+// this many chunks per head and workgroups per launch.
+constexpr int64_t kOneLaunchMaxSplits = 16;
+constexpr int64_t kOneLaunchMaxWorkgroups = 384;
 constexpr int kNominalCUs = 256;
 // A dispatch counts its work-items in 32 bits: at most this many 256-thread
 // workgroups per launch (decode and append kernels alike).
@@ -234,9 +238,9 @@ WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p, const Pagi
   if (p.route == 2)   // aux: slab prefix [B+1] | head pieces [2, B*8]
     return workspace_layout(0, 2ull * (uint64_t)p.num_workgroups * (pg.on ? gqa::kPagedSlotRows : 4),
                             (uint64_t)d->batch + 1 + 2ull * (uint64_t)d->batch * GQA_NUM_KV_HEADS);
-  const bool fused = (d->flags & GQA_FLAG_FUSED_COMBINE) != 0;
   const uint64_t ctrl =
-      fused ? (((uint64_t)d->batch * GQA_NUM_KV_HEADS * sizeof(uint32_t) + 255) & ~255ull) : 0;
+      p.fused_merge ? (((uint64_t)d->batch * GQA_NUM_KV_HEADS * sizeof(uint32_t) + 255) & ~255ull)
+                    : 0;
   return workspace_layout(ctrl,
                           (uint64_t)d->batch * (uint64_t)pg.q_tokens * (uint64_t)d->num_q_heads *
                               (uint64_t)p.num_splits,
@@ -245,10 +249,14 @@ WorkspaceLayout plan_layout(const gqa_desc_t* d, const gqa_plan_t& p, const Pagi
 
 // grid_wgs: resident workgroups of the balanced kernel on the target device,
 // cus: its compute units (0, 0: the nominal kNominalBalancedGrid and
-// kNominalCUs, for host-only planning).
+// kNominalCUs, for host-only planning). one_launch_ok: an automatic chunked
+// plan may merge in the attention kernel (contiguous cache with an allocated
+// workspace; the paged kernels and the static no-alloc scratch have no
+// zeroed per-head counters).
 gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, int grid_wgs = 0,
-                       const Paging& pg = Paging(), int cus = 0) {
+                       const Paging& pg = Paging(), int cus = 0, bool one_launch_ok = true) {
   const int64_t C = d->capacity;
+  p->fused_merge = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
   if (num_splits < 0) return fail(GQA_ERR_INVALID_ARG, "num_splits must be >= 0 (got %d)", num_splits);
   const int64_t slabs_per_head = (C + 63) / 64;
   const int64_t slabs_at_capacity = (int64_t)d->batch * GQA_NUM_KV_HEADS * slabs_per_head;
@@ -272,9 +280,20 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, i
   }
   const int64_t granules = (C + GQA_CHUNK_GRANULE - 1) / GQA_CHUNK_GRANULE;
   int64_t chunk_granules;
+  bool small_auto = false;
   if (num_splits == 0) {
     if (C <= GQA_SHORT_CAPACITY_MAX) {
       chunk_granules = granules;
+    } else if (slabs_at_capacity < kNominalBalancedGrid) {
+      // Small problems (too few 64-slot slabs for the balanced grid):
+      // chunks of about an eighth of the capacity, in 64-slot steps, from 64
+      // to 256 slots. Measured on MI355X over 1-5 requests and capacities of
+      // 128-6000 slots: within 2-8% of the best chunk size at every shape,
+      // where fixed 64-slot chunks were up to 1.7x slower beyond 2k slots.
+      const int64_t per = (C + 7) / 8;
+      const int64_t chunk = std::min<int64_t>(256, std::max<int64_t>(64, (per + 63) / 64 * 64));
+      chunk_granules = chunk / GQA_CHUNK_GRANULE;
+      small_auto = true;
     } else {
       // Automatic, in whole workgroup steps (64 tokens): chunks of about
       // kChunkBytes of K+V each (long enough to amortise a workgroup's
@@ -311,6 +330,15 @@ gqa_status_t make_plan(const gqa_desc_t* d, int32_t num_splits, gqa_plan_t* p, i
   p->num_splits = (int32_t)S;
   p->chunk_tokens = (int32_t)chunk;
   p->num_workgroups = (int32_t)wgs;
+  // A small automatic split merges in the attention kernel (one launch): its
+  // last workgroup per head merges the head. Measured on MI355X, that beat
+  // the second launch while a head has at most 16 chunks and the grid at
+  // most 384 workgroups (single requests: 5-16% faster per step); beyond
+  // that the grid's workgroups each waiting on their counter cost more.
+  if (small_auto && one_launch_ok && !pg.on && S > 1 && S <= kOneLaunchMaxSplits &&
+      wgs <= kOneLaunchMaxWorkgroups)
+    p->fused_merge = 1;
+  if (S <= 1) p->fused_merge = 0;
   p->workspace_bytes = S > 1 ? plan_layout(d, *p, pg).total : 0;
   return GQA_OK;
 }
@@ -396,7 +424,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.counters = (ws && p.route != 2) ? reinterpret_cast<uint32_t*>(base) : nullptr;
   a.slab_prefix = (ws && p.route == 2) ? reinterpret_cast<int32_t*>(base + wl.aux_offset) : nullptr;
   a.head_pieces = a.slab_prefix ? a.slab_prefix + d->batch + 1 : nullptr;
-  a.fused_combine = (d->flags & GQA_FLAG_FUSED_COMBINE) ? 1 : 0;
+  a.fused_combine = p.fused_merge;
   a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
   set_shares(a, tier_size, pg.on);
   a.batch = d->batch;
@@ -566,8 +594,9 @@ gqa_status_t decode_checked(const gqa_desc_t* desc, const void* q, const void* k
     }
     // The control words must start at zero. A plan with more of them than the
     // last one finds partials of the earlier plan there: clear those bytes
-    // (not during a capture, where that would record a memset).
-    const size_t ctrl = (size_t)plan_layout(desc, p, pg).ctrl_bytes;
+    // (not during a capture, where that would record a memset; an automatic
+    // one-launch plan then takes the two-launch merge, which needs none).
+    size_t ctrl = (size_t)plan_layout(desc, p, pg).ctrl_bytes;
     if (ctrl > ce.zero_bytes) {
       hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
       hipError_t e = hipStreamIsCapturing(stream, &cs);
@@ -575,14 +604,22 @@ gqa_status_t decode_checked(const gqa_desc_t* desc, const void* q, const void* k
         (void)hipGetLastError();
         return fail(GQA_ERR_HIP, "hipStreamIsCapturing failed: %s", hipGetErrorString(e));
       }
-      if (cs != hipStreamCaptureStatusNone)
+      if (cs != hipStreamCaptureStatusNone && !(desc->flags & GQA_FLAG_FUSED_COMBINE)) {
+        st = make_plan(desc, 0, &p, 0, pg, 0, /*one_launch_ok=*/false);
+        if (st != GQA_OK) return st;
+        ctrl = (size_t)plan_layout(desc, p, pg).ctrl_bytes;   // 0: no control words
+      } else if (cs != hipStreamCaptureStatusNone) {
         return fail(GQA_ERR_CAPTURE,
                     "the convenience call would clear %llu workspace bytes while the stream is "
                     "capturing; use the prepare / launch_gqa_decode_prepared pair",
                     (unsigned long long)(ctrl - ce.zero_bytes));
-      e = hipMemsetAsync(static_cast<char*>(ce.ptr) + ce.zero_bytes, 0, ctrl - ce.zero_bytes, stream);
-      if (e != hipSuccess)
-        return fail(GQA_ERR_HIP, "hipMemsetAsync of the workspace failed: %s", hipGetErrorString(e));
+      } else {
+        e = hipMemsetAsync(static_cast<char*>(ce.ptr) + ce.zero_bytes, 0, ctrl - ce.zero_bytes,
+                           stream);
+        if (e != hipSuccess)
+          return fail(GQA_ERR_HIP, "hipMemsetAsync of the workspace failed: %s",
+                      hipGetErrorString(e));
+      }
     }
     // Launches leave the control words at zero; everything after them is now dirty.
     ce.zero_bytes = ctrl;
@@ -629,7 +666,7 @@ gqa_status_t decode_no_alloc_checked(const gqa_desc_t* desc, const void* q, cons
                 (unsigned long long)GQA_NO_ALLOC_SCRATCH_BYTES);
   };
   gqa_plan_t p;
-  gqa_status_t st = make_plan(desc, 0, &p);
+  gqa_status_t st = make_plan(desc, 0, &p, 0, Paging(), 0, /*one_launch_ok=*/false);
   if (st != GQA_OK) return st;
   // The host-only plan already decides the chunked routes' workspace (and
   // bounds the balanced one by a nominal grid), so an oversized request is
@@ -640,7 +677,8 @@ gqa_status_t decode_no_alloc_checked(const gqa_desc_t* desc, const void* q, cons
   st = check_device(&dev);
   if (st != GQA_OK) return st;
   if (p.route == 2) {
-    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc, false), Paging(), device_cus(dev));
+    st = make_plan(desc, 0, &p, device_balanced_grid(dev, desc, false), Paging(), device_cus(dev),
+                   /*one_launch_ok=*/false);
     if (st != GQA_OK) return st;
   }
   void* ws = nullptr;
@@ -651,9 +689,9 @@ gqa_status_t decode_no_alloc_checked(const gqa_desc_t* desc, const void* q, cons
       return fail(GQA_ERR_HIP, "looking up the no-alloc scratch on device %d failed: %s", dev,
                   hipGetErrorString(e));
   }
-  // Nothing in the workspace needs to start at zero here: without the fused
-  // merge, every partial row and bookkeeping word a launch reads was written
-  // by that launch.
+  // Nothing in the workspace needs to start at zero here: without the
+  // one-launch merge (never planned for this entry point), every partial row
+  // and bookkeeping word a launch reads was written by that launch.
   return enqueue(step_args(desc, q, kv, scales, seq_lens, q_scale, out, p, ws, Paging(),
                            device_cus(dev)),
                  desc, false, stream);

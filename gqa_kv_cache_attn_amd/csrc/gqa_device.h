@@ -525,10 +525,65 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ---------------------------------------------------------------------------
+// Partials read back inside the launch that wrote them (the one-launch
+// merge). Each XCD has its own L2, not coherent with the others', so a partial
+// that a workgroup on another XCD reads within the same launch goes through
+// device-coherent accesses: the loads and stores the compiler emits for
+// relaxed agent-scope atomics (stores write through the L2, loads are not
+// served from a stale L2 line). Ordering comes from waiting for the stores
+// to complete before the counter update that announces them (publish_piece).
+// An agent-scope release/acquire fence pair would instead write back and
+// invalidate the whole L2 of the XCD for every piece.
+// ---------------------------------------------------------------------------
+template <bool kCoherent>
+__device__ __forceinline__ float2 load_partial(const float2* p) {
+  if constexpr (kCoherent) {
+    const unsigned long long v = __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_bit_cast(float2, v);
+  } else {
+    return *p;
+  }
+}
+
+template <bool kCoherent>
+__device__ __forceinline__ void store_partial(float2* p, float2 v) {
+  if constexpr (kCoherent) {
+    __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                       __builtin_bit_cast(unsigned long long, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    *p = v;
+  }
+}
+
+// Announce a piece of `total` units of one head: every thread of the
+// workgroup has stored its share of the piece with store_partial<true>; once
+// those stores have completed (s_waitcnt vmcnt(0) in each wave, then the
+// barrier), one thread adds the piece's `units` to the head's counter with a
+// device-scope atomic. Returns, in every thread, whether this piece completed
+// the head (the caller then merges it); that thread also resets the counter,
+// so every launch finds it at zero. s_flag is a workgroup-shared int.
+__device__ __forceinline__ bool publish_piece(uint32_t* counter, uint32_t units, uint32_t total,
+                                              int* s_flag) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev =
+        __hip_atomic_fetch_add(counter, units, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prev + units == total;
+    if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = last;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
 // NB partial O rows base + j0 + u (u < NB) of a merge, loaded together and
 // accumulated with their weights, which lane j of wk holds for row base + j.
 // Rows at or past cnt get weight 0 and read the fallback row instead.
-template <int NB, typename RowFn>
+template <int NB, bool kCoherent = false, typename RowFn>
 __device__ __forceinline__ void merge_batch(const float2* po, RowFn& row, size_t fallback, int base,
                                             int j0, int cnt, float wk, int lane, float& o0,
                                             float& o1) {
@@ -540,7 +595,7 @@ __device__ __forceinline__ void merge_batch(const float2* po, RowFn& row, size_t
     f[u] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wk), min(j, 63)));
     if (j >= cnt) f[u] = 0.f;
     const size_t r = f[u] != 0.f ? row(base + j) : fallback;
-    v[u] = po[r * (kHeadDim / 2) + lane];
+    v[u] = load_partial<kCoherent>(po + r * (kHeadDim / 2) + lane);
   }
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
@@ -554,17 +609,18 @@ __device__ __forceinline__ void merge_batch(const float2* po, RowFn& row, size_t
 // costs one round trip to memory. Addresses depend only on n, not on the
 // weights; rows at or past n read the first row again and, like empty rows
 // (max -inf, O possibly stale), enter with weight 0 through a select.
-template <int NB, int QT, typename RowFn>
+template <int NB, int QT, bool kCoherent, typename RowFn>
 __device__ __forceinline__ void merge_few(const StepArgs& a, int n, RowFn& row, char* outp) {
   using E = Elem<QT>;
   const int lane = threadIdx.x & 63;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   const float2* po = reinterpret_cast<const float2*>(a.part_o);
   const size_t fallback = row(0);
-  const float2 mv = ml[lane < n ? row(lane) : fallback];
+  const float2 mv = load_partial<kCoherent>(ml + (lane < n ? row(lane) : fallback));
   float2 v[NB];
 #pragma unroll
-  for (int u = 0; u < NB; ++u) v[u] = po[(u < n ? row(u) : fallback) * (kHeadDim / 2) + lane];
+  for (int u = 0; u < NB; ++u)
+    v[u] = load_partial<kCoherent>(po + (u < n ? row(u) : fallback) * (kHeadDim / 2) + lane);
   const float mk = lane < n ? mv.x : -INFINITY;
   const float M = wave_max(mk);   // finite: at least one row holds data
   const float wk = mk != -INFINITY ? fast_exp2(mk - M) : 0.f;
@@ -589,18 +645,19 @@ __device__ __forceinline__ void merge_few(const StepArgs& a, int n, RowFn& row, 
 // single round of loads. Beyond that the (m, l) pairs of 64 rows at a time are
 // loaded one per lane; the O rows follow in batches of 32, 16 and then 8
 // independent loads, so a head split into 64 pieces (one request spread over
-// the whole grid) waits for two rounds of loads, not eight.
-template <int QT, typename RowFn>
+// the whole grid) waits for two rounds of loads, not eight. kCoherent: the
+// rows were written in this launch (load_partial).
+template <int QT, bool kCoherent = false, typename RowFn>
 __device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, char* outp) {
-  if (n <= 8) return merge_few<8, QT>(a, n, row, outp);
-  if (n <= 16) return merge_few<16, QT>(a, n, row, outp);
-  if (n <= 32) return merge_few<32, QT>(a, n, row, outp);
+  if (n <= 8) return merge_few<8, QT, kCoherent>(a, n, row, outp);
+  if (n <= 16) return merge_few<16, QT, kCoherent>(a, n, row, outp);
+  if (n <= 32) return merge_few<32, QT, kCoherent>(a, n, row, outp);
   using E = Elem<QT>;
   const int lane = threadIdx.x & 63;
   const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
   const float2* po = reinterpret_cast<const float2*>(a.part_o);
   float mloc = -INFINITY;
-  for (int k = lane; k < n; k += 64) mloc = fmaxf(mloc, ml[row(k)].x);
+  for (int k = lane; k < n; k += 64) mloc = fmaxf(mloc, load_partial<kCoherent>(ml + row(k)).x);
   const float M = wave_max(mloc);   // finite: at least one row holds data
   const size_t fallback = row(0);   // a row that holds data, read with weight 0
   float lloc = 0.f, o0 = 0.f, o1 = 0.f;
@@ -608,7 +665,7 @@ __device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, 
     const int k = base + lane;
     float wk = 0.f;
     if (k < n) {
-      const float2 v = ml[row(k)];
+      const float2 v = load_partial<kCoherent>(ml + row(k));
       if (v.x != -INFINITY) {
         wk = fast_exp2(v.x - M);
         lloc += wk * v.y;
@@ -617,13 +674,13 @@ __device__ __forceinline__ void merge_rows(const StepArgs& a, int n, RowFn row, 
     const int cnt = min(64, n - base);
     int j0 = 0;
     for (; cnt - j0 >= 32; j0 += 32)
-      merge_batch<32>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
+      merge_batch<32, kCoherent>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
     if (cnt - j0 >= 16) {
-      merge_batch<16>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
+      merge_batch<16, kCoherent>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
       j0 += 16;
     }
     for (; j0 < cnt; j0 += 8)
-      merge_batch<8>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
+      merge_batch<8, kCoherent>(po, row, fallback, base, j0, cnt, wk, lane, o0, o1);
   }
   const float inv = a.v_scale / wave_sum(lloc);
   E::store2(outp, o0 * inv, o1 * inv);

@@ -54,7 +54,7 @@ namespace {
 // wave r < G takes head G g + r. Only the chunks that start below the current
 // length are read, so partials left by an earlier launch with longer lengths
 // never enter the result.
-template <int QT, int G>
+template <int QT, int G, bool kCoherent = false>
 __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int g, int L) {
   using E = Elem<QT>;
   const int lane = threadIdx.x & 63;
@@ -68,7 +68,7 @@ __device__ __forceinline__ void combine_head_group(const StepArgs& a, int b, int
     E::store2(outp, 0.f, 0.f);
     return;
   }
-  merge_rows<QT>(a, n, [&](int k) -> size_t { return head * (size_t)S + k; }, outp);
+  merge_rows<QT, kCoherent>(a, n, [&](int k) -> size_t { return head * (size_t)S + k; }, outp);
 }
 
 // One workgroup attends the G query rows of (request b, KV head g) over the
@@ -264,26 +264,22 @@ __global__ __launch_bounds__(kThreads, GQA_MIN_WAVES_PER_SIMD) void gqa_attentio
     if (er < G)
       E::store2(static_cast<char*>(a.out) + (head * kHeadDim + ed) * 2, o0 * inv, o1 * inv);
   } else {
+    // With the one-launch merge another workgroup of this launch reads the
+    // partial: device-coherent stores (store_partial).
+    constexpr bool kShared = kMode == kModeSplitFused;
     const size_t slot = head * (size_t)S + split;
     if (er < G) {
-      *reinterpret_cast<float2*>(a.part_o + slot * kHeadDim + ed) = make_float2(o0, o1);
-      if ((tid & 63) == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(M, lsum);
+      store_partial<kShared>(reinterpret_cast<float2*>(a.part_o + slot * kHeadDim + ed),
+                             make_float2(o0, o1));
+      if ((tid & 63) == 0)
+        store_partial<kShared>(reinterpret_cast<float2*>(a.part_ml + slot * 2),
+                               make_float2(M, lsum));
     }
     if constexpr (kMode == kModeSplitFused) {
-      // Publish this chunk, count it, and let the head's last chunk combine.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __syncthreads();
-      if (tid == 0) {
-        const unsigned n_valid = (unsigned)((L + a.chunk_tokens - 1) / a.chunk_tokens);
-        const unsigned prev = atomicAdd(a.counters + bg, 1u);
-        const int last = (prev + 1u == n_valid);
-        if (last) atomicExch(a.counters + bg, 0u);   // ready for the next launch
-        s_last = last;
-      }
-      __syncthreads();
-      if (!s_last) return;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      combine_head_group<QT, G>(a, b, g, L);
+      // Count this chunk; the head's last chunk merges all of them.
+      const unsigned n_valid = (unsigned)((L + a.chunk_tokens - 1) / a.chunk_tokens);
+      if (!publish_piece(a.counters + bg, 1u, n_valid, &s_last)) return;
+      combine_head_group<QT, G, true>(a, b, g, L);
     }
   }
 }

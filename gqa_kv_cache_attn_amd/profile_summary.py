@@ -144,7 +144,7 @@ def cmd_phases(a):
         if "gqa" in name and "append" not in name:
             if seen_marker:
                 cur.append(r)
-        elif "Fill" in name or "fill" in name:
+        elif "FillFunctor" in name:
             if cur:
                 passes.append(cur)
             cur, seen_marker = [], True
@@ -154,8 +154,9 @@ def cmd_phases(a):
     passes = passes[-len(names):]
     us = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
     lines = [f"# {a.title}", "", f"command: {a.command}", "",
-             "| pass | steps | attention avg us | combine avg us | gap attention->combine us | "
-             "gap combine->attention us | us per step (first start to last end) |",
+             "| pass | steps | attention avg us | combine avg us | gap attention->combine us "
+             "(median) | gap combine->next attention us (median) | us per step (median start "
+             "to start) |",
              "|---|---|---|---|---|---|---|"]
     for name, p in zip(names, passes):
         att = [r for r in p if "combine" not in r["Kernel_Name"]]
@@ -164,10 +165,12 @@ def cmd_phases(a):
         for x, y in zip(p, p[1:]):
             gap = (int(y["Start_Timestamp"]) - int(x["End_Timestamp"])) / 1e3
             (g_ac if "combine" in y["Kernel_Name"] else g_ca).append(gap)
-        span = (int(p[-1]["End_Timestamp"]) - int(p[0]["Start_Timestamp"])) / 1e3 / max(1, len(att))
+        starts = [int(r["Start_Timestamp"]) for r in att]
+        step = [(y - x) / 1e3 for x, y in zip(starts, starts[1:])]
         f = lambda xs: f"{statistics.fmean(xs):.2f}" if xs else "-"
+        m = lambda xs: f"{statistics.median(xs):.2f}" if xs else "-"
         lines.append(f"| {name} | {len(att)} | {f([us(r) for r in att])} | {f([us(r) for r in com])} "
-                     f"| {f(g_ac)} | {f(g_ca)} | {span:.2f} |")
+                     f"| {m(g_ac)} | {m(g_ca)} | {m(step)} |")
     lines.append("")
     lines.append(f"kernel_source_sha256_16 = {kernel_source_digest(a.kernel)}")
     with open(a.out, "w") as f:

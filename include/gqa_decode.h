@@ -117,19 +117,24 @@ typedef struct gqa_desc {
 } gqa_desc_t;
 
 /* Split plans merge their chunks with a log-sum-exp combine kernel launched
- * right after the attention kernel on the same stream. With this flag the
- * last workgroup to finish a (request, KV head) merges inside the attention
- * kernel instead (one launch; a per-head counter in the workspace, reset by
- * that workgroup, tells it that it is last). The fused form needs an
- * agent-scope release/acquire fence pair around every workgroup's partial,
- * which on a multi-XCD part costs more than the second launch saves, so it
- * is opt-in. */
+ * right after the attention kernel on the same stream, or, in one launch,
+ * inside the attention kernel: the last workgroup to finish a (request, KV
+ * head) merges it (a per-head counter in the workspace, reset by that
+ * workgroup, tells it that it is last; the partials travel through
+ * device-coherent stores and loads, with no cache-wide fence). The automatic
+ * plan takes the one-launch merge for small problems (a chunked split of at
+ * most 16 chunks per head and 384 workgroups over a contiguous cache), where
+ * it saves the second launch; on large grids the workgroups' waits on their
+ * counters cost more than that launch. This flag asks for the one-launch
+ * merge on any chunked plan (and keeps the plan off the balanced split). */
 #define GQA_FLAG_FUSED_COMBINE 1
 
 /* Launch plan chosen for a descriptor (host arithmetic only).
  * route 0 (short, capacity <= 64) and single-chunk plans: one workgroup per
  * (request, KV head), output normalised in place, no workspace.
- * route 1 (chunked split, explicit num_splits >= 2, or the fused merge):
+ * route 1 (chunked split: explicit num_splits >= 2, the fused-merge flag, or
+ * an automatic plan for a problem too small for the balanced split, whose
+ * chunks then hold about an eighth of the capacity, 64 to 256 slots):
  * num_splits chunks of chunk_tokens slots per (request, KV head) -> FP32
  * partials -> log-sum-exp combine, as the article's split routes.
  * route 2 (balanced split, the automatic choice above capacity 64 for up to
@@ -146,6 +151,8 @@ typedef struct gqa_plan {
   int32_t chunk_tokens;    /* tokens per chunk (multiple of GQA_CHUNK_GRANULE) or slab (64) */
   int32_t num_workgroups;  /* workgroups of the attention kernel */
   uint64_t workspace_bytes;/* FP32 partials (+ counters / slab prefix); 0 when no merge */
+  int32_t fused_merge;     /* 1: one launch, the last workgroup of each head merges it
+                              (GQA_FLAG_FUSED_COMBINE, or a small automatic split) */
 } gqa_plan_t;
 
 typedef struct gqa_prepared gqa_prepared_t;

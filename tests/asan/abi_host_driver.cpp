@@ -174,6 +174,7 @@ void check_plan(const gqa_plan_t& p, int32_t batch, int32_t C, int32_t ns) {
     EXPECT((int64_t)(p.num_splits - 1) * p.chunk_tokens < C);
     EXPECT((p.num_splits > 1) == (p.workspace_bytes > 0));
     EXPECT((int64_t)p.num_workgroups == (int64_t)batch * 8 * p.num_splits);
+    if (p.fused_merge) EXPECT(p.num_splits > 1);
   }
 }
 

@@ -157,7 +157,38 @@ def test_auto_plan_is_the_balanced_split(B, C):
         return
     G = nominal_balanced_grid(B, C)
     assert p == {"route": 2, "num_splits": 0, "chunk_tokens": 64, "num_workgroups": G,
-                 "workspace_bytes": balanced_ws(B, G)}
+                 "workspace_bytes": balanced_ws(B, G), "fused_merge": 0}
+
+
+def small_chunk(C):
+    """Automatic chunk of a problem too small for the balanced split: about an
+    eighth of the capacity in 64-slot steps, from 64 to 256 slots."""
+    return min(256, max(64, -(-(-(-C // 8)) // 64) * 64))
+
+
+@pytest.mark.parametrize("B,C", [(1, 65), (1, 128), (1, 500), (1, 1024), (1, 2048), (1, 4096),
+                                 (1, 6000), (2, 1024), (4, 1024), (5, 1000), (11, 512),
+                                 (40, 128), (47, 65)])
+def test_small_automatic_plans_and_the_one_launch_merge(B, C):
+    assert B * 8 * -(-C // 64) < 768
+    p = b.gqa_plan(desc(batch=B, capacity=C))
+    T = small_chunk(C)
+    S = -(-C // T)
+    one = 1 < S <= 16 and B * 8 * S <= 384
+    ctrl = ((B * 8 * 4 + 255) // 256) * 256 if one else 0
+    assert p == {"route": 1, "num_splits": S, "chunk_tokens": T, "num_workgroups": B * 8 * S,
+                 "workspace_bytes": ctrl + B * 32 * S * 130 * 4 if S > 1 else 0,
+                 "fused_merge": int(one)}
+    # An explicit split count keeps the two-launch merge unless the flag asks.
+    if S > 1:
+        assert b.gqa_plan(desc(batch=B, capacity=C), S)["fused_merge"] == 0
+    # The paged kernels take no one-launch merge.
+    P = 16
+    pp = b.gqa_plan_paged(b.GqaPagedDesc(batch=B, q_tokens=1, num_q_heads=32, num_kv_heads=8,
+                                         head_dim=128, q_dtype=b.GQA_BF16, kv_dtype=b.GQA_BF16,
+                                         k_scale=1.0, v_scale=1.0, flags=0, page_size=P,
+                                         num_pages=B * (-(-C // P)), max_pages=-(-C // P)))
+    assert pp["fused_merge"] == 0
 
 
 @pytest.mark.parametrize("kv,slot", [(b.GQA_BF16, 512), (b.GQA_FP8_E4M3, 256),
@@ -190,9 +221,10 @@ def test_chunked_auto_plan_is_consistent(B, C):
     # control words (fused merge: one uint32 counter per (request, KV head)),
     # then FP32 partials (O, then max/sum)
     fused = B <= 4096
-    ctrl = ((B * 8 * 4 + 255) // 256) * 256 if fused else 0
+    ctrl = ((B * 8 * 4 + 255) // 256) * 256 if fused and S > 1 else 0
     want_ws = ctrl + B * 32 * S * 130 * 4 if S > 1 else 0
     assert p["workspace_bytes"] == want_ws
+    assert p["fused_merge"] == int(fused and S > 1)
 
 
 @pytest.mark.parametrize("C", [100, 1000, 1024, 65536])

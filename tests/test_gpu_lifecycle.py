@@ -91,6 +91,36 @@ def test_convenience_call_refuses_to_allocate_inside_capture():
     assert torch.all(x == 1.0)
 
 
+def test_convenience_call_under_capture_takes_two_launches_when_counters_are_dirty():
+    """A small problem's automatic plan merges in one launch, which needs its
+    per-head counters at zero. When an earlier, larger plan left partials in
+    the stream's cached workspace, clearing them inside a capture would record
+    a memset, so the captured call takes the two-launch merge instead of
+    failing; its replays equal the eager one-launch result bit for bit."""
+    b = binding()
+    big = _inputs(B=8, C=8192, seed=61)
+    small = _inputs(B=1, C=1024, seed=62)
+    assert b.gqa_plan(b.make_desc(small["q"], small["kv"]))["fused_merge"] == 1
+    out_big, eager, replayed = (torch.empty_like(x["q"]) for x in (big, small, small))
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        b.gqa_decode(big["q"], big["kv"], big["seq_lens"], big["q_scale"], out_big)
+        b.gqa_decode(small["q"], small["kv"], small["seq_lens"], small["q_scale"], eager)
+        # the small call cleared its counters; the big one dirties them again
+        b.gqa_decode(big["q"], big["kv"], big["seq_lens"], big["q_scale"], out_big)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        b.gqa_decode(small["q"], small["kv"], small["seq_lens"], small["q_scale"], replayed)
+    for _ in range(3):
+        replayed.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(replayed.view(torch.int16), eager.view(torch.int16))
+    compare(replayed, oracle_pairs(small, all_pairs(1)), small, "captured convenience, small")
+    del graph
+
+
 def test_two_handles_on_two_concurrent_streams():
     b = binding()
     inp1 = _inputs(seed=41)
