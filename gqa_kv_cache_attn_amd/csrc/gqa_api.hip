@@ -144,12 +144,13 @@ int device_cus(int dev) {
 #ifndef GQA_SHARE_ODD
 #define GQA_SHARE_ODD 920
 #endif
-// The paged kernel at two workgroups per CU sees a larger odd-XCD gap: a sweep
-// of its odd share (840-920) was fastest at 860 on the 16-slot bf16 and 64-slot
-// fp8 pools (1.2-1.3% over 920); the INT8 pool (three per CU) was slower below
-// 920, and the contiguous kernels were within noise of 920 at 860-900.
+// The paged kernel at two workgroups per CU takes the same odd-XCD share: a
+// sweep on one box favoured 860 by 1.2-1.3% on the 16-slot bf16 and 64-slot
+// fp8 pools, but on a second box 920 was 1.1-1.2% faster on both (three
+// alternating samples each), so the difference is within the spread between
+// boxes and one share serves both kernels.
 #ifndef GQA_SHARE_ODD_PAGED_TWO
-#define GQA_SHARE_ODD_PAGED_TWO 860
+#define GQA_SHARE_ODD_PAGED_TWO GQA_SHARE_ODD
 #endif
 
 // a.grid_wgs must be set: the shares depend on how many workgroups share a CU.

@@ -6,6 +6,8 @@
         --fetch F_counter_collection.csv --write W_counter_collection.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N \\
         --algorithmic-bytes A --command "C" --out profiles/gqa_attention_kernel_W_traffic.txt
+    python -m gqa_kv_cache_attn_amd.profile_summary counters --csv A.csv B.csv --elements E \\
+        --title T --command "C" --out profiles/X.txt
     python -m gqa_kv_cache_attn_amd.profile_summary phases --trace K_kernel_trace.csv \\
         --names direct,graph1,... --title T --command "C" --out profiles/X.txt
 
@@ -178,6 +180,58 @@ def cmd_phases(a):
     print("\n".join(lines))
 
 
+def _counters_by_name(path, match):
+    """{counter name: mean per dispatch} over the dispatches of the matching kernel."""
+    acc = {}
+    for r in csv.DictReader(open(path)):
+        if match in r["Kernel_Name"]:
+            acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.fmean(v) for k, v in acc.items()}
+
+
+def cmd_counters(a):
+    """Instruction and busy-cycle counters of one kernel, with the ratios that
+    say how much of the matrix and vector units the kernel keeps busy."""
+    match = f"::{a.kernel}<"
+    vals = {}
+    for path in a.csv:
+        vals.update(_counters_by_name(path, match))
+    if not vals:
+        raise SystemExit(f"no dispatch of {a.kernel} in {a.csv}")
+    lines = [f"# {a.title}", "", f"command: {a.command}", "",
+             f"kernel: {a.kernel}; counters averaged per dispatch; {a.elements} KV elements "
+             f"(valid K and V values) per launch", "",
+             "| counter | per launch |", "|---|---|"]
+    for k in sorted(vals):
+        lines.append(f"| {k} | {vals[k]:.6g} |")
+    lines.append("")
+    simds = a.cus * 4
+    gui = vals.get("GRBM_GUI_ACTIVE")
+    if gui:
+        # GRBM_GUI_ACTIVE is summed over the XCDs; each counts the kernel's cycles.
+        cycles = gui / a.xcds
+        lines.append(f"GPU-busy cycles per XCD: {cycles:.6g} ({cycles / (a.clock_ghz * 1e3):.1f} us at "
+                     f"{a.clock_ghz} GHz)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals:
+            lines.append(f"MFMA busy: {100 * vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (cycles * simds):.2f}% "
+                         f"of the {simds} SIMDs' cycles")
+        if "SQ_ACTIVE_INST_VALU" in vals:
+            # quad-cycles, summed over waves; at most `waves per SIMD` waves issue per SIMD
+            lines.append(f"VALU active: {100 * 4 * vals['SQ_ACTIVE_INST_VALU'] / (cycles * simds):.2f}% "
+                         f"of the SIMDs' cycles (summed over waves)")
+    e = a.elements
+    for k, label in (("SQ_INSTS_VALU", "VALU"), ("SQ_INSTS_MFMA", "MFMA"), ("SQ_INSTS_VMEM_RD", "VMEM read"),
+                     ("SQ_INSTS_LDS", "LDS"), ("SQ_INSTS_SALU", "SALU")):
+        if k in vals:
+            lines.append(f"{label} instructions per 1000 KV elements: {1000 * vals[k] / e:.3f} "
+                         f"(per lane-element: {vals[k] * 64 / e:.3f})")
+    lines.append("")
+    lines.append(f"kernel_source_sha256_16 = {kernel_source_digest(a.kernel)}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -202,8 +256,18 @@ def main():
     for k in ("trace", "names", "title", "command", "out"):
         ph.add_argument("--" + k, required=True)
     ph.add_argument("--kernel", default="gqa_balanced_attention_kernel")
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", nargs="+", required=True)
+    for k in ("title", "command", "out"):
+        c.add_argument("--" + k, required=True)
+    c.add_argument("--kernel", default="gqa_balanced_attention_kernel")
+    c.add_argument("--elements", type=int, required=True, help="valid K and V values per launch")
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--clock-ghz", type=float, default=2.4)
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "phases": cmd_phases}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "phases": cmd_phases,
+     "counters": cmd_counters}[a.cmd](a)
 
 
 if __name__ == "__main__":
