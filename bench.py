@@ -316,10 +316,12 @@ def _event(stream):
 
 
 def _marker(dev, k):
-    """A tiny fill kernel between measurement passes, so a rocprofv3 kernel
-    trace of this run can be split into its passes (outside every timed region)."""
+    """A tiny kernel between measurement passes, so a rocprofv3 kernel trace of
+    this run can be split into its passes (outside every timed region). It is
+    torch's negation of a 256-element tensor, which nothing else in this
+    program launches (torch's graph replays launch small fills of their own)."""
     import torch
-    torch.full((256,), float(k + 1), device=dev)
+    torch.full((256,), float(k + 1), device=dev).neg_()
     torch.cuda.synchronize()
 
 
@@ -376,6 +378,42 @@ def time_graph(case, K, stream, steps_per_graph):
     return e0.elapsed_time(e1) * 1e3 / steps, (h1 - h0) * 1e6 / launches, steps
 
 
+def time_graph_floor(dev, K, stream):
+    """The same replay loop over a graph of two one-block fill kernels: the
+    runtime's own cost per graph launch, whatever the graph holds. Returns
+    (GPU µs per replay, host µs per replay call)."""
+    import torch
+    t = torch.zeros(64, device=dev)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        t.fill_(1.0)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        t.fill_(2.0)
+        t.fill_(3.0)
+    n, t0 = 0, time.perf_counter()
+    while n < 10 or time.perf_counter() - t0 < 0.2:
+        graph.replay()
+        n += 1
+        if n % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0, e1 = _event(stream), _event(stream)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    h0 = time.perf_counter()
+    for _ in range(K):
+        graph.replay()
+    h1 = time.perf_counter()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1e3 / K, (h1 - h0) * 1e6 / K
+
+
 def config_entry(case, direct_us, graph1, graph16):
     gbps = case.nbytes / (direct_us * 1e-6) / 1e9
     return {
@@ -398,13 +436,14 @@ def measure_config(name, args, dev, stream, phase):
     w = WORKLOADS_BY_NAME[name]      # as defined: the headline's overrides do not apply
     print(f"[bench] config {w.name}", file=sys.stderr, flush=True)
     case = Case(w, dev)
-    case.warm(0.3, 100)
-    K = max(args.steps, 48)
     _marker(dev, phase)
-    direct = time_direct(case, K, stream)
+    case.warm(1.0, 100)
+    K = max(args.steps, 48)
     _marker(dev, phase + 1)
-    g1 = time_graph(case, K, stream, 1)
+    direct = time_direct(case, K, stream)
     _marker(dev, phase + 2)
+    g1 = time_graph(case, K, stream, 1)
+    _marker(dev, phase + 3)
     g16 = time_graph(case, K, stream, GRAPH_STEPS)
     entry = config_entry(case, direct, g1, g16)
     entry["steps_timed"] = K
@@ -457,9 +496,15 @@ def run(args, dev, arch, stream):
     case = Case(w, dev, args.num_splits, args.fused_combine, args.page_order)
     paged, inp, out, nbytes, lens = case.paged, case.inp, case.out, case.nbytes, case.lens
     plan = dict(case.plan)
-    plan["combine"] = "fused (last workgroup)" if args.fused_combine else "separate kernel"
+    if plan.get("fused_merge"):
+        plan["combine"] = "one launch (the last workgroup of each head merges it)"
+    elif plan["route"] != 2 and plan["num_splits"] == 1:
+        plan["combine"] = "none (one chunk per head)"
+    else:
+        plan["combine"] = "separate kernel"
 
     K = args.steps
+    _marker(dev, 99)
     if args.warmup is not None:
         W = args.warmup
         for _ in range(W):
@@ -506,6 +551,8 @@ def run(args, dev, arch, stream):
     _marker(dev, 103)
     g16 = time_graph(case, K, stream, GRAPH_STEPS)
     _marker(dev, 104)
+    floor = time_graph_floor(dev, max(K, 48), stream)
+    _marker(dev, 106)
     if not args.no_configs or w.name in CONFIG_WORKLOADS:
         configs[w.name] = {**config_entry(case, ms_per_step * 1e3, g1, g16), "steps_timed": K}
 
@@ -611,6 +658,9 @@ def run(args, dev, arch, stream):
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_graph_replay": round(g1[0], 2),
         "us_per_step_graph_16step": round(g16[0], 2),
+        "graph_launch_floor": {"us_per_replay": round(floor[0], 2),
+                               "host_us_per_replay": round(floor[1], 2),
+                               "graph": "two one-block fill kernels"},
         "us_per_call_convenience": round(convenience_us, 2),
         "us_per_call_cold": {"p10": round(pct(cold, 10), 2), "p50": round(pct(cold, 50), 2),
                              "p90": round(pct(cold, 90), 2)} if cold else None,

@@ -10,15 +10,17 @@
         --title T --command "C" --out profiles/X.txt
     python -m gqa_kv_cache_attn_amd.profile_summary phases --trace K_kernel_trace.csv \\
         --names direct,graph1,... --title T --command "C" --out profiles/X.txt
+    python -m gqa_kv_cache_attn_amd.profile_summary calibrate [--gib 1] [--iters 3]   (GPU)
 
 `traffic` scales each counter by what it reads for a plain elementwise pass
-of known size (torch's bitwise_not over a 1 GiB uint8 tensor into another:
-N bytes read, N bytes written per launch), so counter units become bytes; it
-records the kernel-source digest the counters were taken with, and bench.py
-only reports the figure while that digest still matches the source.
+of known size (`calibrate`: torch's bitwise_not over a 1 GiB uint8 tensor
+into another, N bytes read, N bytes written per launch), so counter units
+become bytes. It records the kernel-source digest the counters were taken
+with, and bench.py only reports the figure while that digest still matches
+the source.
 
 `phases` splits a kernel trace of a bench.py run at the marker kernels bench
-places between its measurement passes (a fill of a 256-element tensor) and
+places between its measurement passes (a negation of a 256-element tensor) and
 reports, per pass, the decode kernels' average durations, the gaps between
 consecutive kernels and the time per step.
 """
@@ -140,20 +142,24 @@ def cmd_phases(a):
     rows = sorted(csv.DictReader(open(a.trace)), key=lambda r: int(r["Start_Timestamp"]))
     # Passes: runs of decode kernels between marker kernels (bench places a
     # marker before each pass). Other kernels (input generation) are dropped.
+    # A marker is the negation kernel bench launches between passes (torch's
+    # graph replays launch small fills of their own, so fills cannot mark).
+    # Passes with no decode kernel (the graph-launch floor) are dropped.
     passes, cur, seen_marker = [], [], False
     for r in rows:
         name = r["Kernel_Name"]
         if "gqa" in name and "append" not in name:
             if seen_marker:
                 cur.append(r)
-        elif "FillFunctor" in name:
+        elif a.marker in name:
             if cur:
                 passes.append(cur)
             cur, seen_marker = [], True
     if cur:
         passes.append(cur)
     names = a.names.split(",")
-    passes = passes[-len(names):]
+    if len(names) != len(passes):
+        raise SystemExit(f"{len(passes)} passes with decode kernels in the trace, {len(names)} names given")
     us = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
     lines = [f"# {a.title}", "", f"command: {a.command}", "",
              "| pass | steps | attention avg us | combine avg us | gap attention->combine us "
@@ -232,6 +238,22 @@ def cmd_counters(a):
     print("\n".join(lines))
 
 
+def cmd_calibrate(a):
+    """The calibration pass the traffic summaries scale by (run under
+    rocprofv3 --pmc): torch's bitwise_not over an N GiB uint8 tensor into
+    another, `iters` times, so each launch reads and writes N GiB."""
+    import torch
+    n = a.gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(0x5A)
+    dst = torch.empty_like(src)
+    for _ in range(a.iters):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    assert int(dst[0]) == 0xA5 and int(dst[-1]) == 0xA5
+    print(f"bitwise_not over {n} bytes x {a.iters}")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -256,6 +278,8 @@ def main():
     for k in ("trace", "names", "title", "command", "out"):
         ph.add_argument("--" + k, required=True)
     ph.add_argument("--kernel", default="gqa_balanced_attention_kernel")
+    ph.add_argument("--marker", default="neg_kernel",
+                    help="substring naming the marker kernel between passes")
     c = sub.add_parser("counters")
     c.add_argument("--csv", nargs="+", required=True)
     for k in ("title", "command", "out"):
@@ -265,9 +289,12 @@ def main():
     c.add_argument("--cus", type=int, default=256)
     c.add_argument("--xcds", type=int, default=8)
     c.add_argument("--clock-ghz", type=float, default=2.4)
+    k = sub.add_parser("calibrate")
+    k.add_argument("--gib", type=int, default=1)
+    k.add_argument("--iters", type=int, default=3)
     a = ap.parse_args()
     {"stats": cmd_stats, "traffic": cmd_traffic, "phases": cmd_phases,
-     "counters": cmd_counters}[a.cmd](a)
+     "counters": cmd_counters, "calibrate": cmd_calibrate}[a.cmd](a)
 
 
 if __name__ == "__main__":
