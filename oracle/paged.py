@@ -16,7 +16,11 @@ What is computed.
   ``[batch, max_pages]``: slot ``j`` of request ``b`` is row ``j % page_size``
   of page ``block_table[b, j // page_size]``. An INT8 pool carries its row
   scales as ``[num_pages, 2, 8, page_size]`` bf16 (Orin Qwen3-VL doc, "INT8 KV
-  cache": one scale per (position, KV head) row).
+  cache": one scale per (position, KV head) row), or, as a second layout,
+  indexed by the request's position instead of the page:
+  ``[batch, 2, 8, max_pages * page_size]``, the scale of slot ``j`` of
+  request ``b`` at ``[b, plane, g, j]`` (the contiguous INT8 cache's scale
+  layout, whatever page holds the row).
 * Several query tokens. The Thor vLLM notes on MTP (K draft tokens per step,
   verified by the target model each step) imply a pass over K + 1 new tokens
   per request. Reading taken: ``T`` query tokens per request, ``q`` of shape
@@ -42,7 +46,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .gqa_oracle import HEAD_DIM, NUM_KV_HEADS, gqa_decode_head
+from .gqa_oracle import HEAD_DIM, NUM_KV_HEADS, decode_int8_rows, gqa_decode_head
 from .kv_append import quantise_fp8, quantise_int8_rows
 
 
@@ -113,6 +117,25 @@ def gqa_decode_paged_reference(q: np.ndarray, kv_pages: np.ndarray, block_table,
     return gqa_decode_multi(q, rows, lens, q_scale, k_scale, v_scale)
 
 
+def int8_rows_by_position(pool_codes, scale_bits_by_position, block_table, seq_lens,
+                          page_size: int):
+    """Decoded fp64 logical rows [2, 8, L_b, 128] of every request of an INT8
+    pool whose row scales are indexed by position: the codes gathered through
+    the block table, times the scales ``scale_bits_by_position[b, :, :, :L_b]``."""
+    table = np.asarray(block_table)
+    scales = np.asarray(scale_bits_by_position)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if table.ndim != 2 or scales.shape[:3] != (table.shape[0], 2, NUM_KV_HEADS) or \
+            scales.shape[3] != table.shape[1] * page_size:
+        raise ValueError("scales must be [batch, 2, 8, max_pages * page_size]")
+    rows = []
+    for b in range(table.shape[0]):
+        L = int(lens[b])
+        codes = gather_pages(pool_codes, table[b], L, page_size)
+        rows.append(decode_int8_rows(codes, scales[b, :, :, :L]))
+    return rows
+
+
 def kv_append_paged_reference(pool_bits: np.ndarray, block_table, positions, k_new_f32,
                               v_new_f32, kv_dtype: str, k_scale: float = 1.0,
                               v_scale: float = 1.0, new_bits=None) -> np.ndarray:
@@ -148,18 +171,24 @@ def kv_append_paged_reference(pool_bits: np.ndarray, block_table, positions, k_n
 
 
 def kv_append_paged_int8_reference(pool_codes, pool_scale_bits, block_table, positions, k_new_f32,
-                                   v_new_f32, k_scale: float = 1.0, v_scale: float = 1.0):
+                                   v_new_f32, k_scale: float = 1.0, v_scale: float = 1.0,
+                                   scales_by_position: bool = False):
     """Return copies of an INT8 pool (codes [num_pages, 2, 8, P, 128], bf16
-    scale bits [num_pages, 2, 8, P]) after appending T tokens per request,
-    each row quantised as in kv_append.quantise_int8_rows. Slots and pages
-    are found as in kv_append_paged_reference; tokens are written in (b, t)
-    order."""
+    scale bits [num_pages, 2, 8, P], or [B, 2, 8, max_pages * P] with
+    ``scales_by_position``) after appending T tokens per request, each row
+    quantised as in kv_append.quantise_int8_rows. Slots and pages are found
+    as in kv_append_paged_reference; a token whose slot or page is skipped
+    writes no scale either. Tokens are written in (b, t) order."""
     codes = np.array(pool_codes, copy=True)
     scales = np.array(pool_scale_bits, copy=True)
     num_pages, _, H, P, D = codes.shape
-    assert H == NUM_KV_HEADS and D == HEAD_DIM and scales.shape == (num_pages, 2, H, P)
     table = np.asarray(block_table)
     B, max_pages = table.shape
+    assert H == NUM_KV_HEADS and D == HEAD_DIM
+    if scales_by_position:
+        assert scales.shape == (B, 2, H, max_pages * P)
+    else:
+        assert scales.shape == (num_pages, 2, H, P)
     T = np.asarray(k_new_f32).shape[1]
     for b in range(B):
         for t in range(T):
@@ -170,8 +199,11 @@ def kv_append_paged_int8_reference(pool_codes, pool_scale_bits, block_table, pos
             if not 0 <= page < num_pages:
                 continue
             row = s % P
-            codes[page, 0, :, row, :], scales[page, 0, :, row] = \
-                quantise_int8_rows(k_new_f32[b][t], k_scale)
-            codes[page, 1, :, row, :], scales[page, 1, :, row] = \
-                quantise_int8_rows(v_new_f32[b][t], v_scale)
+            for plane, (new, scale) in enumerate(((k_new_f32, k_scale), (v_new_f32, v_scale))):
+                c, sb = quantise_int8_rows(new[b][t], scale)
+                codes[page, plane, :, row, :] = c
+                if scales_by_position:
+                    scales[b, plane, :, s] = sb
+                else:
+                    scales[page, plane, :, row] = sb
     return codes, scales

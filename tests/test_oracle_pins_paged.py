@@ -13,7 +13,9 @@ from oracle import HEAD_DIM, NUM_KV_HEADS, decode_int8_rows, gqa_decode_referenc
 from oracle.brute import brute_decode
 from oracle.kv_append import (kv_append_int8_reference, kv_append_reference, quantise_fp8,
                                quantise_int8_rows)
-from oracle.paged import (gather_pages, gqa_decode_multi, gqa_decode_paged_reference, kv_append_paged_int8_reference, kv_append_paged_reference)
+from oracle.paged import (gather_pages, gqa_decode_multi, gqa_decode_paged_reference,
+                          int8_rows_by_position, kv_append_paged_int8_reference,
+                          kv_append_paged_reference)
 
 
 def _scatter_case(rng, B, P, max_pages, lens, spare=3, dtype=np.float64):
@@ -271,3 +273,113 @@ def test_int8_append_lands_at_its_slots_and_skips_what_is_out_of_range():
     keep = ~touched
     assert np.array_equal(got.transpose(0, 3, 1, 2, 4)[keep], codes.transpose(0, 3, 1, 2, 4)[keep])
     assert np.array_equal(gsc.transpose(0, 3, 1, 2)[keep], sbits.transpose(0, 3, 1, 2)[keep])
+
+
+# ---------------------------------------------------------------------------
+# INT8 pools whose row scales are indexed by position ([B, 2, 8, max_pages * P]).
+
+def _int8_pool_case(rng, B, P, max_pages, spare=3):
+    num_pages = B * max_pages + spare
+    codes = rng.integers(-127, 128, size=(num_pages, 2, NUM_KV_HEADS, P, HEAD_DIM)).astype(np.int8)
+    # finite positive bf16 scales spread over 2^-14 .. 2^4 (exponent field 113..131)
+    sbits = (rng.integers(113, 132, size=(num_pages, 2, NUM_KV_HEADS, P)) << 7 |
+             rng.integers(0, 128, size=(num_pages, 2, NUM_KV_HEADS, P))).astype(np.uint16)
+    table = rng.permutation(num_pages)[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    return codes, sbits, table
+
+
+@pytest.mark.parametrize("P", [16, 32, 64])
+def test_position_scales_decode_as_the_page_scales_they_were_gathered_from(P):
+    """Relabelling invariance: the same pool with its page scales moved to the
+    positions that read them decodes to the same rows, element for element
+    (a plane/head transposition or an off-by-one slot in the position
+    indexing fails this)."""
+    rng = np.random.default_rng(60 + P)
+    B, max_pages = 3, 4
+    codes, sbits, table = _int8_pool_case(rng, B, P, max_pages)
+    lens = [max_pages * P, 1, 2 * P + 5]
+    C = max_pages * P
+    pos_scales = np.full((B, 2, NUM_KV_HEADS, C), 0x7FC0, dtype=np.uint16)   # NaN past L
+    for b in range(B):
+        L = lens[b]
+        pos_scales[b, :, :, :L] = gather_pages(sbits[..., None], table[b], L, P)[..., 0]
+    got = int8_rows_by_position(codes, pos_scales, table, lens, P)
+    for b in range(B):
+        L = lens[b]
+        want = decode_int8_rows(gather_pages(codes, table[b], L, P),
+                                gather_pages(sbits[..., None], table[b], L, P)[..., 0])
+        assert got[b].shape == (2, NUM_KV_HEADS, L, HEAD_DIM)
+        assert np.array_equal(got[b], want)
+
+
+def test_position_scales_on_an_identity_table_are_the_contiguous_int8_cache():
+    """With page b holding request b's slots in order, the pool and its
+    position scales are the contiguous INT8 cache and its scale array, and
+    decode with the contiguous definition."""
+    rng = np.random.default_rng(61)
+    B, C = 2, 16
+    codes = rng.integers(-127, 128, size=(B, 2, NUM_KV_HEADS, C, HEAD_DIM)).astype(np.int8)
+    sbits = (rng.integers(118, 128, size=(B, 2, NUM_KV_HEADS, C)) << 7).astype(np.uint16)
+    lens = [16, 9]
+    table = np.arange(B).reshape(B, 1)
+    rows = int8_rows_by_position(codes, sbits, table, lens, C)
+    q = rng.standard_normal((B, 1, 32, HEAD_DIM))
+    got = gqa_decode_multi(q, rows, lens, 0.7, 0.5, 2.0)[:, 0]
+    X = decode_int8_rows(codes, sbits)
+    want = gqa_decode_reference(q[:, 0], X, lens, 0.7, 0.5, 2.0)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-14)
+
+
+def test_position_scale_append_on_an_identity_table_is_the_contiguous_int8_append():
+    rng = np.random.default_rng(62)
+    B, C = 3, 16
+    codes = rng.integers(-127, 128, size=(B, 2, NUM_KV_HEADS, C, HEAD_DIM)).astype(np.int8)
+    sbits = rng.integers(0, 1 << 15, size=(B, 2, NUM_KV_HEADS, C)).astype(np.uint16)
+    k = rng.standard_normal((B, 1, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    v = rng.standard_normal((B, 1, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    pos = [0, 15, 9]
+    table = np.arange(B).reshape(B, 1)
+    got = kv_append_paged_int8_reference(codes, sbits, table, pos, k, v, 0.5, 2.0,
+                                         scales_by_position=True)
+    want = kv_append_int8_reference(codes, sbits, k[:, 0], v[:, 0], pos, 0.5, 2.0)
+    assert all(np.array_equal(g, w) for g, w in zip(got, want))
+
+
+def test_position_scale_append_writes_the_scale_at_the_position_and_skips_with_the_row():
+    """Across a page boundary, with shuffled pages: the codes land as in the
+    page-scale append (separately pinned) and each scale at [b, plane, g,
+    slot]; a token whose slot lies past the table or whose entry lies outside
+    the pool writes neither; every other scale is unchanged."""
+    rng = np.random.default_rng(63)
+    P, B, T, max_pages, num_pages = 16, 4, 3, 3, 12
+    codes = rng.integers(-127, 128, size=(num_pages, 2, NUM_KV_HEADS, P, HEAD_DIM)).astype(np.int8)
+    page_sb = rng.integers(0, 1 << 15, size=(num_pages, 2, NUM_KV_HEADS, P)).astype(np.uint16)
+    pos_sb = rng.integers(0, 1 << 15, size=(B, 2, NUM_KV_HEADS, max_pages * P)).astype(np.uint16)
+    k = rng.standard_normal((B, T, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    v = rng.standard_normal((B, T, NUM_KV_HEADS, HEAD_DIM)).astype(np.float32)
+    table = np.array([[3, 7, 1], [0, -1, 2], [4, num_pages, 6], [8, 9, 11]])
+    pos = [P - 1, P - 2, 2 * P - 1, 3 * P - 1]
+    got_c, got_s = kv_append_paged_int8_reference(codes, pos_sb, table, pos, k, v, 0.25, 4.0,
+                                                  scales_by_position=True)
+    want_c, _ = kv_append_paged_int8_reference(codes, page_sb, table, pos, k, v, 0.25, 4.0)
+    assert np.array_equal(got_c, want_c)
+    touched = np.zeros((B, max_pages * P), dtype=bool)
+    for b in range(B):
+        for t in range(T):
+            s_ = pos[b] + t
+            if s_ >= max_pages * P or not 0 <= table[b, s_ // P] < num_pages:
+                continue
+            _, ks = quantise_int8_rows(k[b, t], 0.25)
+            _, vs = quantise_int8_rows(v[b, t], 4.0)
+            assert np.array_equal(got_s[b, 0, :, s_], ks) and np.array_equal(got_s[b, 1, :, s_], vs)
+            touched[b, s_] = True
+    assert touched.sum() == 3 + 2 + 2 + 1
+    keep = ~touched
+    assert np.array_equal(got_s.transpose(0, 3, 1, 2)[keep], pos_sb.transpose(0, 3, 1, 2)[keep])
+
+
+def test_position_scales_reject_a_wrong_shape():
+    rng = np.random.default_rng(64)
+    codes, sbits, table = _int8_pool_case(rng, 2, 16, 2)
+    with pytest.raises(ValueError):
+        int8_rows_by_position(codes, np.zeros((2, 2, NUM_KV_HEADS, 16), np.uint16), table, [5, 5], 16)
