@@ -69,6 +69,9 @@ def parse_args():
                     help="paged workloads: override the page size (slots per page)")
     ap.add_argument("--q-tokens", type=int, default=0,
                     help="paged workloads: override the query tokens per request")
+    ap.add_argument("--scales-by-position", action="store_true",
+                    help="INT8 page pools: row scales indexed by position "
+                         "([batch, 2, 8, max_pages * page_size]) instead of beside their rows")
     ap.add_argument("--page-order", choices=("random", "ordered"), default="random",
                     help="paged workloads: the block table as drawn (a random permutation "
                          "of the pool) or each request's pages in pool order, as an "
@@ -135,7 +138,7 @@ def cpu_baseline_paged(inp, w, budget_s):
 
     from gqa_kv_cache_attn_amd.inputs import kv_slot_bytes, storage_bits
     from oracle import decode_int8_rows, decode_storage
-    from oracle.paged import gqa_decode_paged_reference
+    from oracle.paged import gqa_decode_multi, gqa_decode_paged_reference, int8_rows_by_position
 
     try:
         from threadpoolctl import threadpool_info
@@ -150,12 +153,23 @@ def cpu_baseline_paged(inp, w, budget_s):
         n = -(-L // P)
         ids = inp["block_table"][b, :n].long()
         pages = storage_bits(inp["kv_pages"].index_select(0, ids))   # D2H copies are not timed
-        sc = storage_bits(inp["kv_scales"].index_select(0, ids)) if w.kv_dtype == "int8" else None
+        by_pos = inp.get("scales_by_position", False)
+        if w.kv_dtype != "int8":
+            sc = None
+        elif by_pos:
+            sc = storage_bits(inp["kv_scales"][b:b + 1, :, :, :n * P])
+        else:
+            sc = storage_bits(inp["kv_scales"].index_select(0, ids))
         qb = storage_bits(inp["q"][b:b + 1])
         t0 = time.perf_counter()
-        dec = decode_int8_rows(pages, sc) if sc is not None else decode_storage(pages, w.kv_dtype)
-        out = gqa_decode_paged_reference(decode_storage(qb, w.q_dtype), dec, np.arange(n)[None, :],
-                                         [L], P, w.q_scale, w.k_scale, w.v_scale)
+        q = decode_storage(qb, w.q_dtype)
+        if by_pos:
+            rows = int8_rows_by_position(pages, sc, np.arange(n)[None, :], [L], P)
+            out = gqa_decode_multi(q, rows, [L], w.q_scale, w.k_scale, w.v_scale)
+        else:
+            dec = decode_int8_rows(pages, sc) if sc is not None else decode_storage(pages, w.kv_dtype)
+            out = gqa_decode_paged_reference(q, dec, np.arange(n)[None, :], [L], P, w.q_scale,
+                                             w.k_scale, w.v_scale)
         spent += time.perf_counter() - t0
         assert np.all(np.isfinite(out))
         nbytes += L * 8 * kv_slot_bytes(w.kv_dtype) + w.q_tokens * w.num_q_heads * 128 * 4
@@ -237,6 +251,9 @@ def _workload(args, name):
         B, C, lo, hi = (int(x) for x in args.shape.split(","))
         w = dataclasses.replace(w, batch=B, capacity=C, len_lo=lo, len_hi=hi,
                                 name=f"{w.name}[B={B},C={C},L={lo}..{hi}]")
+    if args.scales_by_position and not (w.page_size and w.kv_dtype == "int8"):
+        print("--scales-by-position applies to INT8 paged workloads only", file=sys.stderr)
+        sys.exit(2)
     if args.page_size or args.q_tokens or args.page_order != "random":
         if not w.page_size:
             print("--page-size / --q-tokens / --page-order apply to paged workloads only",
@@ -247,24 +264,31 @@ def _workload(args, name):
                                 name=f"{w.name}[P={args.page_size or w.page_size},"
                                      f"T={args.q_tokens or w.q_tokens}]"
                                      + ("[pages in order]" if args.page_order == "ordered" else ""))
+    if args.scales_by_position:
+        w = dataclasses.replace(w, name=f"{w.name}[scales by position]")
     return w
 
 
 class Case:
     """One workload's inputs in HBM and its prepared decode step."""
 
-    def __init__(self, w, dev, num_splits=0, fused_combine=False, page_order="random"):
+    def __init__(self, w, dev, num_splits=0, fused_combine=False, page_order="random",
+                 scales_by_position=False):
         import torch
 
         from gqa_kv_cache_attn_amd import binding as b
-        from gqa_kv_cache_attn_amd.inputs import make_inputs, make_paged_inputs
+        from gqa_kv_cache_attn_amd.inputs import make_inputs, make_paged_inputs, position_scales
         self.w, self.dev, self.b = w, dev, b
         self.paged = w.page_size > 0
+        self.by_position = scales_by_position
         inp = make_paged_inputs(w, device=dev) if self.paged else make_inputs(w, device=dev)
         if self.paged and page_order == "ordered":
             B, max_pages = inp["block_table"].shape
             inp["block_table"] = torch.arange(B * max_pages, device=dev,
                                               dtype=torch.int32).reshape(B, max_pages)
+        if scales_by_position:   # the same scales, moved to the slots that read them
+            inp["kv_scales"] = position_scales(inp["kv_scales"], inp["block_table"], w.page_size)
+            inp["scales_by_position"] = True
         self.inp = inp
         self.lens = inp["seq_lens"].cpu().tolist()
         self.nbytes = algorithmic_bytes(self.lens, w.kv_dtype, w.batch, w.num_q_heads,
@@ -277,7 +301,8 @@ class Case:
             self.prep = b.prepare_gqa_decode_paged(
                 inp["q"], inp["kv_pages"], inp["block_table"], inp["seq_lens"], self.out,
                 inp["q_scale"], num_splits=num_splits, k_scale=inp["k_scale"],
-                v_scale=inp["v_scale"], kv_scales=inp["kv_scales"])
+                v_scale=inp["v_scale"], kv_scales=inp["kv_scales"],
+                scales_by_position=scales_by_position)
         elif w.kv_dtype == "int8":
             self.prep = b.prepare_gqa_decode_int8(
                 inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], self.out, inp["q_scale"],
@@ -493,7 +518,8 @@ def run(args, dev, arch, stream):
             configs[name] = measure_config(name, args, dev, stream, 10 * (i + 1))
 
     print(f"[bench] device {arch}; workload {w.name}; generating inputs", file=sys.stderr, flush=True)
-    case = Case(w, dev, args.num_splits, args.fused_combine, args.page_order)
+    case = Case(w, dev, args.num_splits, args.fused_combine, args.page_order,
+                args.scales_by_position)
     paged, inp, out, nbytes, lens = case.paged, case.inp, case.out, case.nbytes, case.lens
     plan = dict(case.plan)
     if plan.get("fused_merge"):
@@ -560,7 +586,8 @@ def run(args, dev, arch, stream):
         if paged:
             b.gqa_decode_paged(inp["q"], inp["kv_pages"], inp["block_table"], inp["seq_lens"],
                                inp["q_scale"], out, k_scale=inp["k_scale"], v_scale=inp["v_scale"],
-                               kv_scales=inp["kv_scales"])
+                               kv_scales=inp["kv_scales"],
+                               scales_by_position=args.scales_by_position)
         elif w.kv_dtype == "int8":
             b.gqa_decode_int8(inp["q"], inp["kv"], inp["kv_scales"], inp["seq_lens"], inp["q_scale"],
                               out, k_scale=inp["k_scale"], v_scale=inp["v_scale"])
@@ -592,7 +619,8 @@ def run(args, dev, arch, stream):
         def append():
             b.gqa_kv_append_paged_int8(inp["kv_pages"], inp["kv_scales"], inp["block_table"],
                                        k_new, v_new, slots, inp["k_scale"], inp["v_scale"],
-                                       num_q_heads=w.num_q_heads)
+                                       num_q_heads=w.num_q_heads,
+                                       scales_by_position=args.scales_by_position)
     elif paged:
         def append():
             b.gqa_kv_append_paged(inp["kv_pages"], inp["block_table"], k_new, v_new, slots,
@@ -652,6 +680,7 @@ def run(args, dev, arch, stream):
                  .get(w.kv_dtype, w.kv_dtype),
         "data": "synthetic",
         "config": {**w.describe(), **({"page_order": args.page_order} if paged else {}),
+                   **({"scales_by_position": True} if args.scales_by_position else {}),
                    "seq_lens_sum": int(sum(lens)),
                    "algorithmic_bytes_per_step": nbytes, "plan": plan},
         "pct_of_peak": round(100 * value / PEAK_HBM_GBPS, 2),

@@ -30,6 +30,7 @@ GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_ALIAS, GQA_ERR_UNSUPPORTED_DEVICE = 0, 1, 2
 GQA_ERR_CAPTURE, GQA_ERR_OUT_OF_MEMORY, GQA_ERR_HIP = 4, 5, 6
 GQA_F16, GQA_BF16, GQA_FP8_E4M3, GQA_INT8_ROWSCALE = 0, 1, 2, 3
 GQA_FLAG_FUSED_COMBINE = 1
+GQA_PAGED_SCALES_BY_POSITION = 2
 NUM_Q_HEADS, NUM_KV_HEADS, HEAD_DIM = 32, 8, 128
 NUM_Q_HEADS_2TO1 = 16
 
@@ -351,9 +352,11 @@ def prepare_gqa_decode_int8(q: torch.Tensor, kv: torch.Tensor, kv_scales: torch.
 
 
 def make_paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.Tensor,
-                    k_scale: float = 1.0, v_scale: float = 1.0) -> GqaPagedDesc:
+                    k_scale: float = 1.0, v_scale: float = 1.0,
+                    scales_by_position: bool = False) -> GqaPagedDesc:
     """q [batch, T, Hq, 128]; kv_pages [num_pages, 2, 8, page_size, 128];
-    block_table [batch, max_pages] int32."""
+    block_table [batch, max_pages] int32. scales_by_position: an int8 pool's
+    row scales are [batch, 2, 8, max_pages * page_size]."""
     if q.dim() != 4 or kv_pages.dim() != 5 or block_table.dim() != 2:
         raise ValueError("q must be [batch, T, Hq, 128], kv_pages [num_pages, 2, 8, page_size, 128] "
                          "and block_table [batch, max_pages]")
@@ -363,11 +366,20 @@ def make_paged_desc(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch.
     return GqaPagedDesc(batch=q.shape[0], q_tokens=q.shape[1], num_q_heads=q.shape[2],
                         num_kv_heads=kv_pages.shape[2], head_dim=q.shape[3],
                         q_dtype=_dtype_code(q, "q"), kv_dtype=_dtype_code(kv_pages, "kv"),
-                        k_scale=k_scale, v_scale=v_scale, flags=0, page_size=kv_pages.shape[3],
-                        num_pages=kv_pages.shape[0], max_pages=block_table.shape[1])
+                        k_scale=k_scale, v_scale=v_scale,
+                        flags=GQA_PAGED_SCALES_BY_POSITION if scales_by_position else 0,
+                        page_size=kv_pages.shape[3], num_pages=kv_pages.shape[0],
+                        max_pages=block_table.shape[1])
 
 
-def _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out):
+def _paged_scale_shape(kv_pages, block_table, scales_by_position):
+    """Shape of an int8 pool's row scales in the chosen layout."""
+    if scales_by_position:
+        return (block_table.shape[0], 2, NUM_KV_HEADS, block_table.shape[1] * kv_pages.shape[3])
+    return tuple(kv_pages.shape[:4])
+
+
+def _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out, scales_by_position=False):
     if block_table.dtype != torch.int32:
         raise ValueError("block_table must be int32")
     _check_per_request(seq_lens, q.shape[0] if q.dim() > 0 else -1, "seq_lens")
@@ -383,9 +395,12 @@ def _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out):
                          f"{tuple(q.shape)} and kv_pages {tuple(kv_pages.shape)}")
     if (kv_scales is None) != (kv_pages.dtype != torch.int8):
         raise ValueError("kv_scales is required for (and only for) an int8 page pool")
+    if scales_by_position and kv_scales is None:
+        raise ValueError("scales_by_position needs an int8 page pool and its kv_scales")
+    want = _paged_scale_shape(kv_pages, block_table, scales_by_position)
     if kv_scales is not None and (kv_scales.dtype != torch.bfloat16 or
-                                  tuple(kv_scales.shape) != tuple(kv_pages.shape[:4])):
-        raise ValueError(f"kv_scales must be bf16 {tuple(kv_pages.shape[:4])}")
+                                  tuple(kv_scales.shape) != want):
+        raise ValueError(f"kv_scales must be bf16 {want}")
     ts = [q, kv_pages, block_table, seq_lens, out] + ([kv_scales] if kv_scales is not None else [])
     _check_devices(*ts)
 
@@ -394,12 +409,12 @@ def gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_table: torch
                      seq_lens: torch.Tensor, q_scale: float = 1.0,
                      out: Optional[torch.Tensor] = None, k_scale: float = 1.0,
                      v_scale: float = 1.0, kv_scales: Optional[torch.Tensor] = None,
-                     stream=None) -> torch.Tensor:
+                     stream=None, scales_by_position: bool = False) -> torch.Tensor:
     """Decode (T query tokens per request, causal among themselves) over a page pool."""
     if out is None:
         out = torch.empty_like(q)
-    _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out)
-    desc = make_paged_desc(q, kv_pages, block_table, k_scale, v_scale)
+    _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out, scales_by_position)
+    desc = make_paged_desc(q, kv_pages, block_table, k_scale, v_scale, scales_by_position)
     with torch.cuda.device(q.device):
         st = _decode_paged(ctypes.byref(desc), _ptr(q), _ptr(kv_pages), _ptr(kv_scales),
                            _ptr(block_table), _ptr(seq_lens), q_scale, _ptr(out),
@@ -412,10 +427,11 @@ def prepare_gqa_decode_paged(q: torch.Tensor, kv_pages: torch.Tensor, block_tabl
                              seq_lens: torch.Tensor, out: torch.Tensor, q_scale: float = 1.0,
                              num_splits: Optional[int] = None, k_scale: float = 1.0,
                              v_scale: float = 1.0,
-                             kv_scales: Optional[torch.Tensor] = None) -> GqaPrepared:
+                             kv_scales: Optional[torch.Tensor] = None,
+                             scales_by_position: bool = False) -> GqaPrepared:
     """Prepare a paged decode step (workspace allocated once, outside capture)."""
-    _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out)
-    desc = make_paged_desc(q, kv_pages, block_table, k_scale, v_scale)
+    _check_paged(q, kv_pages, kv_scales, block_table, seq_lens, out, scales_by_position)
+    desc = make_paged_desc(q, kv_pages, block_table, k_scale, v_scale, scales_by_position)
     h = _vp()
     with torch.cuda.device(q.device):
         st = _prepare_paged(ctypes.byref(desc), _ptr(q), _ptr(kv_pages), _ptr(kv_scales),
@@ -533,11 +549,12 @@ def gqa_kv_append_int8(kv: torch.Tensor, kv_scales: torch.Tensor, k_new: torch.T
 def gqa_kv_append_paged_int8(kv_pages: torch.Tensor, kv_scales: torch.Tensor,
                              block_table: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                              positions: torch.Tensor, k_scale: float = 1.0, v_scale: float = 1.0,
-                             num_q_heads: int = NUM_Q_HEADS_2TO1, stream=None) -> torch.Tensor:
+                             num_q_heads: int = NUM_Q_HEADS_2TO1, stream=None,
+                             scales_by_position: bool = False) -> torch.Tensor:
     """Quantise k_new/v_new [batch, T, 8, 128] row by row into an int8 page pool
     kv_pages [num_pages, 2, 8, page_size, 128] and its bf16 row scales kv_scales
-    [num_pages, 2, 8, page_size] at slots positions[b] + t through block_table;
-    returns kv_pages."""
+    [num_pages, 2, 8, page_size] (scales_by_position: [batch, 2, 8, max_pages *
+    page_size]) at slots positions[b] + t through block_table; returns kv_pages."""
     if block_table.dtype != torch.int32:
         raise ValueError("block_table must be int32")
     _check_per_request(positions, k_new.shape[0] if k_new.dim() > 0 else -1, "positions")
@@ -547,18 +564,22 @@ def gqa_kv_append_paged_int8(kv_pages: torch.Tensor, kv_scales: torch.Tensor,
         raise ValueError("k_new and v_new must have the same shape and dtype")
     if k_new.dim() != 4 or kv_pages.dim() != 5 or block_table.dim() != 2 or \
             block_table.shape[0] != k_new.shape[0] or kv_pages.shape[1] != 2 or \
-            tuple(kv_scales.shape) != tuple(kv_pages.shape[:4]):
+            tuple(kv_scales.shape) != _paged_scale_shape(kv_pages, block_table,
+                                                         scales_by_position):
         raise ValueError("k_new/v_new must be [batch, T, 8, 128], kv_pages "
                          "[num_pages, 2, 8, page_size, 128], kv_scales [num_pages, 2, 8, page_size] "
-                         "and block_table [batch, max_pages]")
+                         "(by position: [batch, 2, 8, max_pages * page_size]) and block_table "
+                         "[batch, max_pages]")
     if kv_pages.shape[2] != k_new.shape[2] or kv_pages.shape[4] != k_new.shape[3]:
         raise ValueError("kv_pages and k_new disagree on KV heads or head_dim")
     _check_devices(kv_pages, kv_scales, block_table, k_new, v_new, positions)
     desc = GqaPagedDesc(batch=k_new.shape[0], q_tokens=k_new.shape[1], num_q_heads=num_q_heads,
                         num_kv_heads=k_new.shape[2], head_dim=k_new.shape[3],
                         q_dtype=_dtype_code(k_new, "q"), kv_dtype=GQA_INT8_ROWSCALE,
-                        k_scale=k_scale, v_scale=v_scale, flags=0, page_size=kv_pages.shape[3],
-                        num_pages=kv_pages.shape[0], max_pages=block_table.shape[1])
+                        k_scale=k_scale, v_scale=v_scale,
+                        flags=GQA_PAGED_SCALES_BY_POSITION if scales_by_position else 0,
+                        page_size=kv_pages.shape[3], num_pages=kv_pages.shape[0],
+                        max_pages=block_table.shape[1])
     with torch.cuda.device(kv_pages.device):
         st = _append_paged_int8(ctypes.byref(desc), _ptr(k_new), _ptr(v_new), _ptr(positions),
                                 _ptr(block_table), _ptr(kv_pages), _ptr(kv_scales),

@@ -54,6 +54,7 @@ struct Paging {
   int32_t num_pages = 0;
   int32_t max_pages = 0;
   const int32_t* block_table = nullptr;
+  bool scales_by_position = false;   // INT8 pool: row scales [batch, 2, 8, capacity]
 };
 
 // Automatic split planning (measured on MI355X: ~1 MiB of K+V per chunk was
@@ -442,6 +443,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.page_shift = pg.page_shift;
   a.num_pages = pg.num_pages;
   a.q_tokens = pg.q_tokens;
+  a.scales_by_position = pg.scales_by_position ? 1 : 0;
   return a;
 }
 
@@ -722,9 +724,14 @@ gqa_status_t check_paged_desc(const gqa_paged_desc_t* pd, gqa_desc_t* d, Paging*
   if ((int64_t)pd->max_pages * P > GQA_MAX_CAPACITY)
     return fail(GQA_ERR_INVALID_ARG, "max_pages * page_size must be <= %d (got %lld)",
                 GQA_MAX_CAPACITY, (long long)pd->max_pages * P);
-  if (pd->flags != 0)
-    return fail(GQA_ERR_INVALID_ARG, "the paged entry points take no flags (got 0x%x)",
+  if ((pd->flags & ~GQA_PAGED_SCALES_BY_POSITION) != 0)
+    return fail(GQA_ERR_INVALID_ARG,
+                "the paged entry points take no flags but GQA_PAGED_SCALES_BY_POSITION (got 0x%x)",
                 (unsigned)pd->flags);
+  if ((pd->flags & GQA_PAGED_SCALES_BY_POSITION) && pd->kv_dtype != GQA_INT8_ROWSCALE)
+    return fail(GQA_ERR_INVALID_ARG,
+                "GQA_PAGED_SCALES_BY_POSITION needs an INT8_ROWSCALE pool (kv dtype %d)",
+                pd->kv_dtype);
   *d = gqa_desc_t{};
   d->batch = pd->batch;
   d->capacity = pd->max_pages * P;
@@ -750,6 +757,7 @@ gqa_status_t check_paged_desc(const gqa_paged_desc_t* pd, gqa_desc_t* d, Paging*
   pg->num_pages = pd->num_pages;
   pg->max_pages = pd->max_pages;
   pg->block_table = nullptr;
+  pg->scales_by_position = (pd->flags & GQA_PAGED_SCALES_BY_POSITION) != 0;
   return GQA_OK;
 }
 
@@ -757,6 +765,14 @@ gqa_status_t check_paged_desc(const gqa_paged_desc_t* pd, gqa_desc_t* d, Paging*
 size_t pool_bytes_of(const gqa_paged_desc_t* pd) {
   return (size_t)pd->num_pages * 2 * GQA_NUM_KV_HEADS * (size_t)pd->page_size * GQA_HEAD_DIM *
          elem_bytes(pd->kv_dtype);
+}
+
+// Bytes of an INT8 pool's row scales, in the layout the flags select.
+size_t scale_bytes_of(const gqa_paged_desc_t* pd) {
+  const size_t per_head = (pd->flags & GQA_PAGED_SCALES_BY_POSITION)
+                              ? (size_t)pd->batch * (size_t)pd->max_pages * (size_t)pd->page_size
+                              : (size_t)pd->num_pages * (size_t)pd->page_size;
+  return per_head * 2 * GQA_NUM_KV_HEADS * 2;
 }
 
 // Checks a paged descriptor and a decode call's buffers (see check_paged_desc).
@@ -768,7 +784,6 @@ gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const v
   if (!scale_ok(q_scale))
     return fail(GQA_ERR_INVALID_ARG, "q_scale must be finite and > 0 (got %g)", (double)q_scale);
   const bool int8 = pd->kv_dtype == GQA_INT8_ROWSCALE;
-  const int P = pd->page_size;
   pg->block_table = table;
   if (pd->batch == 0) return GQA_OK;
   if (!q || !pool || !table || !lens || !out || (int8 && !scales))
@@ -786,9 +801,8 @@ gqa_status_t check_paged_args(const gqa_paged_desc_t* pd, const void* q, const v
   const size_t B = (size_t)pd->batch;
   const size_t q_bytes =
       B * (size_t)pd->q_tokens * (size_t)pd->num_q_heads * GQA_HEAD_DIM * elem_bytes(pd->q_dtype);
-  const size_t rows = (size_t)pd->num_pages * 2 * GQA_NUM_KV_HEADS * (size_t)P;
   const size_t pool_bytes = pool_bytes_of(pd);
-  const size_t sc_bytes = int8 ? rows * 2 : 0;
+  const size_t sc_bytes = int8 ? scale_bytes_of(pd) : 0;
   const size_t table_bytes = B * (size_t)pd->max_pages * sizeof(int32_t);
   if (ranges_overlap(out, q_bytes, q, q_bytes) || ranges_overlap(out, q_bytes, pool, pool_bytes) ||
       ranges_overlap(out, q_bytes, lens, B * sizeof(int32_t)) ||
@@ -895,8 +909,7 @@ gqa_status_t append_paged(const gqa_paged_desc_t* desc, const void* k_new, const
       ranges_overlap(kv_pages, pool_bytes, block_table, table_bytes))
     return fail(GQA_ERR_ALIAS, "kv_pages must not overlap k_new, v_new, positions or block_table");
   if (int8) {
-    const size_t sc_bytes =
-        (size_t)desc->num_pages * 2 * GQA_NUM_KV_HEADS * (size_t)desc->page_size * 2;
+    const size_t sc_bytes = scale_bytes_of(desc);
     if (ranges_overlap(kv_scales, sc_bytes, kv_pages, pool_bytes) ||
         ranges_overlap(kv_scales, sc_bytes, k_new, row_bytes) ||
         ranges_overlap(kv_scales, sc_bytes, v_new, row_bytes) ||
@@ -923,6 +936,7 @@ gqa_status_t append_paged(const gqa_paged_desc_t* desc, const void* k_new, const
   a.max_pages = desc->max_pages;
   a.page_shift = pg.page_shift;
   a.num_pages = desc->num_pages;
+  a.scales_by_position = pg.scales_by_position ? 1 : 0;
   hipError_t e = gqa::enqueue_kv_append(a, desc->q_dtype, desc->kv_dtype, stream);
   if (e != hipSuccess) return fail(GQA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -49,6 +49,8 @@ struct StepArgs {
   int32_t page_shift;        // log2(page_size)
   int32_t num_pages;
   int32_t q_tokens;          // T query tokens per request (q, out: [batch, T, Hq, 128]); 1 otherwise
+  int32_t scales_by_position;  // INT8 pool: kv_scales is [batch, 2, 8, capacity], indexed by
+                               // the request's slot instead of the page row
 };
 
 // Arguments of one KV append (one new token per request).
@@ -73,6 +75,8 @@ struct AppendArgs {
   int32_t max_pages = 0;
   int32_t page_shift = 0;
   int32_t num_pages = 0;
+  // INT8 pool: the row scales are [batch, 2, 8, capacity], indexed by slot.
+  int32_t scales_by_position = 0;
 };
 
 hipError_t enqueue_kv_append(const AppendArgs& args, int src_dtype, int kv_dtype, hipStream_t stream);

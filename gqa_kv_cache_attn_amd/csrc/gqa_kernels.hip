@@ -564,7 +564,13 @@ __global__ __launch_bounds__(256) void gqa_kv_append_kernel(AppendArgs a) {
       w[i >> 2] |= ((u32)(int)q & 0xffu) << (8 * (i & 3));
     }
     *reinterpret_cast<u32x2*>(static_cast<char*>(a.kv) + dst) = (u32x2){w[0], w[1]};
-    if (chunk == 0) static_cast<uint16_t*>(a.kv_scales)[dst_row] = (uint16_t)sb;
+    if (chunk == 0) {
+      const size_t scale_row =
+          a.scales_by_position
+              ? ((size_t)(b * 2 + plane) * kKvHeads + g) * (size_t)a.capacity + (size_t)pos
+              : dst_row;
+      static_cast<uint16_t*>(a.kv_scales)[scale_row] = (uint16_t)sb;
+    }
   } else {
     *reinterpret_cast<u32x4*>(static_cast<char*>(a.kv) + dst * 2) = in;
   }

@@ -8,7 +8,8 @@
 // block_table[b][j / page_size]. The pages name a paged-KV decode backend
 // (FreeToken Turing notes, change 2) without a layout; this one is the
 // library's reading. An INT8 pool carries its bf16 row scales as
-// [num_pages, 2, 8, page_size] (Orin Qwen3-VL doc, "INT8 KV cache").
+// [num_pages, 2, 8, page_size] (Orin Qwen3-VL doc, "INT8 KV cache"), or,
+// indexed by position, as [batch, 2, 8, max_pages * page_size].
 //
 // Queries. q and out are [batch, T, Hq, 128]: the T tokens are the last T of
 // the request's L slots, and token t attends slots j < L - T + 1 + t, so the
@@ -60,6 +61,8 @@ template <int KVT>
 struct PagedHead {
   const char* kv;
   const char* scales;
+  const char* ks_pos;   // scales indexed by position: this (request, KV head)'s K and V
+  const char* vs_pos;   // scale rows (null for the pool layout)
   const int32_t* table_row;
   int g, shift, num_pages, c1;
 
@@ -80,9 +83,16 @@ struct PagedHead {
     pl.c1 = nrows;
     pl.quads = true;   // pages hold multiples of 16 rows: scale quads are 8-byte aligned
     if constexpr (KVT == kI8) {
-      const size_t splane = (size_t)P * 2;
-      pl.ks = make_rsrc(scales + ((size_t)(page * 2 + 0) * kKvHeads + g) * splane, (u32)nrows * 2);
-      pl.vs = make_rsrc(scales + ((size_t)(page * 2 + 1) * kKvHeads + g) * splane, (u32)nrows * 2);
+      if (ks_pos != nullptr) {   // by position: the page's slots in the request's scale rows
+        pl.ks = make_rsrc(ks_pos + (size_t)page_start * 2, (u32)nrows * 2);
+        pl.vs = make_rsrc(vs_pos + (size_t)page_start * 2, (u32)nrows * 2);
+      } else {
+        const size_t splane = (size_t)P * 2;
+        pl.ks = make_rsrc(scales + ((size_t)(page * 2 + 0) * kKvHeads + g) * splane,
+                          (u32)nrows * 2);
+        pl.vs = make_rsrc(scales + ((size_t)(page * 2 + 1) * kKvHeads + g) * splane,
+                          (u32)nrows * 2);
+      }
     }
     return pl;
   }
@@ -109,7 +119,9 @@ struct PagedHead {
 // blocks, as the contiguous balanced kernel does, so each 128-byte line of a
 // scale plane is read once. 1: pages of at least 64 slots (a block lies in
 // one page); 2: pages of 16 or 32 slots (a block spans 4 or 2 pages; the
-// scale pool must fit 32-bit offsets). 0: the waves take interleaved tiles.
+// scale pool must fit 32-bit offsets); 3: scales indexed by position, any
+// page size (a block's scales are 128 contiguous bytes per plane). 0: the
+// waves take interleaved tiles.
 template <int QT, int KVT, int G, int kBlocks = 0, class Emit>
 __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, int c0, int c1,
                                              int L, PagedLds& lds, Emit&& emit) {
@@ -140,6 +152,15 @@ __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, in
   PagedHead<KVT> ph;
   ph.kv = static_cast<const char*>(a.kv);
   ph.scales = static_cast<const char*>(a.kv_scales);
+  ph.ks_pos = nullptr;
+  ph.vs_pos = nullptr;
+  if constexpr (KVT == kI8) {
+    if (a.scales_by_position) {
+      const size_t srow = (size_t)a.capacity * 2;
+      ph.ks_pos = ph.scales + ((size_t)(b * 2 + 0) * kKvHeads + g) * srow;
+      ph.vs_pos = ph.scales + ((size_t)(b * 2 + 1) * kKvHeads + g) * srow;
+    }
+  }
   ph.table_row = a.block_table + (size_t)b * a.max_pages;
   ph.g = g;
   ph.shift = a.page_shift;
@@ -166,13 +187,15 @@ __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, in
 #pragma unroll
   for (int c = 0; c < 8; ++c) st.o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (KVT == kI8 && kBlocks == 2) {
-    // Whole 64-slot blocks over pages of 16 or 32 slots: each of a block's
-    // four tiles gets the descriptors of its own page, and the block's row
-    // scales come from one 2-byte load per lane and plane through a
-    // descriptor over the whole scale pool, at the lane's page (slots at or
-    // past c1 get an offset past the pool: they read 0). Page ids come from
-    // the table four per block (its tiles' pages), sixteen blocks per load.
+  if constexpr (KVT == kI8 && (kBlocks == 2 || kBlocks == 3)) {
+    // Whole 64-slot blocks over pages of any size: each of a block's four
+    // tiles gets the descriptors of its own page, and the block's row scales
+    // come from one 2-byte load per lane and plane. Pool layout (2, pages of
+    // 16 or 32 slots): through a descriptor over the whole scale pool, at the
+    // lane's page (slots at or past c1 get an offset past the pool: they read
+    // 0). By position (3): through descriptors over the request's K and V
+    // scale rows, bounded at c1. Page ids come from the table four per block
+    // (its tiles' pages), sixteen blocks per load.
     int base = __builtin_amdgcn_readfirstlane(c0 + 64 * wave);
     if (base < c1) {
       u32x4* sk = lds.k[wave];
@@ -188,22 +211,39 @@ __device__ __forceinline__ void attend_paged(const StepArgs& a, int b, int g, in
       };
       int kb0 = 0;                                   // block held by lanes 0..3
       int ids = tile_ids(base0);
-      const u32 pool_bytes = (u32)a.num_pages * (u32)(2 * kKvHeads * 2) * (u32)P;
-      const __amdgpu_buffer_rsrc_t ks_pool = make_rsrc(ph.scales, pool_bytes);
-      // Byte offset of the K scale of slot bbase + lane (the V scale is one
-      // plane further on, + 8 P 2 bytes); past the pool when at or past c1.
+      __amdgpu_buffer_rsrc_t ks_src, vs_src;
+      if constexpr (kBlocks == 3) {
+        ks_src = make_rsrc(ph.ks_pos, (u32)c1 * 2);   // the K scale row, up to c1
+        vs_src = make_rsrc(ph.vs_pos, (u32)c1 * 2);
+      } else {
+        const u32 pool_bytes = (u32)a.num_pages * (u32)(2 * kKvHeads * 2) * (u32)P;
+        ks_src = make_rsrc(ph.scales, pool_bytes);
+        vs_src = ks_src;
+      }
+      // Byte offset of the K scale of slot bbase + lane. Pool layout: the V
+      // scale is one plane further on (+ 8 P 2 bytes), and slots at or past
+      // c1 get an offset past the pool. By position: the slot's offset in
+      // both rows (the descriptors end at c1).
       auto scale_offset = [&](int kb, int bbase) -> u32 {
-        const int page = __shfl(ids, 4 * (kb - kb0) + (lane >> 4));
         const int slot = bbase + lane;
-        return slot < c1 ? (u32)page * (u32)(2 * kKvHeads * 2 * P) + (u32)(g * 2 * P) +
-                               (u32)((slot & (P - 1)) * 2)
-                         : 0xffffffffu;
+        if constexpr (kBlocks == 3) {
+          return (u32)slot * 2u;
+        } else {
+          const int page = __shfl(ids, 4 * (kb - kb0) + (lane >> 4));
+          return slot < c1 ? (u32)page * (u32)(2 * kKvHeads * 2 * P) + (u32)(g * 2 * P) +
+                                 (u32)((slot & (P - 1)) * 2)
+                           : 0xffffffffu;
+        }
       };
       auto load_scales = [&](u32 off) -> BlockScales {
         BlockScales r;
-        r.k = __builtin_amdgcn_raw_buffer_load_b16(ks_pool, off, 0, kLoadAux);
-        r.v = __builtin_amdgcn_raw_buffer_load_b16(
-            ks_pool, off == 0xffffffffu ? off : off + (u32)(kKvHeads * 2 * P), 0, kLoadAux);
+        r.k = __builtin_amdgcn_raw_buffer_load_b16(ks_src, off, 0, kLoadAux);
+        if constexpr (kBlocks == 3) {
+          r.v = __builtin_amdgcn_raw_buffer_load_b16(vs_src, off, 0, kLoadAux);
+        } else {
+          r.v = __builtin_amdgcn_raw_buffer_load_b16(
+              ks_src, off == 0xffffffffu ? off : off + (u32)(kKvHeads * 2 * P), 0, kLoadAux);
+        }
         return r;
       };
       int kb = 0, row;
@@ -496,7 +536,8 @@ __global__ __launch_bounds__(kThreads) void gqa_paged_combine_kernel(StepArgs a)
 // workgroup w takes slabs [bound(w), bound(w + 1)); heads covered whole are
 // written directly, first and last pieces go to slots 2w and 2w + 1 of
 // kRowsMax rows each. kBlocks: see attend_paged (INT8 pools: 1 for pages of
-// at least 64 slots, 2 for pages of 16 or 32).
+// at least 64 slots, 2 for pages of 16 or 32, 3 for scales indexed by
+// position).
 template <int QT, int KVT, int G, int kBlocks>
 __global__ __launch_bounds__(kThreads, GQA_PAGED_MIN_WAVES_PER_SIMD) void
 gqa_paged_balanced_kernel(StepArgs a) {
@@ -618,8 +659,13 @@ hipError_t enqueue_paged_typed(const StepArgs& a, hipStream_t stream, hipEvent_t
     int blocks = 0;
     if constexpr (KVT == kI8) {
       const int64_t scale_pool = (int64_t)a.num_pages * (2 * kKvHeads * 2) << a.page_shift;
-      blocks = a.page_shift >= 6 ? 1 : (scale_pool < (int64_t)UINT32_MAX ? 2 : 0);
-      if (blocks == 1)
+      blocks = a.scales_by_position ? 3
+               : a.page_shift >= 6  ? 1
+                                    : (scale_pool < (int64_t)UINT32_MAX ? 2 : 0);
+      if (blocks == 3)
+        hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, 3>), dim3(a.grid_wgs),
+                           dim3(kThreads), 0, stream, a);
+      else if (blocks == 1)
         hipLaunchKernelGGL((gqa_paged_balanced_kernel<QT, KVT, G, 1>), dim3(a.grid_wgs),
                            dim3(kThreads), 0, stream, a);
       else if (blocks == 2)

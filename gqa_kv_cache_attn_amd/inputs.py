@@ -186,9 +186,11 @@ def _encode_block(x: torch.Tensor, w: Workload):
 
 def make_paged_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
                       seq_lens: Optional[torch.Tensor] = None, spare_pages: int = 5,
-                      pages_per_draw: int = 4096):
+                      pages_per_draw: int = 4096, scales_by_position: bool = False):
     """Draw one paged workload: q [B, T, Hq, 128], the pool [num_pages, 2, 8, P, 128]
-    (+ row scales for int8), block_table [B, max_pages] int32 and the lengths."""
+    (+ row scales for int8), block_table [B, max_pages] int32 and the lengths.
+    scales_by_position (int8): the same draw, with the row scales moved to
+    [B, 2, 8, max_pages * P] (position_scales)."""
     assert w.page_size > 0
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
@@ -221,9 +223,25 @@ def make_paged_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
         if scales is not None:
             scales[p0:p0 + n] = sc
         del x, vals, sc
+    if scales_by_position:
+        assert scales is not None, "scales_by_position needs an int8 pool"
+        scales = position_scales(scales, table, P)
     return {"q": q, "kv_pages": pool, "kv_scales": scales, "block_table": table,
             "seq_lens": lens, "q_scale": w.q_scale, "k_scale": w.k_scale, "v_scale": w.v_scale,
-            "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype, "page_size": P}
+            "q_dtype": w.q_dtype, "kv_dtype": w.kv_dtype, "page_size": P,
+            "scales_by_position": scales_by_position}
+
+
+def position_scales(kv_scales: torch.Tensor, block_table: torch.Tensor,
+                    page_size: int) -> torch.Tensor:
+    """An INT8 pool's row scales moved from the page layout [num_pages, 2, 8, P]
+    to the position layout [batch, 2, 8, max_pages * P]: the scale of request
+    b's slot j is the one stored beside that slot's row (table entries are
+    clamped into the pool, as the kernels clamp them)."""
+    B, max_pages = block_table.shape
+    ids = block_table.long().clamp(0, kv_scales.shape[0] - 1).reshape(-1)
+    g = kv_scales.index_select(0, ids).reshape(B, max_pages, 2, NUM_KV_HEADS, page_size)
+    return g.permute(0, 2, 3, 1, 4).reshape(B, 2, NUM_KV_HEADS, max_pages * page_size).contiguous()
 
 
 def storage_bits(t: torch.Tensor):

@@ -252,7 +252,10 @@ GQA_API gqa_status_t gqa_decode_no_alloc(const gqa_desc_t* desc, const void* q, 
  * Layouts (device memory):
  *   q           [batch, q_tokens, Hq, 128]       q_dtype, 16-byte aligned
  *   kv_pages    [num_pages, 2, 8, page_size, 128] kv_dtype (plane 0 = K), 16-byte aligned
- *   kv_scales   [num_pages, 2, 8, page_size]     bf16, INT8_ROWSCALE only (else NULL)
+ *   kv_scales   [num_pages, 2, 8, page_size]     bf16, INT8_ROWSCALE only (else NULL);
+ *               with GQA_PAGED_SCALES_BY_POSITION instead
+ *               [batch, 2, 8, max_pages * page_size]: the scale of request b's
+ *               slot j at [b, plane, g, j], whatever page holds the row
  *   block_table [batch, max_pages] int32: request b's slot j is row j % page_size of
  *               page block_table[b][j / page_size]; read on the device only
  *   seq_lens    [batch] int32, device only: L_b counts the q_tokens new slots
@@ -269,6 +272,16 @@ GQA_API gqa_status_t gqa_decode_no_alloc(const gqa_desc_t* desc, const void* q, 
 #define GQA_MAX_PAGE_SIZE (1 << 16)
 /* q_tokens x (query heads per KV head) may not exceed this (one MFMA tile). */
 #define GQA_PAGED_MAX_ROWS 16
+/* gqa_paged_desc_t.flags bit, INT8_ROWSCALE pools only: the row scales are
+ * indexed by position ([batch, 2, 8, max_pages * page_size], the contiguous
+ * INT8 cache's scale layout) instead of living beside their rows in the pool.
+ * The Orin Qwen3-VL doc ("INT8 KV cache") keeps one bf16 scale per (position,
+ * KV head) row without fixing where it is stored. With pages of 16 or 32
+ * slots, a head's scales for one page fill only 32 or 64 bytes of a 128-byte
+ * line in the pool layout, and the kernels fetch the whole line; indexed by
+ * position, each line holds 64 consecutive scales of one head. The decode
+ * and append entry points must be given the same layout. */
+#define GQA_PAGED_SCALES_BY_POSITION 2
 
 typedef struct gqa_paged_desc {
   int32_t batch;        /* >= 0; 0 makes every call a no-op */
@@ -280,7 +293,8 @@ typedef struct gqa_paged_desc {
   int32_t kv_dtype;     /* gqa_dtype_t, as for gqa_desc_t */
   float k_scale;        /* as for gqa_desc_t */
   float v_scale;
-  int32_t flags;        /* must be 0 (the one-launch merge is not offered here) */
+  int32_t flags;        /* 0, or GQA_PAGED_SCALES_BY_POSITION for an INT8_ROWSCALE pool
+                           (the one-launch merge is not offered here) */
   int32_t page_size;    /* slots per page: a power of two in [16, GQA_MAX_PAGE_SIZE] */
   int32_t num_pages;    /* pages in the pool, >= 1 */
   int32_t max_pages;    /* block_table row length, >= 1; max_pages * page_size <= GQA_MAX_CAPACITY */
@@ -381,9 +395,12 @@ GQA_API gqa_status_t gqa_kv_append_paged(const gqa_paged_desc_t* desc, const voi
 /* As gqa_kv_append_paged, for an INT8_ROWSCALE pool: each row is quantised
  * as in gqa_kv_append_int8 and its bf16 scale goes to row `s % page_size` of
  * page block_table[b][s / page_size] in kv_scales [num_pages, 2, 8,
- * page_size] (2-byte aligned; the layout gqa_decode_paged reads). kv_scales
- * must not overlap kv_pages, k_new, v_new, positions or block_table
- * (GQA_ERR_ALIAS); a non-INT8 descriptor is rejected (GQA_ERR_INVALID_ARG). */
+ * page_size] (2-byte aligned; the layout gqa_decode_paged reads), or, with
+ * GQA_PAGED_SCALES_BY_POSITION, to [b, plane, g, s] of kv_scales [batch, 2,
+ * 8, max_pages * page_size]. A token whose slot or page entry is skipped
+ * writes no scale either. kv_scales must not overlap kv_pages, k_new, v_new,
+ * positions or block_table (GQA_ERR_ALIAS); a non-INT8 descriptor is
+ * rejected (GQA_ERR_INVALID_ARG). */
 GQA_API gqa_status_t gqa_kv_append_paged_int8(const gqa_paged_desc_t* desc, const void* k_new,
                                               const void* v_new, const int32_t* positions,
                                               const int32_t* block_table, void* kv_pages,

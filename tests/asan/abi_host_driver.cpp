@@ -249,6 +249,14 @@ void paged() {
     d.flags = GQA_FLAG_FUSED_COMBINE;
     EXPECT(gqa_validate_args_paged(&d, Q, KV, nullptr, TABLE, LENS, 1.f, OUT, 0) ==
            GQA_ERR_INVALID_ARG);
+    d.flags = GQA_PAGED_SCALES_BY_POSITION;   // a bf16 pool has no scales to index
+    EXPECT(gqa_validate_args_paged(&d, Q, KV, nullptr, TABLE, LENS, 1.f, OUT, 0) ==
+           GQA_ERR_INVALID_ARG);
+    d = pdesc(4096, 2, 16, 1 << 20, 8192, GQA_INT8_ROWSCALE, 16);
+    d.flags = GQA_PAGED_SCALES_BY_POSITION;   // scales [4096, 2, 8, 131072]: 16 GiB
+    EXPECT(gqa_validate_args_paged(&d, Q, KV, SCALES, TABLE, LENS, 1.f, OUT, 0) == GQA_OK);
+    gqa_plan_t p;
+    EXPECT(gqa_plan_decode_paged(&d, 0, &p) == GQA_OK && p.route == 2);
   }
   for (int32_t P : {16, 64, 4096})
     for (int32_t B : {1, 3, 64, 4096})

@@ -148,7 +148,8 @@ def run_paged(inp, path="prepared", num_splits=None, out=None):
     if out is None:
         out = torch.empty_like(inp["q"])
     args = (inp["q"], inp["kv_pages"], inp["block_table"], inp["seq_lens"])
-    kw = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"], kv_scales=inp["kv_scales"])
+    kw = dict(k_scale=inp["k_scale"], v_scale=inp["v_scale"], kv_scales=inp["kv_scales"],
+              scales_by_position=inp.get("scales_by_position", False))
     if path == "convenience":
         b.gqa_decode_paged(*args, inp["q_scale"], out, **kw)
         torch.cuda.synchronize()
@@ -162,17 +163,22 @@ def run_paged(inp, path="prepared", num_splits=None, out=None):
 def paged_oracle_request(inp, b, seq_len=None):
     """Oracle output [T, Hq, 128] (fp64) of request b: its pages decoded from the
     stored bits and relabelled 0..n-1 (relabelling is a pinned invariance)."""
-    from oracle.paged import gqa_decode_paged_reference
+    from oracle.paged import gqa_decode_multi, gqa_decode_paged_reference, int8_rows_by_position
     P = inp["page_size"]
     L = int(inp["seq_lens"][b]) if seq_len is None else seq_len
     n = max(1, -(-L // P))
     ids = inp["block_table"][b, :n].long()
     pages = inp["kv_pages"].index_select(0, ids)
+    q = decode_storage(storage_bits(inp["q"][b:b + 1]), inp["q_dtype"])
+    if inp.get("scales_by_position"):
+        # the scales stay with the request's positions: slots 0 .. n P - 1
+        rows = int8_rows_by_position(storage_bits(pages), storage_bits(inp["kv_scales"][b:b + 1, :, :, :n * P]),
+                                     np.arange(n)[None, :], [L], P)
+        return gqa_decode_multi(q, rows, [L], inp["q_scale"], inp["k_scale"], inp["v_scale"])[0]
     if inp["kv_dtype"] == "int8":
         dec = decode_int8_rows(storage_bits(pages), storage_bits(inp["kv_scales"].index_select(0, ids)))
     else:
         dec = decode_storage(storage_bits(pages), inp["kv_dtype"])
-    q = decode_storage(storage_bits(inp["q"][b:b + 1]), inp["q_dtype"])
     ref = gqa_decode_paged_reference(q, dec, np.arange(n)[None, :], [L], P, inp["q_scale"],
                                      inp["k_scale"], inp["v_scale"])
     return ref[0]

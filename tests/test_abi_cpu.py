@@ -364,12 +364,47 @@ def test_paged_other_descriptor_checks():
     assert vp(pdesc(max_pages=0)) == INVALID
     assert vp(pdesc(P=1 << 16, max_pages=65)) == INVALID          # > GQA_MAX_CAPACITY slots
     assert vp(pdesc(flags=1)) == INVALID                            # no one-launch merge here
+    assert vp(pdesc(flags=8)) == INVALID
     assert vp(pdesc(ks=0.5)) == INVALID                             # scale on a 16-bit pool
     assert vp(pdesc(kv=b.GQA_INT8_ROWSCALE, hq=16)) == INVALID      # int8 needs its scales
     assert vp(pdesc(), sc=5 * 1024 * MiB) == INVALID                # scales only for int8
     assert vp(pdesc(), table=None) == INVALID
     assert vp(pdesc(), table=TABLE + 2) == INVALID                  # 4-byte alignment
     assert vp(pdesc(), qs=0.0) == INVALID
+
+
+def test_paged_scales_by_position_flag_is_int8_only_and_sizes_the_scales():
+    """GQA_PAGED_SCALES_BY_POSITION: accepted only with an INT8 pool; the
+    scales then span batch * 2 * 8 * max_pages * page_size bf16 values, and
+    out may not overlap them."""
+    POS = b.GQA_PAGED_SCALES_BY_POSITION
+    SCALES = 5 * 1024 * MiB
+    d = pdesc(batch=2, kv=b.GQA_INT8_ROWSCALE, hq=16, T=2, P=16, num_pages=100, max_pages=8,
+              flags=POS)
+    assert vp(d, sc=SCALES) == OK
+    assert vp(pdesc(flags=POS)) == INVALID and "INT8" in b.last_error()        # bf16 pool
+    assert vp(pdesc(kv=b.GQA_FP8_E4M3, ks=0.5, vs=0.5, flags=POS)) == INVALID
+    assert vp(pdesc(kv=b.GQA_INT8_ROWSCALE, hq=16, flags=4), sc=SCALES) == INVALID
+    assert vp(pdesc(kv=b.GQA_INT8_ROWSCALE, hq=16, flags=POS | 1), sc=SCALES) == INVALID
+    by_pos = 2 * 2 * 8 * 8 * 16 * 2        # [batch, 2, 8, max_pages * page_size] bf16
+    in_pool = 100 * 2 * 8 * 16 * 2         # [num_pages, 2, 8, page_size] bf16
+    assert by_pos < in_pool
+    assert vp(d, sc=SCALES, out=SCALES + by_pos - 16) == ALIAS
+    assert vp(d, sc=SCALES, out=SCALES + by_pos) == OK
+    d0 = pdesc(batch=2, kv=b.GQA_INT8_ROWSCALE, hq=16, T=2, P=16, num_pages=100, max_pages=8)
+    assert vp(d0, sc=SCALES, out=SCALES + by_pos) == ALIAS       # the pool layout is larger
+    assert vp(d0, sc=SCALES, out=SCALES + in_pool) == OK
+    # the append takes the same flag and the same size
+    app = b._append_paged_int8
+    K, V, POSN = 1 << 30, 3 << 30, 4 << 30
+    pool = POOL
+
+    def call(desc_, sc=SCALES, pos=POSN):
+        return app(ctypes.byref(desc_), K, V, pos, TABLE, pool, sc, None)
+
+    assert call(d, pos=SCALES + by_pos - 4) == ALIAS
+    assert call(d, pos=SCALES + by_pos) not in (INVALID, ALIAS)
+    assert call(pdesc(flags=POS)) == INVALID
 
 
 def test_paged_aliasing_by_address_range():
