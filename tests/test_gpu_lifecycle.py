@@ -79,7 +79,7 @@ def test_convenience_call_refuses_to_allocate_inside_capture():
     plan = b.gqa_plan(b.make_desc(inp["q"], inp["kv"]))
     assert plan["workspace_bytes"] > 0
     x = torch.zeros(4, device="cuda")
-    stream = torch.cuda.Stream()        # fresh stream: its workspace cache is empty
+    stream = torch.cuda.Stream()   # no convenience call has used this pooled stream yet
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         with pytest.raises(b.GqaError) as ei:
@@ -103,6 +103,9 @@ def test_convenience_call_under_capture_takes_two_launches_when_counters_are_dir
     assert b.gqa_plan(b.make_desc(small["q"], small["kv"]))["fused_merge"] == 1
     out_big, eager, replayed = (torch.empty_like(x["q"]) for x in (big, small, small))
     stream = torch.cuda.Stream()
+    # torch's pooled streams do not wait for the default stream, where the
+    # inputs were just drawn
+    stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
         b.gqa_decode(big["q"], big["kv"], big["seq_lens"], big["q_scale"], out_big)
         b.gqa_decode(small["q"], small["kv"], small["seq_lens"], small["q_scale"], eager)
