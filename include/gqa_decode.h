@@ -165,8 +165,11 @@ typedef struct gqa_prepared gqa_prepared_t;
  * same stream are ordered and may share the cache. Calls from several host
  * threads are safe: the cache lookup, any growth (which synchronises the
  * stream before freeing the old buffer) and the enqueue happen under one
- * lock, so no call launches with a buffer another call has freed. The
- * prepared pair below is the capture-safe interface. */
+ * lock, so no call launches with a buffer another call has freed. Entries
+ * live until the process ends and are keyed by the stream handle: a stream
+ * created later with the same handle value reuses the entry, so synchronise a
+ * stream before destroying it. The prepared pair below is the capture-safe
+ * interface. */
 GQA_API gqa_status_t gqa_decode(const gqa_desc_t* desc, const void* q, const void* kv,
                                 const int32_t* seq_lens, float q_scale, void* out,
                                 hipStream_t stream);
