@@ -123,13 +123,12 @@ int device_cus(int dev) {
 // and by parity (odd workgroups run on odd-numbered XCDs). Measured on MI355X
 // with equal shares (per-workgroup timestamps, 64k bf16 and 128k fp8
 // workloads): the second and third workgroup of each CU took 1.1-1.2x and
-// 1.25-1.45x as long as the first, and workgroups on odd XCDs 1.07-1.1x as
-// long as on even ones, reproducibly from launch to launch and whatever
-// slabs they read. These defaults (a sweep of five sets) lift the long-context
-// kernels by 1-3 points of HBM peak. With two workgroups per CU the second
-// is barely slower: a sweep of its share (780-960) was fastest at 960 on
-// both workloads (0.4-0.7% over 840). Build-time knobs; shares only move
-// range boundaries, never the result's correctness.
+// 1.25-1.45x as long as the first, whatever slabs they read; the tier shares
+// (a sweep of five sets) lift the long-context kernels by 1-3 points of HBM
+// peak. With two workgroups per CU the second is barely slower: a sweep of
+// its share (780-960) was fastest at 960 on both workloads (0.4-0.7% over
+// 840). Build-time knobs; shares only move range boundaries, never the
+// result's correctness.
 #ifndef GQA_SHARE_TIER1
 #define GQA_SHARE_TIER1 840
 #endif
@@ -142,24 +141,28 @@ int device_cus(int dev) {
 #ifndef GQA_SHARE_TIER3
 #define GQA_SHARE_TIER3 670
 #endif
+// Odd-XCD share with two or three workgroups per CU, contiguous and paged.
+// Interleaved A/B runs on five boxes (three alternating samples per variant
+// and box) improved every long workload monotonically from 920 up to
+// 1000-1060: 128k fp8 -2.1%, 128k INT8 -2.5%, 64k bf16 -1.9%, the ragged
+// batch -2.3%, the fp8 / INT8 / bf16 page pools -2.9 / -2.6 / -1.6% at 1060;
+// 1100 was about as fast and 1150-1300 slower again.
 #ifndef GQA_SHARE_ODD
-#define GQA_SHARE_ODD 920
+#define GQA_SHARE_ODD 1060
 #endif
-// The paged kernel at two workgroups per CU takes the same odd-XCD share: a
-// sweep on one box favoured 860 by 1.2-1.3% on the 16-slot bf16 and 64-slot
-// fp8 pools, but on a second box 920 was 1.1-1.2% faster on both (three
-// alternating samples each), so the difference is within the spread between
-// boxes and one share serves both kernels.
-#ifndef GQA_SHARE_ODD_PAGED_TWO
-#define GQA_SHARE_ODD_PAGED_TWO GQA_SHARE_ODD
+// With one workgroup per CU (single requests, small caches) the same sweep
+// was mixed (bf16 and fp8 1-2% faster at 1000-1100, INT8 1% slower), so
+// those grids keep the earlier share.
+#ifndef GQA_SHARE_ODD_ONE_PER_CU
+#define GQA_SHARE_ODD_ONE_PER_CU 920
 #endif
 
 // a.grid_wgs must be set: the shares depend on how many workgroups share a CU.
-void set_shares(gqa::StepArgs& a, int tier_size, bool paged) {
+void set_shares(gqa::StepArgs& a, int tier_size) {
   int tier[gqa::kShareTiers] = {1000, GQA_SHARE_TIER1, GQA_SHARE_TIER2, GQA_SHARE_TIER3};
   const bool two = tier_size > 0 && a.grid_wgs == 2 * tier_size;
   if (two) tier[1] = GQA_SHARE_TIER1_OF_TWO;
-  const int odd = paged && two ? GQA_SHARE_ODD_PAGED_TWO : GQA_SHARE_ODD;
+  const int odd = tier_size > 0 && a.grid_wgs > tier_size ? GQA_SHARE_ODD : GQA_SHARE_ODD_ONE_PER_CU;
   // tier_size 0 (unknown) or a grid of one tier: plain equal shares
   a.tier_size = tier_size > 0 ? tier_size : (1 << 28);
   for (int t = 0; t < gqa::kShareTiers; ++t) {
@@ -428,7 +431,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.head_pieces = a.slab_prefix ? a.slab_prefix + d->batch + 1 : nullptr;
   a.fused_combine = p.fused_merge;
   a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
-  set_shares(a, tier_size, pg.on);
+  set_shares(a, tier_size);
   a.batch = d->batch;
   a.capacity = d->capacity;
   a.num_splits = p.num_splits;
