@@ -150,19 +150,25 @@ int device_cus(int dev) {
 #ifndef GQA_SHARE_ODD
 #define GQA_SHARE_ODD 1060
 #endif
-// With one workgroup per CU (single requests, small caches) the same sweep
-// was mixed (bf16 and fp8 1-2% faster at 1000-1100, INT8 1% slower), so
-// those grids keep the earlier share.
+// With one workgroup per CU (single requests and small 16-bit or INT8
+// caches; fp8 keeps two per CU) a bf16 request of 100k slots ran 1.7-1.8%
+// faster at 1000 than at 920 on two boxes, while INT8 ran 0.6-0.9% slower,
+// so 16-bit grids take 1000 there and INT8 grids keep 920.
 #ifndef GQA_SHARE_ODD_ONE_PER_CU
-#define GQA_SHARE_ODD_ONE_PER_CU 920
+#define GQA_SHARE_ODD_ONE_PER_CU 1000
+#endif
+#ifndef GQA_SHARE_ODD_ONE_PER_CU_INT8
+#define GQA_SHARE_ODD_ONE_PER_CU_INT8 920
 #endif
 
 // a.grid_wgs must be set: the shares depend on how many workgroups share a CU.
-void set_shares(gqa::StepArgs& a, int tier_size) {
+void set_shares(gqa::StepArgs& a, int tier_size, int kv_dtype) {
   int tier[gqa::kShareTiers] = {1000, GQA_SHARE_TIER1, GQA_SHARE_TIER2, GQA_SHARE_TIER3};
   const bool two = tier_size > 0 && a.grid_wgs == 2 * tier_size;
   if (two) tier[1] = GQA_SHARE_TIER1_OF_TWO;
-  const int odd = tier_size > 0 && a.grid_wgs > tier_size ? GQA_SHARE_ODD : GQA_SHARE_ODD_ONE_PER_CU;
+  const int odd = tier_size > 0 && a.grid_wgs > tier_size ? GQA_SHARE_ODD
+                  : kv_dtype == GQA_INT8_ROWSCALE       ? GQA_SHARE_ODD_ONE_PER_CU_INT8
+                                                        : GQA_SHARE_ODD_ONE_PER_CU;
   // tier_size 0 (unknown) or a grid of one tier: plain equal shares
   a.tier_size = tier_size > 0 ? tier_size : (1 << 28);
   for (int t = 0; t < gqa::kShareTiers; ++t) {
@@ -431,7 +437,7 @@ gqa::StepArgs step_args(const gqa_desc_t* d, const void* q, const void* kv, cons
   a.head_pieces = a.slab_prefix ? a.slab_prefix + d->batch + 1 : nullptr;
   a.fused_combine = p.fused_merge;
   a.grid_wgs = p.route == 2 ? p.num_workgroups : 0;
-  set_shares(a, tier_size);
+  set_shares(a, tier_size, d->kv_dtype);
   a.batch = d->batch;
   a.capacity = d->capacity;
   a.num_splits = p.num_splits;
