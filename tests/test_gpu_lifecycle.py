@@ -1,7 +1,7 @@
 """GPU lifecycle of the prepared API: hipGraph capture and replay with lengths
 rewritten in place, the convenience call's refusal to allocate inside a
-capture, two handles on concurrent streams, guard bands, and error paths
-that must leave the output untouched."""
+capture, two handles on concurrent streams, guard bands, error paths that
+must leave the output untouched, and the timed launch."""
 
 import pytest
 import torch
@@ -237,4 +237,47 @@ def test_balanced_grid_follows_the_problem_size(kd, hq, B, C, one_per_cu):
     torch.cuda.synchronize()
     pairs = [(b, g) for b in range(B) for g in range(8)][:16]
     compare(out, oracle_pairs(inp, pairs), inp, f"grid {W} {kd} B={B} C={C}")
+    prep.destroy()
+
+
+@pytest.mark.parametrize("plan", ["balanced", "chunked", "one_launch", "paged"])
+def test_timed_launch_gives_the_same_bits_with_its_events_in_order(plan):
+    """launch_gqa_decode_prepared_timed, which bench times the attention kernel
+    with: the same output as the plain launch, bit for bit; its three events
+    recorded in stream order (start, after the attention kernel, end); and any
+    of them may be left out."""
+    from gqa_kv_cache_attn_amd.inputs import make_paged_inputs
+    b = binding()
+    if plan == "paged":
+        w = Workload("life_timed_paged", 3, 4096, 1, 4096, "bf16", "bf16", q_scale=0.8, seed=77,
+                     page_size=16, q_tokens=2)
+        inp = make_paged_inputs(w, device="cuda")
+        out = torch.full_like(inp["q"], float("nan"))
+        prep = b.prepare_gqa_decode_paged(inp["q"], inp["kv_pages"], inp["block_table"],
+                                          inp["seq_lens"], out, inp["q_scale"])
+    else:
+        inp = _inputs(B=1, C=1024, seed=78) if plan == "one_launch" else _inputs(seed=79)
+        out = torch.full_like(inp["q"], float("nan"))
+        prep = _prepare(inp, out, num_splits=8 if plan == "chunked" else None)
+    want_route = {"balanced": 2, "chunked": 1, "one_launch": 1, "paged": 2}[plan]
+    assert prep.plan["route"] == want_route
+    assert prep.plan["fused_merge"] == (1 if plan == "one_launch" else 0)
+    b.launch_gqa_decode_prepared(prep)
+    torch.cuda.synchronize()
+    plain = out.clone()
+    out.fill_(float("nan"))
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for e in evs:
+        e.record()                                 # creates the underlying HIP event
+    b.launch_gqa_decode_prepared_timed(prep, *evs)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), plain.view(torch.int16))
+    t_att, t_rest = evs[0].elapsed_time(evs[1]), evs[1].elapsed_time(evs[2])
+    assert t_att > 0 and t_rest >= 0, (t_att, t_rest)
+    for left_out in range(3):
+        out.fill_(float("nan"))
+        b.launch_gqa_decode_prepared_timed(prep, *[None if i == left_out else e
+                                                   for i, e in enumerate(evs)])
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), left_out
     prep.destroy()
